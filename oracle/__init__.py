@@ -1,0 +1,41 @@
+"""CPU float64 oracle of one Qwen3/Qwen3-VL text decoder layer's causal prefill.
+
+TEST INFRASTRUCTURE ONLY. This package is the plain, slow, obviously correct
+definition that the GPU path is checked against. Only the test suite, the
+smoke check and the bench's CPU-baseline leg may import it; the product path
+(the HIP library and its Python binding) never does, and this package imports
+nothing from the product path.
+
+Every function works in float64 on host numpy arrays. Matrix products use
+numpy's matmul as a library primitive; nothing is blocked, fused or reordered
+beyond the definitions the docstrings cite.
+
+Sources (web pages, cited by title and item):
+  * cortiq-engine 0.8.21, ``qwen3te.rs`` (Qwen3-VL as a prompt encoder):
+    module doc, ``rms_norm_into``, ``silu``, ``norm_rope``, the per-pair
+    causal attention loop and ``attention_gemm``, ``mrope_positions``,
+    ``encode_with_images``.
+  * hf2q 0.1.1, ``qwen3vl_text/forward.rs``: module doc (per-layer graph of
+    the peer reference), the DeepStack residual injection (Phase D).
+  * inferencelayer 0.2.3, ``vision.rs``: ``mrope_positions`` (M-RoPE
+    positions) and ``act_inplace`` (SiLU).
+
+Parity pins: every function here is pinned by the ``-m "not gpu"`` tests
+against closed forms, invariants, textbook formulations and brute force; no
+function is left unpinned.
+"""
+
+from .qwen3_layer import (  # noqa: F401
+    causal_gqa_attention,
+    layer_prefill,
+    layer_prefill_rows,
+    linear,
+    mrope_axes,
+    mrope_positions,
+    qk_norm_mrope,
+    rms_norm,
+    rope_inv_freq,
+    silu,
+    stack_prefill,
+    swiglu_ffn,
+)

@@ -1,0 +1,18 @@
+"""Seeded synthetic inputs for the Qwen3/Qwen3-VL decoder-layer prefill.
+
+This module is shared by the oracle-side tests and the GPU-side tests and
+bench. It holds no part of the layer's arithmetic: it only draws seeded
+normal variates, rounds them to the storage precision, and lays out the
+three-axis position table a workload prescribes. Every array it returns is
+a host numpy array.
+"""
+
+from .configs import CONFIGS, LayerConfig, get_config  # noqa: F401
+from .gen import (  # noqa: F401
+    WEIGHT_NAMES,
+    make_deepstack,
+    make_layer_weights,
+    make_positions,
+    make_x,
+    round_to_bf16,
+)

@@ -1,0 +1,125 @@
+"""Seeded normal draws for weights, hidden states, DeepStack slabs and positions.
+
+Every tensor is drawn from its own numpy ``SFC64`` stream, keyed by the seed,
+the tensor's name and a block index, in fixed blocks of ``_BLOCK`` values; so
+a tensor's values do not depend on how many threads draw it. Values are
+drawn in float64, scaled, rounded to float32, and (for bf16 workloads) rounded
+to the nearest bf16 value with ties to even; they are returned as float32
+arrays holding those exact values.
+"""
+
+import hashlib
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+_BLOCK = 1 << 22
+
+WEIGHT_NAMES = ("attn_norm", "wq", "wk", "wv", "q_norm", "k_norm", "wo",
+                "ffn_norm", "w_gate", "w_up", "w_down")
+
+
+def _key(name):
+    return int.from_bytes(hashlib.blake2b(name.encode(), digest_size=8).digest(), "little")
+
+
+def _normal_block(seed, key, blk, n):
+    g = np.random.Generator(np.random.SFC64(np.random.SeedSequence([seed, key, blk])))
+    return g.standard_normal(n)
+
+
+def round_to_bf16(a):
+    """Round float32 values to the nearest bf16 value (ties to even), kept as float32."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) & np.uint32(0xFFFF0000)
+    return r.view(np.float32)
+
+
+def normal(seed, name, shape, mean=0.0, std=1.0, dtype="bf16", threads=8):
+    """mean + std * N(0,1) draws for tensor `name`, rounded to the storage dtype."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.float32)
+    key = _key(name)
+
+    def fill(b):
+        lo = b * _BLOCK
+        hi = min(n, lo + _BLOCK)
+        v = _normal_block(seed, key, b, hi - lo) * std + mean
+        out[lo:hi] = v.astype(np.float32)
+
+    nblk = (n + _BLOCK - 1) // _BLOCK
+    if nblk <= 1 or threads <= 1:
+        for b in range(nblk):
+            fill(b)
+    else:
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(fill, range(nblk)))
+    if dtype == "bf16":
+        out = round_to_bf16(out)
+    return out.reshape(shape)
+
+
+def make_layer_weights(cfg, layer=0):
+    """The eleven weight tensors of decoder layer `layer`, torch nn.Linear layout [out, in].
+
+    Projection weights ~ N(0, 0.02), norm weights ~ 1 + N(0, 0.1); no biases.
+    """
+    h, hd, f = cfg.hidden, cfg.head_dim, cfg.ffn
+    shapes = {
+        "attn_norm": (h,), "wq": (cfg.q_dim, h), "wk": (cfg.kv_dim, h), "wv": (cfg.kv_dim, h),
+        "q_norm": (hd,), "k_norm": (hd,), "wo": (h, cfg.q_dim), "ffn_norm": (h,),
+        "w_gate": (f, h), "w_up": (f, h), "w_down": (h, f),
+    }
+    w = {}
+    for name in WEIGHT_NAMES:
+        is_norm = name.endswith("norm")
+        w[name] = normal(cfg.seed, f"L{layer}.{name}", shapes[name],
+                         mean=1.0 if is_norm else 0.0, std=0.1 if is_norm else 0.02,
+                         dtype=cfg.dtype)
+    return w
+
+
+def make_x(cfg):
+    """Input hidden states [S, H] ~ N(0, 1) (bf16-exact values for bf16 workloads)."""
+    return normal(cfg.seed, "x", (cfg.seq_len, cfg.hidden), dtype=cfg.dtype)
+
+
+def make_positions(cfg):
+    """The [3, S] int32 (t, h, w) position table the workload prescribes.
+
+    Text-only: t = h = w = token index. Image span: text tokens before the span
+    count 0, 1, ...; the span's merged grid tokens come in 2x2 block-major order
+    with t pinned at the span's first position and h, w = that position plus the
+    grid row and column; text after the span resumes at the span's first
+    position plus the grid's longer side and counts up.
+    """
+    s = cfg.seq_len
+    pos = np.empty((3, s), dtype=np.int32)
+    idx = np.arange(s, dtype=np.int32)
+    pos[:] = idx
+    if cfg.positions == "image_span":
+        p0, gh, gw = cfg.span_start, cfg.span_h, cfg.span_w
+        n = gh * gw
+        k = np.arange(n)
+        blk, sub = k // 4, k % 4
+        blocks_per_row = gw // 2
+        row = 2 * (blk // blocks_per_row) + sub // 2
+        col = 2 * (blk % blocks_per_row) + sub % 2
+        pos[0, p0:p0 + n] = p0
+        pos[1, p0:p0 + n] = p0 + row
+        pos[2, p0:p0 + n] = p0 + col
+        after = np.arange(s - (p0 + n), dtype=np.int32) + p0 + max(gh, gw)
+        pos[:, p0 + n:] = after
+    return pos
+
+
+def make_deepstack(cfg):
+    """(rows, slab): DeepStack rows (the image span, ascending) and the [n, H] slab
+    ~ N(0, deepstack_std) added on them; (None, None) when the workload has none."""
+    if cfg.deepstack_std <= 0:
+        return None, None
+    rows = np.arange(cfg.span_start, cfg.span_start + cfg.span_len, dtype=np.int32)
+    slab = normal(cfg.seed, "deepstack", (len(rows), cfg.hidden), std=cfg.deepstack_std,
+                  dtype=cfg.dtype)
+    return rows, slab
