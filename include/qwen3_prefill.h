@@ -1,0 +1,200 @@
+/*
+ * qwen3_prefill.h — C ABI of the MI355X (gfx950) Qwen3/Qwen3-VL text decoder-layer prefill.
+ *
+ * The library computes the full-sequence causal prefill of one Qwen3/Qwen3-VL text
+ * decoder layer (no KV cache, every token at once):
+ *
+ *   xn = RMSNorm(x, attn_norm)                                 plain weight, eps inside the sqrt
+ *   q, k, v = xn Wq^T, xn Wk^T, xn Wv^T                        no biases
+ *   q, k = per-head RMSNorm (q_norm / k_norm), then interleaved three-axis MRoPE
+ *   o = causal GQA softmax(q k^T / sqrt(head_dim)) v
+ *   y1 = x + o Wo^T
+ *   y2 = y1 + (silu(RMSNorm(y1, ffn_norm) Wg^T) * (RMSNorm(y1, ffn_norm) Wu^T)) Wd^T
+ *   y2[rows[i]] += deepstack[i]                                 optional, image-token rows only
+ *
+ * Sources (web pages, cited by title and item):
+ *   hf2q 0.1.1, qwen3vl_text/forward.rs — module doc (the per-layer graph of the peer
+ *     reference), Phase D (position-gated DeepStack residual add), argument validation of
+ *     `forward_text_prefill_logits_last`.
+ *   cortiq-engine 0.8.21, qwen3te.rs — module doc (q/k RMSNorm before the rotation, GQA,
+ *     split-half RoPE, plain-w RMSNorm, no final norm), `rms_norm_into`, `silu`, `norm_rope`,
+ *     `attention_gemm`, the per-pair causal loop and `encode_with_images`.
+ *   inferencelayer 0.2.3, vision.rs — `mrope_positions` (what the three position axes hold).
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller. The library never allocates
+ *     or frees device memory inside these calls and keeps no pointer after a call returns.
+ *   - Matrices are row-major. Weights use the torch nn.Linear layout [out_features, in_features].
+ *     Activations are token-major: [seq_len, ...]; q/k/v/attention outputs are [seq_len, heads,
+ *     head_dim] contiguous.
+ *   - bf16 / f16 tensors hold IEEE bfloat16 / binary16 bit patterns (uint16_t); f32 tensors hold
+ *     IEEE binary32.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the default stream).
+ *     No call synchronizes the device.
+ *   - Arguments are checked on the host before anything is enqueued. A failed check returns a
+ *     nonzero qwen3_status, enqueues nothing, and sets a message readable through
+ *     qwen3_last_error(). There is no fallback path: an unsupported shape is an error.
+ *   - A HIP launch error returns QWEN3_ERR_HIP with the HIP error text.
+ */
+#ifndef QWEN3_PREFILL_H
+#define QWEN3_PREFILL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { QWEN3_F32 = 0, QWEN3_BF16 = 1, QWEN3_F16 = 2 } qwen3_dtype;
+
+typedef enum {
+  QWEN3_OK = 0,
+  QWEN3_ERR_INVALID_ARG = 1,  /* a pointer, size or relation among sizes is invalid      */
+  QWEN3_ERR_UNSUPPORTED = 2,  /* valid, but a shape or dtype this library does not run   */
+  QWEN3_ERR_WORKSPACE = 3,    /* workspace pointer NULL or smaller than required         */
+  QWEN3_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed              */
+} qwen3_status;
+
+/* Shape and numerics of one decoder layer.
+ *   hidden      H; multiple of 256, at most 16384.
+ *   n_heads     query heads nh; n_heads % n_kv_heads == 0 and n_heads / n_kv_heads in {1,2,4,8}
+ *               (16-bit operands); any divisor for f32.
+ *   n_kv_heads  KV heads nkv (GQA: query head h reads KV head h / (nh / nkv), cortiq-engine
+ *               qwen3te.rs, `attention_gemm`).
+ *   head_dim    hd: 128 for 16-bit operands; 64 or 128 for f32.
+ *   ffn         F, the SwiGLU width; multiple of 128.
+ *   rms_eps     eps added to the mean of squares inside the square root (`rms_norm_into`).
+ *   rope_theta  RoPE base: pair i < hd/2 turns at theta^(-2i/hd) per position (`norm_rope`).
+ *   mrope_section  (t, h, w) pair counts: sum == hd/2, 3*h <= hd/2 and 3*w <= hd/2. Pair i
+ *               follows the h axis when i % 3 == 1 and i < 3*h, the w axis when i % 3 == 2 and
+ *               i < 3*w, and the t axis otherwise (Qwen3-VL interleaved MRoPE, `norm_rope`).
+ *   wdtype      dtype of the weights: QWEN3_BF16, QWEN3_F16 or QWEN3_F32.
+ *   act_dtype   dtype of the intermediate matrix-product operands (normalized activations,
+ *               q, k, v, attention probabilities and output, the SwiGLU activation):
+ *                 QWEN3_F16  fp16 operands, fp32 accumulation and softmax (with bf16 weights,
+ *                            each weight tile is converted to fp16 on its way into LDS: exact
+ *                            for |w| in [2^-17, 65504]);
+ *                 QWEN3_BF16 bf16 operands (bf16 weights only);
+ *                 QWEN3_F32  fp32 end to end (requires wdtype QWEN3_F32).
+ *               fp16 and bf16 run at the same MFMA rate; fp16 keeps 3 more mantissa bits,
+ *               which the 8B/32B-shaped layers need to stay within 2e-2 of an exact
+ *               reference, but it holds magnitudes only up to 65504.
+ *   resid_dtype dtype of the residual stream x_in/x_out; must be QWEN3_F32.
+ */
+typedef struct {
+  int32_t hidden, n_heads, n_kv_heads, head_dim, ffn;
+  float rms_eps, rope_theta;
+  int32_t mrope_section[3];
+  qwen3_dtype wdtype;
+  qwen3_dtype act_dtype;
+  qwen3_dtype resid_dtype;
+} qwen3_layer_cfg;
+
+/* Device pointers to one layer's weights, all of dtype cfg.wdtype, layout [out, in]. */
+typedef struct {
+  const void *attn_norm;   /* [H]                 input RMSNorm weight                    */
+  const void *wq;          /* [nh*hd, H]                                                  */
+  const void *wk;          /* [nkv*hd, H]                                                 */
+  const void *wv;          /* [nkv*hd, H]                                                 */
+  const void *q_norm;      /* [hd]                per-head RMSNorm weight on q            */
+  const void *k_norm;      /* [hd]                per-head RMSNorm weight on k            */
+  const void *wo;          /* [H, nh*hd]                                                  */
+  const void *ffn_norm;    /* [H]                 post-attention RMSNorm weight           */
+  const void *w_gate;      /* [F, H]                                                      */
+  const void *w_up;        /* [F, H]                                                      */
+  const void *w_down;      /* [H, F]                                                      */
+} qwen3_layer_weights;
+
+/* Bytes of device workspace qwen3_layer_prefill needs for `seq_len` tokens (0 if cfg is
+ * NULL or seq_len < 1). The workspace holds the normalized activations, q/k/v, the attention
+ * output and the SwiGLU activation; its contents on entry do not matter. */
+size_t qwen3_layer_workspace_bytes(const qwen3_layer_cfg *cfg, int32_t seq_len);
+
+/* One decoder layer over all `seq_len` tokens (the recipe at the top of this file).
+ *   x_in, x_out   [S, H] f32 residual stream in and out; x_out may equal x_in (in place),
+ *                 other overlaps are not allowed.
+ *   positions     [3, S] int32: the t row, then the h row, then the w row. A text token has
+ *                 t = h = w; an image token has one t per image and h, w on its merged grid
+ *                 (inferencelayer vision.rs, `mrope_positions`). Values must be >= 0.
+ *   ds_rows, n_ds DeepStack rows: n_ds >= 0 strictly increasing row indices < S, or NULL/0
+ *                 (hf2q forward.rs, Phase D: the slab is added on image-token rows only).
+ *   ds            [n_ds, H] of cfg.wdtype: ds[i] is added to output row ds_rows[i] after the
+ *                 FFN residual; must be NULL when n_ds == 0 and non-NULL otherwise. The row
+ *                 values are device data, read by the kernel: an entry outside [0, S) or not
+ *                 greater than the entry before it is skipped (nothing is added for it).
+ *   workspace     at least qwen3_layer_workspace_bytes(cfg, S) bytes, 256-byte aligned.
+ * Errors: seq_len < 1, NULL pointers, unsupported shapes, a bad DeepStack row list, or a
+ * small workspace return a nonzero status before anything is enqueued. */
+int qwen3_layer_prefill(const qwen3_layer_cfg *cfg, const qwen3_layer_weights *w,
+                        const void *x_in, void *x_out, int32_t seq_len,
+                        const int32_t *positions, const int32_t *ds_rows, int32_t n_ds,
+                        const void *ds, void *workspace, size_t workspace_bytes,
+                        void *stream);
+
+/* Per-head RMSNorm then interleaved-MRoPE rotation of q and k, in place
+ * (cortiq-engine qwen3te.rs, `norm_rope`).
+ *   q [S, n_heads, head_dim], k [S, n_kv_heads, head_dim] of `dtype`, contiguous.
+ *   q_norm, k_norm [head_dim] of `norm_dtype`. Each (token, head) row x is replaced by
+ *   r = x / sqrt(mean(x^2) + eps) * norm_w, then for i < hd/2 the pair (r_i, r_{i+hd/2}) is
+ *   rotated by phi = positions[axis(i)][s] * theta^(-2i/hd) (axis rule under qwen3_layer_cfg).
+ *   positions [3, S] int32 as for qwen3_layer_prefill. head_dim 64 or 128; any dtypes. The
+ *   norm and rotation run in fp32 (the angle is formed and range-reduced in fp64). */
+int qk_norm_mrope(void *q, void *k, int32_t seq_len, int32_t n_heads, int32_t n_kv_heads,
+                  int32_t head_dim, const void *q_norm, const void *k_norm, float eps,
+                  const int32_t *positions, float theta, const int32_t mrope_section[3],
+                  qwen3_dtype dtype, qwen3_dtype norm_dtype, void *stream);
+
+/* Causal grouped-query attention (cortiq-engine qwen3te.rs, per-pair loop / `attention_gemm`):
+ *   out[s, h] = sum_{j<=s} softmax_j(scale * q[s,h] . k[j,g]) v[j,g],  g = h / (nh / nkv).
+ *   q, out [S, n_heads, head_dim]; k, v [S, n_kv_heads, head_dim]; all `dtype`, contiguous.
+ *   scale is normally 1/sqrt(head_dim). bf16 / f16: head_dim 128, nh/nkv in {1,2,4,8}, 16-bit
+ *   products with fp32 accumulation and fp32 online softmax. f32: head_dim 64 or 128, fp32
+ *   throughout.
+ *   out must not overlap q, k or v. */
+int gqa_causal_attention(const void *q, const void *k, const void *v, void *out,
+                         int32_t seq_len, int32_t n_heads, int32_t n_kv_heads,
+                         int32_t head_dim, float scale, qwen3_dtype dtype, void *stream);
+
+/* SwiGLU feed-forward with optional residual (cortiq-engine qwen3te.rs, gate/up/act/down):
+ *   out = [residual +] (silu(x W_gate^T) * (x W_up^T)) W_down^T,  silu(z) = z / (1 + e^-z).
+ *   W_gate, W_up [ffn, hidden] and W_down [hidden, ffn] of `wdtype`; x_normed [S, hidden] of
+ *   `x_dtype`, which is also the product operand format (the (wdtype, x_dtype) pairs allowed
+ *   are those of (wdtype, act_dtype) in qwen3_layer_cfg). residual [S, hidden] f32 or NULL.
+ *   out [S, hidden] of `out_dtype`: f32, or x_dtype when residual is NULL; out may equal
+ *   residual. workspace holds the [S, ffn] activation: swiglu_ffn_workspace_bytes() bytes. */
+int swiglu_ffn(const void *x_normed, const void *w_gate, const void *w_up, const void *w_down,
+               const void *residual, void *out, int32_t seq_len, int32_t hidden, int32_t ffn,
+               qwen3_dtype wdtype, qwen3_dtype x_dtype, qwen3_dtype out_dtype, void *workspace,
+               size_t workspace_bytes, void *stream);
+size_t swiglu_ffn_workspace_bytes(int32_t seq_len, int32_t ffn, qwen3_dtype x_dtype);
+
+/* Row RMSNorm with a plain weight (cortiq-engine qwen3te.rs, `rms_norm_into`):
+ *   y[s] = x[s] / sqrt(mean_j x[s,j]^2 + eps) * w.
+ *   x [rows, hidden] f32; w [hidden] of w_dtype; y [rows, hidden] of y_dtype.
+ *   hidden a multiple of 256. y must not overlap x. */
+int rms_norm_rows(const float *x, const void *w, void *y, int32_t rows, int32_t hidden,
+                  float eps, qwen3_dtype w_dtype, qwen3_dtype y_dtype, void *stream);
+
+/* Thread-local text of the last nonzero status returned on this thread ("" if none). */
+const char *qwen3_last_error(void);
+
+/* ---- Measurement aid -------------------------------------------------------------------
+ * When enabled, every kernel launched by the calls above is bracketed by a pair of hipEvents
+ * recorded on the call's stream. qwen3_timing_collect() waits for the recorded events, sums
+ * the elapsed time per kernel name, writes up to `max_entries` entries and clears the record.
+ * At most 65536 launches are recorded between collects; later ones are not timed. */
+typedef struct {
+  char name[48];
+  int32_t launches;
+  double total_ms;
+} qwen3_kernel_time;
+
+int qwen3_timing_enable(int enable);
+int qwen3_timing_collect(qwen3_kernel_time *out, int32_t max_entries, int32_t *n_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QWEN3_PREFILL_H */

@@ -1,0 +1,152 @@
+"""Host-side checks of the C ABI library: it loads, exports every symbol the header declares,
+and rejects invalid arguments with the documented status before touching the GPU."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qwen3_prefill.h")
+
+L = pytest.importorskip("transformer_lm_prefill_amd._lib")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.skip("library not built")
+    return L.load()
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return set(re.findall(r"^\s*(?:const\s+)?(?:int|size_t|char\s*\*|void)\s*\*?\s*(\w+)\s*\(", src, flags=re.M))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ("qwen3_layer_prefill", "qk_norm_mrope", "gqa_causal_attention", "swiglu_ffn",
+              "qwen3_layer_workspace_bytes", "qwen3_last_error", "rms_norm_rows"):
+        assert n in names
+    assert names == set(L.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for n in _declared():
+        assert hasattr(lib, n), n
+
+
+def _cfg(**kw):
+    c = L.LayerCfg()
+    d = dict(hidden=2048, n_heads=16, n_kv_heads=8, head_dim=128, ffn=6144, rms_eps=1e-6,
+             rope_theta=5e6, wdtype=L.QWEN3_BF16, act_dtype=L.QWEN3_F16, resid_dtype=L.QWEN3_F32)
+    d.update(kw)
+    sec = d.pop("sections", (24, 20, 20))
+    for k, v in d.items():
+        setattr(c, k, v)
+    c.mrope_section = (ctypes.c_int32 * 3)(*sec)
+    return c
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails its checks first
+
+
+def _weights():
+    return L.LayerWeights(*([FAKE] * 11))
+
+
+def _call_layer(lib, cfg, s=16, ws_bytes=None, n_ds=0, ds=None, ds_rows=None, weights=None,
+                x_out=FAKE, workspace=ctypes.c_void_p(0x100000)):
+    if ws_bytes is None:
+        ws_bytes = lib.qwen3_layer_workspace_bytes(ctypes.byref(cfg), max(s, 1))
+    w = weights or _weights()
+    return lib.qwen3_layer_prefill(ctypes.byref(cfg), ctypes.byref(w), FAKE, x_out, s, FAKE,
+                                   ds_rows, n_ds, ds, workspace, ws_bytes, None)
+
+
+def test_workspace_size_formula(lib):
+    c = _cfg(hidden=4096, n_heads=32, n_kv_heads=8, ffn=12288)
+    s = 4096
+    expect = 2 * s * (4096 + (4096 + 2048) + 4096 + 12288)
+    assert lib.qwen3_layer_workspace_bytes(ctypes.byref(c), s) == expect
+    c32 = _cfg(hidden=4096, n_heads=32, n_kv_heads=8, ffn=12288, wdtype=0, act_dtype=0)
+    assert lib.qwen3_layer_workspace_bytes(ctypes.byref(c32), s) == 2 * expect
+    assert lib.qwen3_layer_workspace_bytes(ctypes.byref(c), 0) == 0
+    assert lib.qwen3_layer_workspace_bytes(None, 16) == 0
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(n_heads=12, n_kv_heads=8), 1, "multiple of n_kv_heads"),
+    (dict(n_heads=32, n_kv_heads=2), 2, "1, 2, 4 or 8"),
+    (dict(head_dim=64, sections=(12, 10, 10)), 2, "head_dim must be 128"),
+    (dict(wdtype=0, act_dtype=2), 2, "supported pairs"),
+    (dict(wdtype=2, act_dtype=1), 2, "supported pairs"),
+    (dict(act_dtype=9), 1, "qwen3_dtype"),
+    (dict(sections=(24, 20, 21)), 1, "sum to head_dim/2"),
+    (dict(sections=(4, 30, 30)), 1, "interleaved"),
+    (dict(hidden=1000), 2, "multiple of 256"),
+    (dict(ffn=100), 2, "multiple of 128"),
+    (dict(resid_dtype=1), 2, "resid_dtype"),
+    (dict(wdtype=7), 1, "qwen3_dtype"),
+    (dict(rope_theta=0.5), 1, "rope_theta"),
+    (dict(rms_eps=-1.0), 1, "rms_eps"),
+])
+def test_bad_config_rejected(lib, kw, status, needle):
+    rc = _call_layer(lib, _cfg(**kw))
+    assert rc == status
+    assert needle in lib.qwen3_last_error().decode()
+
+
+def test_empty_sequence_rejected(lib):
+    rc = _call_layer(lib, _cfg(), s=0, ws_bytes=1 << 30)
+    assert rc == 1 and "empty" in lib.qwen3_last_error().decode()
+
+
+def test_deepstack_argument_rules(lib):
+    c = _cfg()
+    assert _call_layer(lib, c, n_ds=0, ds=FAKE) == 1
+    assert "n_ds == 0" in lib.qwen3_last_error().decode()
+    assert _call_layer(lib, c, n_ds=4, ds=FAKE, ds_rows=None) == 1
+    assert _call_layer(lib, c, n_ds=17, ds=FAKE, ds_rows=FAKE) == 1
+    assert _call_layer(lib, c, n_ds=-1) == 1
+
+
+def test_null_weight_and_workspace_rejected(lib):
+    c = _cfg()
+    w = _weights()
+    w.k_norm = None
+    assert _call_layer(lib, c, weights=w) == 1
+    assert "k_norm" in lib.qwen3_last_error().decode()
+    need = lib.qwen3_layer_workspace_bytes(ctypes.byref(c), 16)
+    assert _call_layer(lib, c, ws_bytes=need - 1) == 3
+    assert _call_layer(lib, c, workspace=None) == 3
+    assert _call_layer(lib, c, workspace=ctypes.c_void_p(0x100010)) == 3
+
+
+def test_partial_overlap_rejected(lib):
+    assert _call_layer(lib, _cfg(), x_out=ctypes.c_void_p(0x1000 + 64)) == 1
+    assert "overlap" in lib.qwen3_last_error().decode()
+
+
+def test_sub_op_argument_checks(lib):
+    sec = (ctypes.c_int32 * 3)(24, 20, 20)
+    assert lib.qk_norm_mrope(FAKE, FAKE, 0, 4, 2, 128, FAKE, FAKE, 1e-6, FAKE, 5e6, sec, 1, 1, None) == 1
+    assert lib.qk_norm_mrope(FAKE, FAKE, 4, 4, 2, 96, FAKE, FAKE, 1e-6, FAKE, 5e6, sec, 1, 1, None) == 2
+    assert lib.qk_norm_mrope(FAKE, FAKE, 4, 4, 2, 128, FAKE, FAKE, 1e-6, FAKE, 5e6, sec, 1, 5, None) == 1
+    assert lib.gqa_causal_attention(FAKE, FAKE, FAKE, FAKE, 8, 6, 4, 128, 0.1, 1, None) == 1
+    assert lib.gqa_causal_attention(FAKE, FAKE, FAKE, FAKE, 8, 4, 2, 128, 0.0, 1, None) == 1
+    assert lib.gqa_causal_attention(FAKE, FAKE, FAKE, FAKE, 8, 4, 2, 64, 0.1, 1, None) == 2
+    assert lib.swiglu_ffn(FAKE, FAKE, FAKE, FAKE, None, FAKE, 8, 2048, 6144, 1, 2, 0, FAKE, 10, None) == 3
+    assert lib.swiglu_ffn(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 2048, 6144, 1, 2, 2, FAKE, 1 << 30, None) == 2
+    assert lib.swiglu_ffn(FAKE, FAKE, FAKE, FAKE, None, FAKE, 8, 2048, 6144, 1, 2, 1, FAKE, 1 << 30, None) == 2
+    assert lib.swiglu_ffn(FAKE, FAKE, FAKE, FAKE, None, FAKE, 8, 2048, 6144, 0, 1, 0, FAKE, 1 << 30, None) == 2
+    assert lib.rms_norm_rows(FAKE, FAKE, FAKE, 4, 300, 1e-6, 1, 1, None) == 2
+    assert lib.rms_norm_rows(FAKE, FAKE, FAKE, 0, 256, 1e-6, 1, 1, None) == 1
+
+
+def test_timing_collect_empty(lib):
+    n = ctypes.c_int32(-1)
+    assert lib.qwen3_timing_collect(None, 0, ctypes.byref(n)) == 0 and n.value == 0

@@ -1,0 +1,19 @@
+"""MI355X (gfx950) prefill of one Qwen3/Qwen3-VL text decoder layer.
+
+The computation runs in libqwen3_prefill.so (hand-written HIP kernels behind a C ABI, see
+include/qwen3_prefill.h). This package is the thin Python binding: it passes torch device
+pointers and the current HIP stream to the library and does no arithmetic of its own.
+"""
+
+from .ops import (  # noqa: F401
+    LayerSpec,
+    Qwen3Error,
+    gqa_causal_attention,
+    layer_prefill,
+    layer_workspace_bytes,
+    qk_norm_mrope,
+    rms_norm_rows,
+    swiglu_ffn,
+    timing_collect,
+    timing_enable,
+)

@@ -1,0 +1,88 @@
+"""ctypes view of libqwen3_prefill.so: structs and prototypes mirroring include/qwen3_prefill.h."""
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqwen3_prefill.so")
+
+QWEN3_F32 = 0
+QWEN3_BF16 = 1
+QWEN3_F16 = 2
+STATUS = {0: "QWEN3_OK", 1: "QWEN3_ERR_INVALID_ARG", 2: "QWEN3_ERR_UNSUPPORTED",
+          3: "QWEN3_ERR_WORKSPACE", 4: "QWEN3_ERR_HIP"}
+
+# Every symbol the header declares.
+EXPORTS = ("qwen3_layer_workspace_bytes", "qwen3_layer_prefill", "qk_norm_mrope",
+           "gqa_causal_attention", "swiglu_ffn", "swiglu_ffn_workspace_bytes", "rms_norm_rows",
+           "qwen3_last_error", "qwen3_timing_enable", "qwen3_timing_collect")
+
+
+class LayerCfg(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("ffn", ctypes.c_int32), ("rms_eps", ctypes.c_float),
+                ("rope_theta", ctypes.c_float), ("mrope_section", ctypes.c_int32 * 3),
+                ("wdtype", ctypes.c_int), ("act_dtype", ctypes.c_int),
+                ("resid_dtype", ctypes.c_int)]
+
+
+class LayerWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("attn_norm", "wq", "wk", "wv", "q_norm", "k_norm",
+                                               "wo", "ffn_norm", "w_gate", "w_up", "w_down")]
+
+
+class KernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_int32),
+                ("total_ms", ctypes.c_double)]
+
+
+class Qwen3Error(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def load():
+    """Load the HIP library; raises if it has not been built (there is no other path)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m transformer_lm_prefill_amd.build_lib`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    lib.qwen3_layer_workspace_bytes.argtypes = [ctypes.POINTER(LayerCfg), i32]
+    lib.qwen3_layer_workspace_bytes.restype = sz
+    lib.qwen3_layer_prefill.argtypes = [ctypes.POINTER(LayerCfg), ctypes.POINTER(LayerWeights),
+                                        vp, vp, i32, vp, vp, i32, vp, vp, sz, vp]
+    lib.qwen3_layer_prefill.restype = ctypes.c_int
+    lib.qk_norm_mrope.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, f32, vp, f32,
+                                  ctypes.POINTER(i32), ctypes.c_int, ctypes.c_int, vp]
+    lib.qk_norm_mrope.restype = ctypes.c_int
+    lib.gqa_causal_attention.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, f32, ctypes.c_int, vp]
+    lib.gqa_causal_attention.restype = ctypes.c_int
+    lib.swiglu_ffn.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_int, ctypes.c_int,
+                               ctypes.c_int, vp, sz, vp]
+    lib.swiglu_ffn.restype = ctypes.c_int
+    lib.swiglu_ffn_workspace_bytes.argtypes = [i32, i32, ctypes.c_int]
+    lib.swiglu_ffn_workspace_bytes.restype = sz
+    lib.rms_norm_rows.argtypes = [vp, vp, vp, i32, i32, f32, ctypes.c_int, ctypes.c_int, vp]
+    lib.rms_norm_rows.restype = ctypes.c_int
+    lib.qwen3_last_error.argtypes = []
+    lib.qwen3_last_error.restype = ctypes.c_char_p
+    lib.qwen3_timing_enable.argtypes = [ctypes.c_int]
+    lib.qwen3_timing_enable.restype = ctypes.c_int
+    lib.qwen3_timing_collect.argtypes = [ctypes.POINTER(KernelTime), i32, ctypes.POINTER(i32)]
+    lib.qwen3_timing_collect.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def check(status):
+    if status != 0:
+        msg = load().qwen3_last_error().decode(errors="replace")
+        raise Qwen3Error(status, msg)

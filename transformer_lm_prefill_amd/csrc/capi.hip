@@ -1,0 +1,454 @@
+// C ABI of the layer library: argument checks, workspace layout, the launch sequence of one
+// decoder layer on the caller's stream, error reporting and optional per-kernel timing.
+//
+// Argument rules follow the pages' own checks where they have them (hf2q 0.1.1,
+// qwen3vl_text/forward.rs, `forward_text_prefill_logits_last`: an empty sequence is an error,
+// the DeepStack rows must lie inside the sequence, a slab needs rows) and fail loudly on any
+// shape the kernels do not run: there is no fallback path.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "qwen3_prefill.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(QWEN3_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// ---- per-kernel timing --------------------------------------------------------------------
+constexpr int kMaxTimed = 65536;
+std::mutex g_tmu;
+bool g_timing = false;
+std::vector<hipEvent_t> g_events;           // 2 per slot, created on demand and reused
+std::vector<const char*> g_slot_name;       // name of the kernel timed in each used slot
+int g_used = 0;
+
+int timing_begin(const char* name, hipStream_t s) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  if (!g_timing || g_used >= kMaxTimed) return -1;
+  const int slot = g_used;
+  while (static_cast<int>(g_events.size()) < 2 * (slot + 1)) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return -1;
+    g_events.push_back(e);
+  }
+  if (static_cast<int>(g_slot_name.size()) <= slot) g_slot_name.resize(slot + 1);
+  g_slot_name[slot] = name;
+  if (hipEventRecord(g_events[2 * slot], s) != hipSuccess) return -1;
+  ++g_used;
+  return slot;
+}
+
+void timing_end(int slot, hipStream_t s) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  (void)hipEventRecord(g_events[2 * slot + 1], s);
+}
+
+struct KTimer {
+  int slot = -1;
+  hipStream_t s;
+  KTimer(const char* name, hipStream_t st) : s(st) {
+    if (g_timing) slot = timing_begin(name, st);
+  }
+  ~KTimer() {
+    if (slot >= 0) timing_end(slot, s);
+  }
+};
+
+// ---- checks ---------------------------------------------------------------------------------
+bool valid_dtype(int d) { return d == QWEN3_F32 || d == QWEN3_BF16 || d == QWEN3_F16; }
+size_t dsize(qwen3_dtype d) { return d == QWEN3_F32 ? 4 : 2; }
+
+// (weights, product operands) pairs the kernels run: f32/f32, bf16/bf16, bf16/f16, f16/f16.
+int check_formats(qwen3_dtype w, qwen3_dtype a) {
+  if (!valid_dtype(w) || !valid_dtype(a))
+    return fail(QWEN3_ERR_INVALID_ARG, "dtype (%d, %d) is not a qwen3_dtype", w, a);
+  const bool ok = (w == QWEN3_F32 && a == QWEN3_F32) || (w == QWEN3_BF16 && a == QWEN3_BF16) ||
+                  (w == QWEN3_BF16 && a == QWEN3_F16) || (w == QWEN3_F16 && a == QWEN3_F16);
+  if (!ok)
+    return fail(QWEN3_ERR_UNSUPPORTED,
+                "weights %d with operands %d: supported pairs are f32/f32, bf16/bf16, bf16/f16, f16/f16", w, a);
+  return QWEN3_OK;
+}
+size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+
+int check_heads(int32_t nh, int32_t nkv, int32_t hd, qwen3_dtype dt) {
+  const char* dname = dt == QWEN3_F16 ? "f16" : "bf16";
+  if (nh < 1 || nkv < 1) return fail(QWEN3_ERR_INVALID_ARG, "n_heads (%d) and n_kv_heads (%d) must be >= 1", nh, nkv);
+  if (nh % nkv != 0)
+    return fail(QWEN3_ERR_INVALID_ARG, "n_heads (%d) must be a multiple of n_kv_heads (%d)", nh, nkv);
+  if (dt != QWEN3_F32) {
+    const int g = nh / nkv;
+    if (hd != 128) return fail(QWEN3_ERR_UNSUPPORTED, "%s head_dim must be 128 (got %d)", dname, hd);
+    if (g != 1 && g != 2 && g != 4 && g != 8)
+      return fail(QWEN3_ERR_UNSUPPORTED, "%s n_heads / n_kv_heads must be 1, 2, 4 or 8 (got %d)", dname, g);
+  } else {
+    if (hd != 64 && hd != 128) return fail(QWEN3_ERR_UNSUPPORTED, "f32 head_dim must be 64 or 128 (got %d)", hd);
+  }
+  return QWEN3_OK;
+}
+
+int check_sections(const int32_t sec[3], int32_t hd) {
+  if (!sec) return fail(QWEN3_ERR_INVALID_ARG, "mrope_section is NULL");
+  const int half = hd / 2;
+  if (sec[0] < 0 || sec[1] < 0 || sec[2] < 0 || sec[0] + sec[1] + sec[2] != half)
+    return fail(QWEN3_ERR_INVALID_ARG, "mrope_section (%d,%d,%d) must be >= 0 and sum to head_dim/2 = %d",
+                sec[0], sec[1], sec[2], half);
+  if (3 * sec[1] > half || 3 * sec[2] > half)
+    return fail(QWEN3_ERR_INVALID_ARG,
+                "mrope_section h (%d) and w (%d) must be <= head_dim/6 for the interleaved layout", sec[1], sec[2]);
+  return QWEN3_OK;
+}
+
+int check_cfg(const qwen3_layer_cfg* c) {
+  if (!c) return fail(QWEN3_ERR_INVALID_ARG, "cfg is NULL");
+  int st = check_formats(c->wdtype, c->act_dtype);
+  if (st) return st;
+  if (c->resid_dtype != QWEN3_F32)
+    return fail(QWEN3_ERR_UNSUPPORTED, "resid_dtype must be QWEN3_F32 (the residual stream is carried in fp32)");
+  if (c->hidden < 256 || c->hidden % 256 != 0 || c->hidden > 16384)
+    return fail(QWEN3_ERR_UNSUPPORTED, "hidden (%d) must be a multiple of 256 in [256, 16384]", c->hidden);
+  if (c->ffn < 128 || c->ffn % 128 != 0)
+    return fail(QWEN3_ERR_UNSUPPORTED, "ffn (%d) must be a positive multiple of 128", c->ffn);
+  st = check_heads(c->n_heads, c->n_kv_heads, c->head_dim, c->act_dtype);
+  if (st) return st;
+  if (static_cast<int64_t>(c->n_heads) * c->head_dim > 65536)
+    return fail(QWEN3_ERR_UNSUPPORTED, "n_heads * head_dim too large");
+  st = check_sections(c->mrope_section, c->head_dim);
+  if (st) return st;
+  if (!(c->rms_eps >= 0.f) || !std::isfinite(c->rms_eps))
+    return fail(QWEN3_ERR_INVALID_ARG, "rms_eps must be finite and >= 0");
+  if (!(c->rope_theta > 1.f) || !std::isfinite(c->rope_theta))
+    return fail(QWEN3_ERR_INVALID_ARG, "rope_theta must be finite and > 1");
+  return QWEN3_OK;
+}
+
+struct Workspace {
+  size_t xn, qkv, o, act, total;
+};
+
+Workspace layout(const qwen3_layer_cfg* c, int32_t S) {
+  const size_t e = dsize(c->act_dtype);
+  const size_t q_dim = static_cast<size_t>(c->n_heads) * c->head_dim;
+  const size_t kv_dim = static_cast<size_t>(c->n_kv_heads) * c->head_dim;
+  Workspace w;
+  w.xn = 0;
+  w.qkv = w.xn + align256(static_cast<size_t>(S) * c->hidden * e);
+  w.o = w.qkv + align256(static_cast<size_t>(S) * (q_dim + 2 * kv_dim) * e);
+  w.act = w.o + align256(static_cast<size_t>(S) * q_dim * e);
+  w.total = w.act + align256(static_cast<size_t>(S) * c->ffn * e);
+  return w;
+}
+
+// ---- building blocks shared by the layer and the sub-op entry points ------------------------
+int run_rmsnorm(const float* x, const void* w, qwen3_dtype wd, void* y, qwen3_dtype yd, int rows,
+                int hidden, float eps, hipStream_t s) {
+  KTimer t("rmsnorm", s);
+  hipError_t e = q3::launch_rmsnorm(x, w, wd, y, yd, rows, hidden, eps, s);
+  return e == hipSuccess ? QWEN3_OK : hip_fail(e, "rmsnorm launch");
+}
+
+int run_qk_norm_mrope(const q3::RopeParams& p, int hd, qwen3_dtype dt, hipStream_t s) {
+  KTimer t("qk_norm_mrope", s);
+  hipError_t e = q3::launch_qk_norm_mrope(p, hd, dt, s);
+  return e == hipSuccess ? QWEN3_OK : hip_fail(e, "qk_norm_mrope launch");
+}
+
+int run_attention(const void* q, const void* k, const void* v, void* o, int64_t qs, int64_t ks,
+                  int64_t vs, int64_t os, int S, int nh, int nkv, int hd, float scale, qwen3_dtype dt,
+                  hipStream_t s) {
+  KTimer t("attention", s);
+  hipError_t e;
+  if (dt != QWEN3_F32) {
+    q3::AttnParams p{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), qs, ks, vs, os,
+                     S, nh, nkv, scale * 1.4426950408889634f};
+    e = q3::launch_attention_mfma(p, dt == QWEN3_F16 ? q3::OPH_F16 : q3::OPH_BF16, s);
+  } else {
+    q3::AttnF32Params p{static_cast<const float*>(q), static_cast<const float*>(k),
+                        static_cast<const float*>(v), static_cast<float*>(o), qs, ks, vs, os,
+                        S, nh, nkv, scale};
+    e = q3::launch_attention_f32(p, hd, s);
+  }
+  return e == hipSuccess ? QWEN3_OK : hip_fail(e, "attention launch");
+}
+
+// One projection. For bf16: epi selects the store; for f32 the same meanings on the f32 kernel.
+struct Proj {
+  const void* A; int64_t lda;
+  const void* B0; const void* B1; const void* B2; int nseg0, nseg1; int64_t ldb;
+  void* C; int64_t ldc;
+  const float* R; int64_t ldr;
+  int M, N, K;
+};
+
+// wd: weight dtype; ad: operand dtype (A, MFMA, 16-bit outputs).
+int run_gemm(const char* name, const Proj& g, int epi, qwen3_dtype wd, qwen3_dtype ad, hipStream_t s) {
+  KTimer t(name, s);
+  hipError_t e;
+  if (ad != QWEN3_F32) {
+    q3::GemmParams p{static_cast<const uint16_t*>(g.A), g.lda, static_cast<const uint16_t*>(g.B0),
+                     static_cast<const uint16_t*>(g.B1), static_cast<const uint16_t*>(g.B2),
+                     g.nseg0, g.nseg1, g.ldb, g.C, g.ldc, g.R, g.ldr, g.M, g.N, g.K};
+    e = q3::launch_gemm_mfma(p, epi, ad == QWEN3_F16 ? q3::OPH_F16 : q3::OPH_BF16, wd == QWEN3_BF16, 0, s);
+  } else {
+    // f32 SwiGLU: N counts F outputs (the dual kernel multiplies gate and up together)
+    q3::GemmF32Params p{static_cast<const float*>(g.A), g.lda, static_cast<const float*>(g.B0),
+                        static_cast<const float*>(g.B1), static_cast<const float*>(g.B2),
+                        g.nseg0, g.nseg1, g.ldb, static_cast<float*>(g.C), g.ldc, g.R, g.ldr,
+                        g.M, epi == q3::EPI_SWIGLU_16 ? g.N / 2 : g.N, g.K};
+    e = q3::launch_gemm_f32(p, epi == q3::EPI_SWIGLU_16, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, name);
+  return QWEN3_OK;
+}
+
+// a = silu(x Wg^T) * (x Wu^T) into act [S, F]; then out = [R +] a Wd^T.
+int run_ffn(const void* x, const void* wg, const void* wu, const void* wd, const float* R, void* out,
+            qwen3_dtype out_dt, void* act, int S, int H, int F, qwen3_dtype wdt, qwen3_dtype adt,
+            hipStream_t s) {
+  Proj gu{x, H, wg, wu, nullptr, 0, 0, H, act, F, nullptr, 0, S, 2 * F, H};
+  int st = run_gemm("gemm_gate_up_swiglu", gu, q3::EPI_SWIGLU_16, wdt, adt, s);
+  if (st) return st;
+  Proj dn{act, F, wd, nullptr, nullptr, H, H, F, out, H, R, H, S, H, F};
+  const int epi = out_dt == QWEN3_F32 ? q3::EPI_STORE_F32 : q3::EPI_STORE_16;
+  return run_gemm(R ? "gemm_down_resid" : "gemm_down", dn, epi, wdt, adt, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qwen3_last_error(void) { return g_err.c_str(); }
+
+size_t qwen3_layer_workspace_bytes(const qwen3_layer_cfg* cfg, int32_t seq_len) {
+  if (!cfg || seq_len < 1 || !valid_dtype(cfg->act_dtype)) return 0;
+  return layout(cfg, seq_len).total;
+}
+
+size_t swiglu_ffn_workspace_bytes(int32_t seq_len, int32_t ffn, qwen3_dtype x_dtype) {
+  if (seq_len < 1 || ffn < 1 || !valid_dtype(x_dtype)) return 0;
+  return align256(static_cast<size_t>(seq_len) * ffn * dsize(x_dtype));
+}
+
+int qwen3_layer_prefill(const qwen3_layer_cfg* cfg, const qwen3_layer_weights* w, const void* x_in,
+                        void* x_out, int32_t seq_len, const int32_t* positions,
+                        const int32_t* ds_rows, int32_t n_ds, const void* ds, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  int st = check_cfg(cfg);
+  if (st) return st;
+  if (seq_len < 1) return fail(QWEN3_ERR_INVALID_ARG, "seq_len must be >= 1 (got %d): empty prompt", seq_len);
+  if (!w) return fail(QWEN3_ERR_INVALID_ARG, "weights is NULL");
+  const void* wp[] = {w->attn_norm, w->wq, w->wk, w->wv, w->q_norm, w->k_norm,
+                      w->wo, w->ffn_norm, w->w_gate, w->w_up, w->w_down};
+  const char* wn[] = {"attn_norm", "wq", "wk", "wv", "q_norm", "k_norm",
+                      "wo", "ffn_norm", "w_gate", "w_up", "w_down"};
+  for (int i = 0; i < 11; ++i)
+    if (!wp[i]) return fail(QWEN3_ERR_INVALID_ARG, "weight %s is NULL", wn[i]);
+  if (!x_in || !x_out) return fail(QWEN3_ERR_INVALID_ARG, "x_in / x_out is NULL");
+  if (!positions) return fail(QWEN3_ERR_INVALID_ARG, "positions is NULL");
+  if (n_ds < 0 || n_ds > seq_len)
+    return fail(QWEN3_ERR_INVALID_ARG, "n_ds (%d) must be in [0, seq_len = %d]", n_ds, seq_len);
+  if (n_ds == 0 && ds) return fail(QWEN3_ERR_INVALID_ARG, "a DeepStack slab was given with n_ds == 0");
+  if (n_ds > 0 && (!ds || !ds_rows))
+    return fail(QWEN3_ERR_INVALID_ARG, "n_ds = %d needs both ds_rows and ds", n_ds);
+  const Workspace L = layout(cfg, seq_len);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(QWEN3_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", L.total, workspace_bytes,
+                workspace ? "" : ", NULL pointer");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(QWEN3_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  {
+    const size_t xb = static_cast<size_t>(seq_len) * cfg->hidden * 4;
+    const char* a = static_cast<const char*>(x_in);
+    const char* b = static_cast<const char*>(x_out);
+    if (a != b && a < b + xb && b < a + xb)
+      return fail(QWEN3_ERR_INVALID_ARG, "x_out partially overlaps x_in (only x_out == x_in is allowed)");
+  }
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const qwen3_dtype wdt = cfg->wdtype, dt = cfg->act_dtype;
+  const int S = seq_len, H = cfg->hidden, nh = cfg->n_heads, nkv = cfg->n_kv_heads, hd = cfg->head_dim;
+  const int F = cfg->ffn;
+  const int q_dim = nh * hd, kv_dim = nkv * hd, qkv_dim = q_dim + 2 * kv_dim;
+  const size_t e = dsize(dt);
+  char* ws = static_cast<char*>(workspace);
+  void* xn = ws + L.xn;
+  char* qkv = ws + L.qkv;
+  void* o = ws + L.o;
+  void* act = ws + L.act;
+  const float* x = static_cast<const float*>(x_in);
+  float* y = static_cast<float*>(x_out);
+
+  // a1: input RMSNorm
+  if ((st = run_rmsnorm(x, w->attn_norm, wdt, xn, dt, S, H, cfg->rms_eps, s))) return st;
+  // a2: q | k | v = xn [Wq; Wk; Wv]^T in one product, token-major [S, q_dim + 2 kv_dim]
+  {
+    Proj p{xn, H, w->wq, w->wk, w->wv, q_dim, q_dim + kv_dim, H, qkv, qkv_dim, nullptr, 0, S, qkv_dim, H};
+    if ((st = run_gemm("gemm_qkv", p, dt == QWEN3_F32 ? q3::EPI_STORE_F32 : q3::EPI_STORE_16, wdt, dt, s)))
+      return st;
+  }
+  // a3+a4: per-head RMSNorm and interleaved MRoPE on q and k, in place
+  {
+    q3::RopeParams p{qkv, qkv + static_cast<size_t>(q_dim) * e, qkv_dim, qkv_dim, S, nh, nkv,
+                     w->q_norm, w->k_norm, wdt, positions, cfg->rms_eps,
+                     std::log2(static_cast<double>(cfg->rope_theta)), cfg->mrope_section[1],
+                     cfg->mrope_section[2]};
+    if ((st = run_qk_norm_mrope(p, hd, dt, s))) return st;
+  }
+  // a5: causal GQA attention -> o [S, q_dim]
+  if ((st = run_attention(qkv, qkv + static_cast<size_t>(q_dim) * e, qkv + static_cast<size_t>(q_dim + kv_dim) * e,
+                          o, qkv_dim, qkv_dim, qkv_dim, q_dim, S, nh, nkv, hd,
+                          1.0f / std::sqrt(static_cast<float>(hd)), dt, s)))
+    return st;
+  // a6: y1 = x + o Wo^T (fp32, into x_out)
+  {
+    Proj p{o, q_dim, w->wo, nullptr, nullptr, H, H, q_dim, y, H, x, H, S, H, q_dim};
+    if ((st = run_gemm("gemm_o_resid", p, q3::EPI_STORE_F32, wdt, dt, s))) return st;
+  }
+  // a7: yn = RMSNorm(y1, ffn_norm) (reuses the xn buffer)
+  if ((st = run_rmsnorm(y, w->ffn_norm, wdt, xn, dt, S, H, cfg->rms_eps, s))) return st;
+  // a8 + a9: y2 = y1 + (silu(yn Wg^T) * (yn Wu^T)) Wd^T
+  if ((st = run_ffn(xn, w->w_gate, w->w_up, w->w_down, y, y, QWEN3_F32, act, S, H, F, wdt, dt, s))) return st;
+  // a10: DeepStack rows
+  if (n_ds > 0) {
+    KTimer t("deepstack_add", s);
+    hipError_t he = q3::launch_deepstack_add(y, ds_rows, ds, wdt, n_ds, S, H, s);
+    if (he != hipSuccess) return hip_fail(he, "deepstack_add launch");
+  }
+  return QWEN3_OK;
+}
+
+int qk_norm_mrope(void* q, void* k, int32_t seq_len, int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
+                  const void* q_norm, const void* k_norm, float eps, const int32_t* positions, float theta,
+                  const int32_t mrope_section[3], qwen3_dtype dtype, qwen3_dtype norm_dtype, void* stream) {
+  if (!valid_dtype(dtype) || !valid_dtype(norm_dtype))
+    return fail(QWEN3_ERR_INVALID_ARG, "dtype (%d, %d) is not a qwen3_dtype", dtype, norm_dtype);
+  if (seq_len < 1) return fail(QWEN3_ERR_INVALID_ARG, "seq_len must be >= 1 (got %d)", seq_len);
+  if (n_heads < 0 || n_kv_heads < 0) return fail(QWEN3_ERR_INVALID_ARG, "head counts must be >= 0");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(QWEN3_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", head_dim);
+  int st = check_sections(mrope_section, head_dim);
+  if (st) return st;
+  if ((n_heads > 0 && (!q || !q_norm)) || (n_kv_heads > 0 && (!k || !k_norm)) || !positions)
+    return fail(QWEN3_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (!(eps >= 0.f) || !(theta > 1.f)) return fail(QWEN3_ERR_INVALID_ARG, "eps must be >= 0 and theta > 1");
+  q3::RopeParams p{q, k, static_cast<int64_t>(n_heads) * head_dim, static_cast<int64_t>(n_kv_heads) * head_dim,
+                   seq_len, n_heads, n_kv_heads, q_norm, k_norm, norm_dtype, positions, eps,
+                   std::log2(static_cast<double>(theta)), mrope_section[1], mrope_section[2]};
+  return run_qk_norm_mrope(p, head_dim, dtype, static_cast<hipStream_t>(stream));
+}
+
+int gqa_causal_attention(const void* q, const void* k, const void* v, void* out, int32_t seq_len,
+                         int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, float scale,
+                         qwen3_dtype dtype, void* stream) {
+  if (!valid_dtype(dtype)) return fail(QWEN3_ERR_INVALID_ARG, "dtype %d is not a qwen3_dtype", dtype);
+  if (seq_len < 1) return fail(QWEN3_ERR_INVALID_ARG, "seq_len must be >= 1 (got %d)", seq_len);
+  int st = check_heads(n_heads, n_kv_heads, head_dim, dtype);
+  if (st) return st;
+  if (!q || !k || !v || !out) return fail(QWEN3_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(QWEN3_ERR_INVALID_ARG, "scale must be finite and > 0");
+  return run_attention(q, k, v, out, static_cast<int64_t>(n_heads) * head_dim,
+                       static_cast<int64_t>(n_kv_heads) * head_dim, static_cast<int64_t>(n_kv_heads) * head_dim,
+                       static_cast<int64_t>(n_heads) * head_dim, seq_len, n_heads, n_kv_heads, head_dim, scale,
+                       dtype, static_cast<hipStream_t>(stream));
+}
+
+int swiglu_ffn(const void* x_normed, const void* w_gate, const void* w_up, const void* w_down,
+               const void* residual, void* out, int32_t seq_len, int32_t hidden, int32_t ffn,
+               qwen3_dtype wdtype, qwen3_dtype x_dtype, qwen3_dtype out_dtype, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  int st = check_formats(wdtype, x_dtype);
+  if (st) return st;
+  if (!valid_dtype(out_dtype)) return fail(QWEN3_ERR_INVALID_ARG, "out_dtype %d is not a qwen3_dtype", out_dtype);
+  if (seq_len < 1) return fail(QWEN3_ERR_INVALID_ARG, "seq_len must be >= 1 (got %d)", seq_len);
+  if (hidden < 256 || hidden % 256 != 0)
+    return fail(QWEN3_ERR_UNSUPPORTED, "hidden (%d) must be a positive multiple of 256", hidden);
+  if (ffn < 128 || ffn % 128 != 0) return fail(QWEN3_ERR_UNSUPPORTED, "ffn (%d) must be a positive multiple of 128", ffn);
+  if (!x_normed || !w_gate || !w_up || !w_down || !out) return fail(QWEN3_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (out_dtype != QWEN3_F32 && (residual || out_dtype != x_dtype))
+    return fail(QWEN3_ERR_UNSUPPORTED, "a 16-bit output must have x_dtype and no residual");
+  const size_t need = swiglu_ffn_workspace_bytes(seq_len, ffn, x_dtype);
+  if (!workspace || workspace_bytes < need)
+    return fail(QWEN3_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+  return run_ffn(x_normed, w_gate, w_up, w_down, static_cast<const float*>(residual), out, out_dtype,
+                 workspace, seq_len, hidden, ffn, wdtype, x_dtype, static_cast<hipStream_t>(stream));
+}
+
+int rms_norm_rows(const float* x, const void* w, void* y, int32_t rows, int32_t hidden, float eps,
+                  qwen3_dtype w_dtype, qwen3_dtype y_dtype, void* stream) {
+  if (!valid_dtype(w_dtype) || !valid_dtype(y_dtype)) return fail(QWEN3_ERR_INVALID_ARG, "bad dtype");
+  if (rows < 1) return fail(QWEN3_ERR_INVALID_ARG, "rows must be >= 1 (got %d)", rows);
+  if (hidden < 256 || hidden % 256 != 0 || hidden > 16384)
+    return fail(QWEN3_ERR_UNSUPPORTED, "hidden (%d) must be a multiple of 256 in [256, 16384]", hidden);
+  if (!x || !w || !y) return fail(QWEN3_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (!(eps >= 0.f)) return fail(QWEN3_ERR_INVALID_ARG, "eps must be >= 0");
+  return run_rmsnorm(x, w, w_dtype, y, y_dtype, rows, hidden, eps, static_cast<hipStream_t>(stream));
+}
+
+int qwen3_timing_enable(int enable) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  g_timing = enable != 0;
+  return QWEN3_OK;
+}
+
+int qwen3_timing_collect(qwen3_kernel_time* out, int32_t max_entries, int32_t* n_out) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  std::map<std::string, std::pair<int, double>> agg;
+  std::vector<std::string> order;
+  for (int i = 0; i < g_used; ++i) {
+    hipError_t e = hipEventSynchronize(g_events[2 * i + 1]);
+    if (e != hipSuccess) {
+      g_used = 0;
+      return hip_fail(e, "timing event synchronize");
+    }
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, g_events[2 * i], g_events[2 * i + 1]);
+    if (e != hipSuccess) {
+      g_used = 0;
+      return hip_fail(e, "timing elapsed time");
+    }
+    const std::string name = g_slot_name[i];
+    if (!agg.count(name)) order.push_back(name);
+    agg[name].first += 1;
+    agg[name].second += ms;
+  }
+  g_used = 0;
+  int n = 0;
+  for (const auto& name : order) {
+    if (n >= max_entries) break;
+    if (out) {
+      std::memset(&out[n], 0, sizeof(out[n]));
+      std::strncpy(out[n].name, name.c_str(), sizeof(out[n].name) - 1);
+      out[n].launches = agg[name].first;
+      out[n].total_ms = agg[name].second;
+    }
+    ++n;
+  }
+  if (n_out) *n_out = n;
+  return QWEN3_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,315 @@
+// 16-bit MFMA GEMM for the layer's projections: C = A · B^T with A [M, K] activations and
+// B [N, K] weights in torch nn.Linear layout, fp32 accumulation on the gfx950 32x32x16 MFMA.
+//
+// Operand formats: A and the MFMA run in one 16-bit format (fp16 or bf16). B is stored in
+// that format, or in bf16 while A is fp16: then each B chunk is converted to fp16 in
+// registers between its global load and its LDS store (exact for |w| in [2^-17, 65504]).
+//
+// Uses (hf2q 0.1.1, qwen3vl_text/forward.rs, module doc; cortiq-engine 0.8.21, qwen3te.rs,
+// `encode_with_images`):
+//   QKV      EPI_STORE_16, B rows drawn from Wq, Wk, Wv in turn (one launch for all three)
+//   o-proj   EPI_STORE_F32 with the residual: y1 = x + o Wo^T
+//   gate/up  EPI_SWIGLU_16: a = silu(yn Wg^T) * (yn Wu^T), the two products in one tile
+//   down     EPI_STORE_F32 with the residual: y2 = y1 + a Wd^T
+//
+// Tiling for gfx950 (256 CUs in 8 XCDs, 160 KiB LDS per CU):
+//   workgroup tile 256 x (64*NB), K step 64, 4 waves in a 2 x 2 grid, each wave 128 x (32*NB)
+//   as 4 x NB MFMA 32x32 blocks (NB = 4: 256 fp32 accumulators per lane, in AGPRs);
+//   A and B tiles staged through a double-buffered LDS ring (global -> registers -> LDS): the
+//   next K step's global loads are issued before this step's MFMAs and stored to the other
+//   LDS buffer after them, one barrier per K step;
+//   MFMA operand fragments are read from LDS one 16-wide K sub-step ahead of the MFMAs that
+//   use them, so LDS latency overlaps matrix work;
+//   16-byte LDS chunks XOR-swizzled by row, so the fragment reads (32 rows, one chunk each)
+//   and the tile stores are free of bank conflicts;
+//   workgroup ids remapped so each XCD (ids congruent mod 8) owns a compact band of tiles
+//   sharing A rows and B columns in its own L2.
+#include "common.h"
+#include "kernels.h"
+
+#ifndef Q3_GEMM_SCHED
+#define Q3_GEMM_SCHED 1
+#endif
+
+namespace q3 {
+
+constexpr int kBM = 256;
+constexpr int kBK = 64;
+constexpr int kGemmThreads = 256;
+
+__device__ __forceinline__ int swz8(int row) { return (row ^ (row >> 3)) & 7; }
+
+// Workgroup id -> (tile row, tile column). Hardware dispatches ids round-robin over the 8
+// XCDs; ids are first regrouped so that XCD x gets a contiguous range of logical ids, then
+// logical ids walk GM tile-rows at a time so concurrently running tiles share operands.
+__device__ __forceinline__ void tile_coords(int bid, int nwg, int tiles_m, int tiles_n, int& tm,
+                                            int& tn) {
+  int L = bid;
+  if ((nwg & 7) == 0) L = (bid & 7) * (nwg >> 3) + (bid >> 3);
+  constexpr int GM = 8;
+  const int per_group = GM * tiles_n;
+  const int group = L / per_group;
+  const int first_m = group * GM;
+  const int gsz = min(tiles_m - first_m, GM);
+  const int in_group = L - group * per_group;
+  tm = first_m + in_group % gsz;
+  tn = in_group / gsz;
+}
+
+template <int NB, int EPI>
+__device__ __forceinline__ const uint16_t* b_row(const GemmParams& p, int tn, int r) {
+  constexpr int BN = 64 * NB;
+  if (EPI == EPI_SWIGLU_16) {
+    // Tile tn covers F columns [tn*BN/2, tn*BN/2 + BN/2). LDS rows come in 64-row segments
+    // gate, up, gate, up, ... so that each wave's 128 columns hold 64 gate columns followed by
+    // the 64 up columns of the same F range: the SwiGLU pairing is then lane-local.
+    const int seg = r >> 6;
+    const int f = tn * (BN / 2) + (seg >> 1) * 64 + (r & 63);
+    return ((seg & 1) ? p.B1 : p.B0) + static_cast<int64_t>(f) * p.ldb;
+  } else {
+    const int n = tn * BN + r;
+    if (n < p.nseg0) return p.B0 + static_cast<int64_t>(n) * p.ldb;
+    if (n < p.nseg1) return p.B1 + static_cast<int64_t>(n - p.nseg0) * p.ldb;
+    return p.B2 + static_cast<int64_t>(n - p.nseg1) * p.ldb;
+  }
+}
+
+__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
+
+template <int NB, int EPI, int OP, bool CVT>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void gemm_mfma_kernel(const GemmParams p) {
+  using F = Fmt<OP>;
+  constexpr int BN = 64 * NB;
+  constexpr int ACH = kBM * 8 / kGemmThreads;  // 16-byte chunks per thread, A tile (8)
+  constexpr int BCH = BN * 8 / kGemmThreads;   // 16-byte chunks per thread, B tile (2*NB)
+  __shared__ u32x4 As[2][kBM * 8];
+  __shared__ u32x4 Bs[2][BN * 8];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1;
+  const int wn = wave & 1;
+  const int tiles_m = (p.M + kBM - 1) / kBM;
+  const int tiles_n = p.N / BN;
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+
+  const int lrow = tid >> 3;  // 0..31
+  const int lch = tid & 7;    // 16-byte chunk within a 64-wide K step
+
+  // A rows: element offsets from A (rows past M are clamped: read, never stored)
+  uint32_t a_off[ACH];
+#pragma unroll
+  for (int j = 0; j < ACH; ++j) {
+    const int r = min(tm * kBM + lrow + 32 * j, p.M - 1);
+    a_off[j] = static_cast<uint32_t>(r) * static_cast<uint32_t>(p.lda) + lch * 8;
+  }
+  const uint16_t* b_src[BCH];
+#pragma unroll
+  for (int j = 0; j < BCH; ++j) b_src[j] = b_row<NB, EPI>(p, tn, lrow + 32 * j) + lch * 8;
+
+  // LDS slots this thread stores (same every K step)
+  int st_a[ACH], st_b[BCH];
+#pragma unroll
+  for (int j = 0; j < ACH; ++j) {
+    const int row = lrow + 32 * j;
+    st_a[j] = row * 8 + (lch ^ swz8(row));
+  }
+#pragma unroll
+  for (int j = 0; j < BCH; ++j) {
+    const int row = lrow + 32 * j;
+    st_b[j] = row * 8 + (lch ^ swz8(row));
+  }
+  // LDS rows this lane reads fragments from
+  const int fr = lane & 31;
+  const int fh = lane >> 5;
+
+  u32x4 ra[ACH], rb[BCH];
+  f32x16 acc[4][NB];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NB; ++ni)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.f;
+
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int j = 0; j < ACH; ++j) ra[j] = *reinterpret_cast<const u32x4*>(p.A + a_off[j] + k0);
+#pragma unroll
+    for (int j = 0; j < BCH; ++j) rb[j] = *reinterpret_cast<const u32x4*>(b_src[j] + k0);
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < ACH; ++j) As[buf][st_a[j]] = ra[j];
+#pragma unroll
+    for (int j = 0; j < BCH; ++j) {
+      u32x4 v = rb[j];
+      if (CVT) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = bf16x2_to_f16x2(v[e]);
+      }
+      Bs[buf][st_b[j]] = v;
+    }
+  };
+  auto fread = [&](int buf, int ks, u32x4 (&fa)[4], u32x4 (&fb)[NB]) {
+    const int ch = ks * 2 + fh;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      const int row = wm * 128 + mi * 32 + fr;
+      fa[mi] = As[buf][row * 8 + (ch ^ swz8(row))];
+    }
+#pragma unroll
+    for (int ni = 0; ni < NB; ++ni) {
+      const int row = wn * 32 * NB + ni * 32 + fr;
+      fb[ni] = Bs[buf][row * 8 + (ch ^ swz8(row))];
+    }
+  };
+
+  const int nk = p.K / kBK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    // next K step's tile (the last step re-reads its own tile: same addresses, no branch)
+    gload(kt + 1 < nk ? (kt + 1) * kBK : kt * kBK);
+    u32x4 fa[2][4], fb[2][NB];
+    fread(buf, 0, fa[0], fb[0]);
+#pragma unroll
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+      if (ks + 1 < kBK / 16) fread(buf, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NB; ++ni)
+          acc[mi][ni] = F::mfma(fa[ks & 1][mi], fb[ks & 1][ni], acc[mi][ni]);
+#if Q3_GEMM_SCHED
+      if (ks + 1 < kBK / 16) {
+        // interleave the next sub-step's fragment reads with this sub-step's MFMAs
+#pragma unroll
+        for (int i = 0; i < 4 + NB; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 DS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4 * NB - (4 + NB), 0);
+      }
+#endif
+    }
+    lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // Epilogue. Accumulator element e of block (mi, ni) in lane l holds
+  // row 8*(e/4) + 4*(l/32) + e%4 and column l%32 of that 32x32 block.
+  const int col_in_blk = lane & 31;
+  const int row_base = tm * kBM + wm * 128 + 4 * (lane >> 5);
+  if (EPI == EPI_SWIGLU_16) {
+    uint16_t* C = static_cast<uint16_t*>(p.C);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NB / 2; ++ni) {
+        const int f = tn * (BN / 2) + wn * 64 + ni * 32 + col_in_blk;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int m = row_base + mi * 32 + 8 * (e >> 2) + (e & 3);
+          if (m < p.M) {
+            const float g = acc[mi][ni][e];
+            const float u = acc[mi][ni + NB / 2][e];
+            C[static_cast<int64_t>(m) * p.ldc + f] = F::from_f32(silu_f(g) * u);
+          }
+        }
+      }
+  } else {
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NB; ++ni) {
+        const int n = tn * BN + wn * 32 * NB + ni * 32 + col_in_blk;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int m = row_base + mi * 32 + 8 * (e >> 2) + (e & 3);
+          if (m < p.M) {
+            const float v = acc[mi][ni][e];
+            if (EPI == EPI_STORE_16) {
+              static_cast<uint16_t*>(p.C)[static_cast<int64_t>(m) * p.ldc + n] = F::from_f32(v);
+            } else {
+              float r = 0.f;
+              if (p.R) r = p.R[static_cast<int64_t>(m) * p.ldr + n];
+              static_cast<float*>(p.C)[static_cast<int64_t>(m) * p.ldc + n] = r + v;
+            }
+          }
+        }
+      }
+  }
+}
+
+int gemm_pick_nb(int M, int N, int epi) {
+  if (epi == EPI_SWIGLU_16) return 4;
+  // Relative per-tile efficiency of the wider tiles (operand reuse), weighed against how
+  // evenly the tile count fills whole rounds of 256 CUs.
+  const double rel[5] = {0, 0, 0.85, 0.95, 1.0};
+  const int tiles_m = (M + kBM - 1) / kBM;
+  int best = 0;
+  double best_score = -1;
+  for (int nb = 4; nb >= 2; --nb) {
+    if (N % (64 * nb) != 0) continue;
+    const int64_t tiles = static_cast<int64_t>(tiles_m) * (N / (64 * nb));
+    const int64_t rounds = (tiles + 255) / 256;
+    const double score = rel[nb] * static_cast<double>(tiles) / static_cast<double>(rounds * 256);
+    if (score > best_score + 1e-9) {
+      best_score = score;
+      best = nb;
+    }
+  }
+  return best;
+}
+
+template <int NB, int EPI, int OP, bool CVT>
+static hipError_t launch_t(const GemmParams& p, hipStream_t s) {
+  const int tiles = ((p.M + kBM - 1) / kBM) * (p.N / (64 * NB));
+  gemm_mfma_kernel<NB, EPI, OP, CVT><<<tiles, kGemmThreads, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+template <int EPI, int OP, bool CVT>
+static hipError_t launch_nb(const GemmParams& p, int nb, hipStream_t s) {
+  if (EPI == EPI_SWIGLU_16) return nb == 4 ? launch_t<4, EPI, OP, CVT>(p, s) : hipErrorInvalidValue;
+  if (nb == 4) return launch_t<4, EPI, OP, CVT>(p, s);
+  if (nb == 3) return launch_t<3, EPI, OP, CVT>(p, s);
+  if (nb == 2) return launch_t<2, EPI, OP, CVT>(p, s);
+  return hipErrorInvalidValue;
+}
+
+template <int OP, bool CVT>
+static hipError_t launch_epi(const GemmParams& p, int epi, int nb, hipStream_t s) {
+  switch (epi) {
+    case EPI_STORE_16: return launch_nb<EPI_STORE_16, OP, CVT>(p, nb, s);
+    case EPI_STORE_F32: return launch_nb<EPI_STORE_F32, OP, CVT>(p, nb, s);
+    case EPI_SWIGLU_16: return launch_nb<EPI_SWIGLU_16, OP, CVT>(p, nb, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_gemm_mfma(const GemmParams& p, int epi, int op, bool b_bf16, int nb, hipStream_t s) {
+  if (p.M <= 0) return hipSuccess;
+  if (nb == 0) nb = gemm_pick_nb(p.M, p.N, epi);
+  if (nb < 2 || nb > 4 || p.N % (64 * nb) != 0 || p.K % kBK != 0 || p.K <= 0)
+    return hipErrorInvalidValue;
+  // A tile offsets are 32-bit element offsets
+  if (static_cast<int64_t>(p.M) * p.lda >= (int64_t(1) << 32)) return hipErrorInvalidValue;
+  if (op == OP_BF16) {
+    if (!b_bf16) return hipErrorInvalidValue;  // bf16 products take bf16 weights
+    return launch_epi<OP_BF16, false>(p, epi, nb, s);
+  }
+  if (op == OP_F16) {
+    return b_bf16 ? launch_epi<OP_F16, true>(p, epi, nb, s) : launch_epi<OP_F16, false>(p, epi, nb, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace q3

@@ -1,0 +1,95 @@
+// Host-side launchers of the gfx950 kernels. Each returns the HIP error of its launch.
+// Shapes are validated by the C-ABI layer (capi.hip) before any launcher is called; the
+// launchers only re-check the preconditions that the kernels' index arithmetic relies on.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q3 {
+
+// Element storage types; the values match qwen3_dtype in the public header.
+enum DType : int { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
+
+// ---- RMSNorm (a row per workgroup) -------------------------------------------------------
+// y[r] = x[r] * rsqrt(mean(x[r]^2) + eps) * w; x f32 [rows, H]; w and y of the given types.
+hipError_t launch_rmsnorm(const float* x, const void* w, int w_dt, void* y, int y_dt, int rows,
+                          int hidden, float eps, hipStream_t s);
+
+// ---- DeepStack rows add -------------------------------------------------------------------
+// y[rows[i], :] += ds[i, :] for i < n; entries outside [0, S) or not above their predecessor
+// are skipped. y f32 [S, H]; ds [n, H] of ds_dt.
+hipError_t launch_deepstack_add(float* y, const int32_t* rows, const void* ds, int ds_dt, int n,
+                                int S, int hidden, hipStream_t s);
+
+// ---- per-head RMSNorm + interleaved MRoPE, in place ---------------------------------------
+struct RopeParams {
+  void* q;            // token t, head h at q + t*q_stride + h*hd
+  void* k;            // token t, kv head h at k + t*k_stride + h*hd
+  int64_t q_stride, k_stride;  // elements between consecutive tokens
+  int S, nh, nkv;
+  const void* q_norm;
+  const void* k_norm;
+  int norm_dt;         // storage type of q_norm / k_norm
+  const int32_t* pos;  // [3, S]
+  float eps;
+  double log2_theta;
+  int sec_h, sec_w;    // interleave bounds: h pairs i%3==1 && i<3*sec_h, w pairs i%3==2 && i<3*sec_w
+};
+hipError_t launch_qk_norm_mrope(const RopeParams& p, int head_dim, int data_dt, hipStream_t s);
+
+// ---- 16-bit MFMA GEMM:  C[m, n] = sum_k A[m, k] * B[n, k]  --------------------------------
+enum GemmEpilogue { EPI_STORE_16 = 0, EPI_STORE_F32 = 1, EPI_SWIGLU_16 = 2 };
+enum Op16Host : int { OPH_BF16 = 0, OPH_F16 = 1 };
+struct GemmParams {
+  const uint16_t* A;   // [M, K] 16-bit, row stride lda
+  int64_t lda;
+  // B rows come from up to three row-major [*, K] matrices (stride ldb): output column n < nseg0
+  // reads B0 row n, n < nseg1 reads B1 row n - nseg0, otherwise B2 row n - nseg1. For
+  // EPI_SWIGLU_16, B0 is W_gate and B1 is W_up, both [F, K].
+  const uint16_t* B0;
+  const uint16_t* B1;
+  const uint16_t* B2;
+  int nseg0, nseg1;
+  int64_t ldb;
+  void* C;             // [M, N] (EPI_SWIGLU_16: [M, N/2]) with row stride ldc
+  int64_t ldc;
+  const float* R;      // EPI_STORE_F32 only: residual added to the product, or nullptr
+  int64_t ldr;
+  int M, N, K;         // N: product columns (for SwiGLU, 2F: gate and up together)
+};
+// op: OPH_BF16 or OPH_F16, the format of A, of the MFMA and of 16-bit outputs. b_bf16: B is
+// stored as bf16 (converted to fp16 on the way to LDS when op is fp16); otherwise B is in op's
+// format. nb: 32-column MFMA blocks per wave along N (tile width 64*nb); 0 picks one.
+hipError_t launch_gemm_mfma(const GemmParams& p, int epi, int op, bool b_bf16, int nb, hipStream_t s);
+int gemm_pick_nb(int M, int N, int epi);
+
+// ---- 16-bit causal GQA flash attention, head_dim 128 --------------------------------------
+struct AttnParams {
+  const uint16_t* q; const uint16_t* k; const uint16_t* v; uint16_t* o;
+  int64_t q_stride, k_stride, v_stride, o_stride;  // elements between consecutive tokens
+  int S, nh, nkv;
+  float scale_log2;    // softmax scale * log2(e)
+};
+hipError_t launch_attention_mfma(const AttnParams& p, int op, hipStream_t s);
+
+// ---- fp32 path -----------------------------------------------------------------------------
+struct GemmF32Params {
+  const float* A; int64_t lda;
+  const float* B0; const float* B1; const float* B2; int nseg0, nseg1; int64_t ldb;
+  float* C; int64_t ldc;
+  const float* R; int64_t ldr;
+  int M, N, K;
+};
+// dual = false: C = A B^T (+ R); dual = true: C[M, N] = silu(A B0^T) * (A B1^T), N = F.
+hipError_t launch_gemm_f32(const GemmF32Params& p, bool dual, hipStream_t s);
+
+struct AttnF32Params {
+  const float* q; const float* k; const float* v; float* o;
+  int64_t q_stride, k_stride, v_stride, o_stride;
+  int S, nh, nkv;
+  float scale;
+};
+hipError_t launch_attention_f32(const AttnF32Params& p, int head_dim, hipStream_t s);
+
+}  // namespace q3

@@ -1,0 +1,212 @@
+// Streaming (HBM-bound) kernels: row RMSNorm, the fused per-head q/k RMSNorm + interleaved
+// MRoPE rotation, and the DeepStack row add.
+//
+// RMSNorm: cortiq-engine 0.8.21, qwen3te.rs, `rms_norm_into` (mean of squares, eps inside the
+// square root, plain weight). q/k norm + rotation: the same page, `norm_rope` (norm before the
+// rotation; split-half pairs (i, i + hd/2); Qwen3-VL's interleaved axis choice per pair).
+// DeepStack: hf2q 0.1.1, qwen3vl_text/forward.rs, Phase D (add on image-token rows only).
+#include "common.h"
+#include "kernels.h"
+
+#include <type_traits>
+
+namespace q3 {
+
+// ------------------------------------------------------------------------------------------
+// RMSNorm: one 256-thread workgroup per row; the row stays in registers between the
+// sum-of-squares pass and the scaling pass, so x is read from HBM once.
+constexpr int kNormThreads = 256;
+constexpr int kNormMaxVec = 16;  // float4 per thread: hidden <= 16384
+
+// Load 4 consecutive elements (index 4c .. 4c+3) of a vector stored as dtype DT, as floats.
+template <int DT>
+__device__ __forceinline__ f32x4 load4(const void* p, int c) {
+  if (DT == DT_F32) return reinterpret_cast<const f32x4*>(p)[c];
+  const uint2 w = reinterpret_cast<const uint2*>(p)[c];
+  if (DT == DT_BF16)
+    return f32x4{bf2f(w.x & 0xFFFF), bf2f(w.x >> 16), bf2f(w.y & 0xFFFF), bf2f(w.y >> 16)};
+  return f32x4{h2f(w.x & 0xFFFF), h2f(w.x >> 16), h2f(w.y & 0xFFFF), h2f(w.y >> 16)};
+}
+
+template <int DT>
+__device__ __forceinline__ void store4(void* p, int64_t c, f32x4 v) {
+  if (DT == DT_F32) {
+    reinterpret_cast<f32x4*>(p)[c] = v;
+  } else {
+    uint2 o;
+    o.x = DT == DT_BF16 ? pack2bf(v[0], v[1]) : Fmt<OP_F16>::pack2(v[0], v[1]);
+    o.y = DT == DT_BF16 ? pack2bf(v[2], v[3]) : Fmt<OP_F16>::pack2(v[2], v[3]);
+    reinterpret_cast<uint2*>(p)[c] = o;
+  }
+}
+
+template <int W_DT, int Y_DT>
+__global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(const float* __restrict__ x,
+                                                               const void* __restrict__ w,
+                                                               void* __restrict__ y, int hidden,
+                                                               float eps) {
+  const int row = blockIdx.x;
+  const int nv = hidden >> 2;
+  const f32x4* xr = reinterpret_cast<const f32x4*>(x + static_cast<int64_t>(row) * hidden);
+  f32x4 v[kNormMaxVec];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < kNormMaxVec; ++i) {
+    const int c = threadIdx.x + i * kNormThreads;
+    if (c < nv) {
+      v[i] = __builtin_nontemporal_load(xr + c);
+      ss += v[i][0] * v[i][0] + v[i][1] * v[i][1] + v[i][2] * v[i][2] + v[i][3] * v[i][3];
+    }
+  }
+  __shared__ float red[kNormThreads / 64];
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int i = 0; i < kNormThreads / 64; ++i) tot += red[i];
+  const float r = 1.0f / sqrtf(tot / static_cast<float>(hidden) + eps);
+#pragma unroll
+  for (int i = 0; i < kNormMaxVec; ++i) {
+    const int c = threadIdx.x + i * kNormThreads;
+    if (c < nv) {
+      const f32x4 g = load4<W_DT>(w, c);
+      const f32x4 o = {v[i][0] * r * g[0], v[i][1] * r * g[1], v[i][2] * r * g[2], v[i][3] * r * g[3]};
+      store4<Y_DT>(y, static_cast<int64_t>(row) * nv + c, o);
+    }
+  }
+}
+
+template <int W_DT>
+static hipError_t rms_launch_y(const float* x, const void* w, void* y, int y_dt, int rows, int hidden,
+                               float eps, hipStream_t s) {
+  dim3 grid(rows), block(kNormThreads);
+  switch (y_dt) {
+    case DT_F32: rmsnorm_kernel<W_DT, DT_F32><<<grid, block, 0, s>>>(x, w, y, hidden, eps); break;
+    case DT_BF16: rmsnorm_kernel<W_DT, DT_BF16><<<grid, block, 0, s>>>(x, w, y, hidden, eps); break;
+    case DT_F16: rmsnorm_kernel<W_DT, DT_F16><<<grid, block, 0, s>>>(x, w, y, hidden, eps); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(const float* x, const void* w, int w_dt, void* y, int y_dt, int rows,
+                          int hidden, float eps, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (hidden % 4 != 0 || hidden > 4 * kNormThreads * kNormMaxVec) return hipErrorInvalidValue;
+  switch (w_dt) {
+    case DT_F32: return rms_launch_y<DT_F32>(x, w, y, y_dt, rows, hidden, eps, s);
+    case DT_BF16: return rms_launch_y<DT_BF16>(x, w, y, y_dt, rows, hidden, eps, s);
+    case DT_F16: return rms_launch_y<DT_F16>(x, w, y, y_dt, rows, hidden, eps, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// DeepStack: one workgroup per slab row.
+__device__ __forceinline__ float load_elem(const void* p, int64_t i, int dt) {
+  if (dt == DT_F32) return static_cast<const float*>(p)[i];
+  const uint16_t h = static_cast<const uint16_t*>(p)[i];
+  return dt == DT_BF16 ? bf2f(h) : h2f(h);
+}
+
+__global__ __launch_bounds__(256) void deepstack_add_kernel(float* __restrict__ y,
+                                                            const int32_t* __restrict__ rows,
+                                                            const void* __restrict__ ds, int ds_dt,
+                                                            int S, int hidden) {
+  const int i = blockIdx.x;
+  const int r = rows[i];
+  const bool ok = r >= 0 && r < S && (i == 0 || rows[i - 1] < r);
+  if (!ok) return;
+  float* yr = y + static_cast<int64_t>(r) * hidden;
+  for (int c = threadIdx.x; c < hidden; c += 256) {
+    yr[c] += load_elem(ds, static_cast<int64_t>(i) * hidden + c, ds_dt);
+  }
+}
+
+hipError_t launch_deepstack_add(float* y, const int32_t* rows, const void* ds, int ds_dt, int n,
+                                int S, int hidden, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  deepstack_add_kernel<<<n, 256, 0, s>>>(y, rows, ds, ds_dt, S, hidden);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// q/k RMSNorm + interleaved MRoPE. One 256-thread workgroup per token. A lane owns rotation
+// pair i = (x_i, x_{i+hd/2}) of one head row, so the rotation is lane-local; the hd/2 lanes of
+// a row reduce the sum of squares with cross-lane shuffles. The angle of pair i depends on
+// the token only (not the head), so each lane forms cos/sin once and applies them to every
+// q and k head of the token.
+//
+// Angle precision: phi = pos * theta^(-2i/hd) is formed in double and reduced to
+// [-pi, pi] in double before the single-precision sincos, so its error does not grow with
+// the position.
+template <int DT, int HD>
+__global__ __launch_bounds__(256) void qk_norm_mrope_kernel(const RopeParams p) {
+  constexpr int HALF = HD / 2;
+  constexpr int ROWS_PER_WAVE = 64 / HALF;          // 1 (hd 128) or 2 (hd 64)
+  constexpr int ROWS_PER_PASS = 4 * ROWS_PER_WAVE;  // 4 waves
+  typedef typename std::conditional<DT == DT_F32, float, uint16_t>::type T;
+  const int s = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int i = lane % HALF;
+  const int sub = (threadIdx.x >> 6) * ROWS_PER_WAVE + lane / HALF;
+
+  int axis = 0;
+  if (i % 3 == 1 && i < 3 * p.sec_h) axis = 1;
+  else if (i % 3 == 2 && i < 3 * p.sec_w) axis = 2;
+  const double pos = static_cast<double>(p.pos[static_cast<int64_t>(axis) * p.S + s]);
+  const double inv = exp2(-(2.0 * i / HD) * p.log2_theta);
+  const double phi = pos * inv;
+  const double two_pi = 6.283185307179586476925286766559;
+  const double red = phi - two_pi * rint(phi / two_pi);
+  float sn, cs;
+  sincosf(static_cast<float>(red), &sn, &cs);
+
+  const int nrows = p.nh + p.nkv;
+  for (int h = sub; h < nrows; h += ROWS_PER_PASS) {
+    const bool is_q = h < p.nh;
+    T* row = is_q ? static_cast<T*>(p.q) + static_cast<int64_t>(s) * p.q_stride + static_cast<int64_t>(h) * HD
+                  : static_cast<T*>(p.k) + static_cast<int64_t>(s) * p.k_stride + static_cast<int64_t>(h - p.nh) * HD;
+    const void* nw = is_q ? p.q_norm : p.k_norm;
+    float a = load_elem(row, i, DT);
+    float b = load_elem(row, i + HALF, DT);
+    const float ss = group_sum(a * a + b * b, HALF);
+    const float r = 1.0f / sqrtf(ss / static_cast<float>(HD) + p.eps);
+    a = a * r * load_elem(nw, i, p.norm_dt);
+    b = b * r * load_elem(nw, i + HALF, p.norm_dt);
+    const float ra = a * cs - b * sn;
+    const float rb = a * sn + b * cs;
+    if (DT == DT_F32) {
+      row[i] = ra;
+      row[i + HALF] = rb;
+    } else if (DT == DT_BF16) {
+      row[i] = f2bf(ra);
+      row[i + HALF] = f2bf(rb);
+    } else {
+      row[i] = f2h(ra);
+      row[i + HALF] = f2h(rb);
+    }
+  }
+}
+
+template <int HD>
+static hipError_t rope_launch(const RopeParams& p, int dt, hipStream_t s) {
+  dim3 grid(p.S), block(256);
+  switch (dt) {
+    case DT_F32: qk_norm_mrope_kernel<DT_F32, HD><<<grid, block, 0, s>>>(p); break;
+    case DT_BF16: qk_norm_mrope_kernel<DT_BF16, HD><<<grid, block, 0, s>>>(p); break;
+    case DT_F16: qk_norm_mrope_kernel<DT_F16, HD><<<grid, block, 0, s>>>(p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_qk_norm_mrope(const RopeParams& p, int head_dim, int data_dt, hipStream_t s) {
+  if (p.S <= 0) return hipSuccess;
+  if (head_dim == 128) return rope_launch<128>(p, data_dt, s);
+  if (head_dim == 64) return rope_launch<64>(p, data_dt, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace q3

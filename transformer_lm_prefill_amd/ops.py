@@ -1,0 +1,180 @@
+"""Python entry points with the C ABI's names: argument marshalling only.
+
+Tensors are torch tensors on the GPU (bf16 or float32, contiguous); work is enqueued on
+torch's current stream. Every check of shapes and sizes happens in the library, which
+raises Qwen3Error (status and message) on any violation.
+"""
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+from ._lib import Qwen3Error  # noqa: F401
+
+WEIGHT_NAMES = ("attn_norm", "wq", "wk", "wv", "q_norm", "k_norm", "wo", "ffn_norm",
+                "w_gate", "w_up", "w_down")
+
+
+@dataclass(frozen=True)
+class LayerSpec:
+    """Shape and numerics of one decoder layer (fields of qwen3_layer_cfg)."""
+    hidden: int
+    n_heads: int
+    n_kv_heads: int
+    head_dim: int
+    ffn: int
+    eps: float = 1e-6
+    theta: float = 5e6
+    sections: tuple = (24, 20, 20)
+    dtype: str = "bf16"      # weights: "bf16", "f16" or "f32"
+    act: str = ""            # matrix-product operands: "f16", "bf16" or "f32"; "" = f16 for
+                             # 16-bit weights, f32 for f32 weights
+
+    @classmethod
+    def of(cls, c, act=""):
+        """From any object with these attribute names."""
+        return cls(c.hidden, c.n_heads, c.n_kv_heads, c.head_dim, c.ffn, c.eps, c.theta,
+                   tuple(c.sections), c.dtype, act)
+
+    @property
+    def act_dtype(self):
+        if self.act:
+            return self.act
+        return "f32" if self.dtype == "f32" else "f16"
+
+
+_CODES = {"f32": _lib.QWEN3_F32, "bf16": _lib.QWEN3_BF16, "f16": _lib.QWEN3_F16}
+TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+
+def _dt(t):
+    if t.dtype == torch.bfloat16:
+        return _lib.QWEN3_BF16
+    if t.dtype == torch.float16:
+        return _lib.QWEN3_F16
+    if t.dtype == torch.float32:
+        return _lib.QWEN3_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _cfg(spec):
+    c = _lib.LayerCfg()
+    c.hidden, c.n_heads, c.n_kv_heads = spec.hidden, spec.n_heads, spec.n_kv_heads
+    c.head_dim, c.ffn = spec.head_dim, spec.ffn
+    c.rms_eps, c.rope_theta = spec.eps, spec.theta
+    c.mrope_section = (ctypes.c_int32 * 3)(*spec.sections)
+    c.wdtype = _CODES[spec.dtype]
+    c.act_dtype = _CODES[spec.act_dtype]
+    c.resid_dtype = _lib.QWEN3_F32
+    return c
+
+
+def layer_workspace_bytes(spec, seq_len):
+    return int(_lib.load().qwen3_layer_workspace_bytes(ctypes.byref(_cfg(spec)), int(seq_len)))
+
+
+def layer_prefill(spec, weights, x, positions, ds_rows=None, ds=None, out=None, workspace=None):
+    """qwen3_layer_prefill: one decoder layer over x [S, H] float32; returns out [S, H] float32.
+
+    weights: mapping of the eleven weight names to tensors of spec's dtype; positions [3, S]
+    int32; ds_rows [n] int32 and ds [n, H] (spec's dtype) for DeepStack, or None.
+    out may be x (in place). workspace: a uint8 tensor of layer_workspace_bytes() or None.
+    """
+    lib = _lib.load()
+    cfg = _cfg(spec)
+    s = x.shape[0]
+    if out is None:
+        out = torch.empty_like(x)
+    need = int(lib.qwen3_layer_workspace_bytes(ctypes.byref(cfg), int(s)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    w = _lib.LayerWeights(*[_ptr(weights[n]) for n in WEIGHT_NAMES])
+    n_ds = 0 if ds_rows is None else int(ds_rows.numel())
+    _lib.check(lib.qwen3_layer_prefill(
+        ctypes.byref(cfg), ctypes.byref(w), _ptr(x), _ptr(out), int(s), _ptr(positions),
+        _ptr(ds_rows), n_ds, _ptr(ds), _ptr(workspace), int(workspace.numel()), _stream()))
+    return out
+
+
+def qk_norm_mrope(q, k, q_norm, k_norm, positions, eps, theta, sections):
+    """In place on q [S, nh, hd] and k [S, nkv, hd]; returns (q, k)."""
+    lib = _lib.load()
+    s, nh, hd = q.shape
+    nkv = k.shape[1]
+    sec = (ctypes.c_int32 * 3)(*sections)
+    _lib.check(lib.qk_norm_mrope(_ptr(q), _ptr(k), int(s), int(nh), int(nkv), int(hd),
+                                 _ptr(q_norm), _ptr(k_norm), float(eps), _ptr(positions),
+                                 float(theta), sec, _dt(q), _dt(q_norm), _stream()))
+    return q, k
+
+
+def gqa_causal_attention(q, k, v, scale=None, out=None):
+    """out [S, nh, hd] = causal GQA softmax(scale q k^T) v."""
+    lib = _lib.load()
+    s, nh, hd = q.shape
+    nkv = k.shape[1]
+    if scale is None:
+        scale = hd ** -0.5
+    if out is None:
+        out = torch.empty_like(q)
+    _lib.check(lib.gqa_causal_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(out), int(s), int(nh),
+                                        int(nkv), int(hd), float(scale), _dt(q), _stream()))
+    return out
+
+
+def swiglu_ffn(x_normed, w_gate, w_up, w_down, residual=None, out_dtype=torch.float32, out=None,
+               workspace=None):
+    """out [S, H] = [residual +] (silu(x Wg^T) * (x Wu^T)) Wd^T."""
+    lib = _lib.load()
+    s, h = x_normed.shape
+    f = w_gate.shape[0]
+    if out is None:
+        out = torch.empty((s, h), dtype=out_dtype, device=x_normed.device)
+    need = int(lib.swiglu_ffn_workspace_bytes(int(s), int(f), _dt(x_normed)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x_normed.device)
+    _lib.check(lib.swiglu_ffn(_ptr(x_normed), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+                              _ptr(residual), _ptr(out), int(s), int(h), int(f), _dt(w_gate),
+                              _dt(x_normed), _dt(out), _ptr(workspace), int(workspace.numel()),
+                              _stream()))
+    return out
+
+
+def rms_norm_rows(x, w, eps, out_dtype=torch.bfloat16, out=None):
+    """y [rows, H] = x / sqrt(mean(x^2) + eps) * w, x float32."""
+    lib = _lib.load()
+    rows, h = x.shape
+    if out is None:
+        out = torch.empty((rows, h), dtype=out_dtype, device=x.device)
+    _lib.check(lib.rms_norm_rows(_ptr(x), _ptr(w), _ptr(out), int(rows), int(h), float(eps),
+                                 _dt(w), _dt(out), _stream()))
+    return out
+
+
+def timing_enable(on=True):
+    _lib.check(_lib.load().qwen3_timing_enable(1 if on else 0))
+
+
+def timing_collect(max_entries=64):
+    """{kernel name: (launches, total ms)} for launches since the last collect."""
+    lib = _lib.load()
+    arr = (_lib.KernelTime * max_entries)()
+    n = ctypes.c_int32(0)
+    _lib.check(lib.qwen3_timing_collect(arr, max_entries, ctypes.byref(n)))
+    return {arr[i].name.decode(): (arr[i].launches, arr[i].total_ms) for i in range(n.value)}
