@@ -31,12 +31,26 @@ def parse():
     ap.add_argument("--config", default="qwen3vl_8b_stack4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (the reference "
+                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    a = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 5}))
 
 
 def kernel_sources_digest():
     """Digest of the GEMM kernel source, to tell whether stored counter data is still current."""
-    p = os.path.join(ROOT, "transformer_lm_prefill_amd", "csrc", "gemm_bf16.hip")
+    p = os.path.join(ROOT, "transformer_lm_prefill_amd", "csrc", "gemm_mfma.hip")
     with open(p, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
@@ -72,6 +86,9 @@ def cpu_baseline(cfg, w0, x, pos, n_tok):
 
 def main():
     args = parse()
+    if args.copy_calib:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               "(the multi-GPU sequence-sharded path is a design, not an implementation)",
@@ -115,8 +132,7 @@ def main():
     def step():
         q3.layer_prefill(spec, layers[0], x0, pos, rows, ds, out=h, workspace=ws)
         for li in range(1, L):
-            q3.layer_prefill(spec, layers[li], h, pos, rows if li < 1 else None, None,
-                             out=h, workspace=ws)
+            q3.layer_prefill(spec, layers[li], h, pos, out=h, workspace=ws)
 
     for _ in range(args.warmup):
         step()

@@ -13,29 +13,29 @@
 //   down     EPI_STORE_F32 with the residual: y2 = y1 + a Wd^T
 //
 // Tiling for gfx950 (256 CUs in 8 XCDs, 160 KiB LDS per CU):
-//   workgroup tile 256 x (64*NB), K step 64, 4 waves in a 2 x 2 grid, each wave 128 x (32*NB)
-//   as 4 x NB MFMA 32x32 blocks (NB = 4: 256 fp32 accumulators per lane, in AGPRs);
+//   workgroup tile 256 x BN (BN = 256, 192 or 128), K step 64, 8 waves (two per SIMD, so one
+//   wave's LDS and memory waits overlap the other's MFMAs), each wave a (256/WM) x (BN/WN)
+//   block of 32x32 MFMA tiles with fp32 accumulators;
 //   A and B tiles staged through a double-buffered LDS ring (global -> registers -> LDS): the
 //   next K step's global loads are issued before this step's MFMAs and stored to the other
 //   LDS buffer after them, one barrier per K step;
 //   MFMA operand fragments are read from LDS one 16-wide K sub-step ahead of the MFMAs that
-//   use them, so LDS latency overlaps matrix work;
+//   use them;
 //   16-byte LDS chunks XOR-swizzled by row, so the fragment reads (32 rows, one chunk each)
-//   and the tile stores are free of bank conflicts;
+//   and the tile stores are free of bank conflicts (rocprofv3 SQ_LDS_BANK_CONFLICT reads 0);
 //   workgroup ids remapped so each XCD (ids congruent mod 8) owns a compact band of tiles
 //   sharing A rows and B columns in its own L2.
 #include "common.h"
 #include "kernels.h"
 
 #ifndef Q3_GEMM_SCHED
-#define Q3_GEMM_SCHED 1
+#define Q3_GEMM_SCHED 0
 #endif
 
 namespace q3 {
 
 constexpr int kBM = 256;
 constexpr int kBK = 64;
-constexpr int kGemmThreads = 256;
 
 __device__ __forceinline__ int swz8(int row) { return (row ^ (row >> 3)) & 7; }
 
@@ -56,15 +56,17 @@ __device__ __forceinline__ void tile_coords(int bid, int nwg, int tiles_m, int t
   tn = in_group / gsz;
 }
 
-template <int NB, int EPI>
+// Source row of B for LDS tile row r of tile column tn.
+template <int BN, int WN, int EPI>
 __device__ __forceinline__ const uint16_t* b_row(const GemmParams& p, int tn, int r) {
-  constexpr int BN = 64 * NB;
   if (EPI == EPI_SWIGLU_16) {
-    // Tile tn covers F columns [tn*BN/2, tn*BN/2 + BN/2). LDS rows come in 64-row segments
-    // gate, up, gate, up, ... so that each wave's 128 columns hold 64 gate columns followed by
-    // the 64 up columns of the same F range: the SwiGLU pairing is then lane-local.
-    const int seg = r >> 6;
-    const int f = tn * (BN / 2) + (seg >> 1) * 64 + (r & 63);
+    // Tile tn covers F columns [tn*BN/2, tn*BN/2 + BN/2). LDS rows come in segments of half a
+    // wave's column width, alternating gate and up, so that each wave's columns hold gate
+    // columns followed by the up columns of the same F range: the SwiGLU pairing is then
+    // lane-local in the accumulators.
+    constexpr int SEG = BN / WN / 2;
+    const int seg = r / SEG;
+    const int f = tn * (BN / 2) + (seg >> 1) * SEG + (r % SEG);
     return ((seg & 1) ? p.B1 : p.B0) + static_cast<int64_t>(f) * p.ldb;
   } else {
     const int n = tn * BN + r;
@@ -76,62 +78,56 @@ __device__ __forceinline__ const uint16_t* b_row(const GemmParams& p, int tn, in
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
-template <int NB, int EPI, int OP, bool CVT>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+// BN: tile width; WM x WN waves (two or four along each side), each owning a wave tile of
+// (256/WM) x (BN/WN) = MI x NI MFMA blocks of 32 x 32.
+template <int BN, int WM, int WN, int EPI, int OP, bool CVT>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * WM * WN, 64 * WM * WN),
+                          amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4)))
 void gemm_mfma_kernel(const GemmParams p) {
   using F = Fmt<OP>;
-  constexpr int BN = 64 * NB;
-  constexpr int ACH = kBM * 8 / kGemmThreads;  // 16-byte chunks per thread, A tile (8)
-  constexpr int BCH = BN * 8 / kGemmThreads;   // 16-byte chunks per thread, B tile (2*NB)
+  constexpr int THREADS = 64 * WM * WN;
+  constexpr int MI = kBM / WM / 32;            // MFMA blocks per wave along M
+  constexpr int NI = BN / WN / 32;             // MFMA blocks per wave along N
+  constexpr int RSTEP = THREADS / 8;           // tile rows covered by one pass of the loaders
+  constexpr int ACH = kBM / RSTEP;             // 16-byte chunks per thread, A tile
+  constexpr int BCH = BN / RSTEP;              // 16-byte chunks per thread, B tile
+  static_assert(MI >= 1 && NI >= 1 && BN % RSTEP == 0, "tile shape");
   __shared__ u32x4 As[2][kBM * 8];
   __shared__ u32x4 Bs[2][BN * 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
+  const int wm = wave / WN;
+  const int wn = wave % WN;
   const int tiles_m = (p.M + kBM - 1) / kBM;
   const int tiles_n = p.N / BN;
   int tm, tn;
   tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
 
-  const int lrow = tid >> 3;  // 0..31
+  const int lrow = tid >> 3;
   const int lch = tid & 7;    // 16-byte chunk within a 64-wide K step
 
   // A rows: element offsets from A (rows past M are clamped: read, never stored)
   uint32_t a_off[ACH];
 #pragma unroll
   for (int j = 0; j < ACH; ++j) {
-    const int r = min(tm * kBM + lrow + 32 * j, p.M - 1);
+    const int r = min(tm * kBM + lrow + RSTEP * j, p.M - 1);
     a_off[j] = static_cast<uint32_t>(r) * static_cast<uint32_t>(p.lda) + lch * 8;
   }
   const uint16_t* b_src[BCH];
 #pragma unroll
-  for (int j = 0; j < BCH; ++j) b_src[j] = b_row<NB, EPI>(p, tn, lrow + 32 * j) + lch * 8;
+  for (int j = 0; j < BCH; ++j) b_src[j] = b_row<BN, WN, EPI>(p, tn, lrow + RSTEP * j) + lch * 8;
 
-  // LDS slots this thread stores (same every K step)
-  int st_a[ACH], st_b[BCH];
-#pragma unroll
-  for (int j = 0; j < ACH; ++j) {
-    const int row = lrow + 32 * j;
-    st_a[j] = row * 8 + (lch ^ swz8(row));
-  }
-#pragma unroll
-  for (int j = 0; j < BCH; ++j) {
-    const int row = lrow + 32 * j;
-    st_b[j] = row * 8 + (lch ^ swz8(row));
-  }
-  // LDS rows this lane reads fragments from
   const int fr = lane & 31;
   const int fh = lane >> 5;
 
   u32x4 ra[ACH], rb[BCH];
-  f32x16 acc[4][NB];
+  f32x16 acc[MI][NI];
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < NB; ++ni)
+    for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.f;
 
@@ -143,7 +139,10 @@ void gemm_mfma_kernel(const GemmParams p) {
   };
   auto lstore = [&](int buf) {
 #pragma unroll
-    for (int j = 0; j < ACH; ++j) As[buf][st_a[j]] = ra[j];
+    for (int j = 0; j < ACH; ++j) {
+      const int row = lrow + RSTEP * j;
+      As[buf][row * 8 + (lch ^ swz8(row))] = ra[j];
+    }
 #pragma unroll
     for (int j = 0; j < BCH; ++j) {
       u32x4 v = rb[j];
@@ -151,19 +150,20 @@ void gemm_mfma_kernel(const GemmParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = bf16x2_to_f16x2(v[e]);
       }
-      Bs[buf][st_b[j]] = v;
+      const int row = lrow + RSTEP * j;
+      Bs[buf][row * 8 + (lch ^ swz8(row))] = v;
     }
   };
-  auto fread = [&](int buf, int ks, u32x4 (&fa)[4], u32x4 (&fb)[NB]) {
+  auto fread = [&](int buf, int ks, u32x4 (&fa)[MI], u32x4 (&fb)[NI]) {
     const int ch = ks * 2 + fh;
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-      const int row = wm * 128 + mi * 32 + fr;
+    for (int mi = 0; mi < MI; ++mi) {
+      const int row = wm * (32 * MI) + mi * 32 + fr;
       fa[mi] = As[buf][row * 8 + (ch ^ swz8(row))];
     }
 #pragma unroll
-    for (int ni = 0; ni < NB; ++ni) {
-      const int row = wn * 32 * NB + ni * 32 + fr;
+    for (int ni = 0; ni < NI; ++ni) {
+      const int row = wn * (32 * NI) + ni * 32 + fr;
       fb[ni] = Bs[buf][row * 8 + (ch ^ swz8(row))];
     }
   };
@@ -177,27 +177,16 @@ void gemm_mfma_kernel(const GemmParams p) {
     const int buf = kt & 1;
     // next K step's tile (the last step re-reads its own tile: same addresses, no branch)
     gload(kt + 1 < nk ? (kt + 1) * kBK : kt * kBK);
-    u32x4 fa[2][4], fb[2][NB];
+    u32x4 fa[2][MI], fb[2][NI];
     fread(buf, 0, fa[0], fb[0]);
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
       if (ks + 1 < kBK / 16) fread(buf, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
+      for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < NB; ++ni)
+        for (int ni = 0; ni < NI; ++ni)
           acc[mi][ni] = F::mfma(fa[ks & 1][mi], fb[ks & 1][ni], acc[mi][ni]);
-#if Q3_GEMM_SCHED
-      if (ks + 1 < kBK / 16) {
-        // interleave the next sub-step's fragment reads with this sub-step's MFMAs
-#pragma unroll
-        for (int i = 0; i < 4 + NB; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 DS read
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4 * NB - (4 + NB), 0);
-      }
-#endif
     }
     lstore(buf ^ 1);
     __syncthreads();
@@ -206,30 +195,30 @@ void gemm_mfma_kernel(const GemmParams p) {
   // Epilogue. Accumulator element e of block (mi, ni) in lane l holds
   // row 8*(e/4) + 4*(l/32) + e%4 and column l%32 of that 32x32 block.
   const int col_in_blk = lane & 31;
-  const int row_base = tm * kBM + wm * 128 + 4 * (lane >> 5);
+  const int row_base = tm * kBM + wm * (32 * MI) + 4 * (lane >> 5);
   if (EPI == EPI_SWIGLU_16) {
     uint16_t* C = static_cast<uint16_t*>(p.C);
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < NB / 2; ++ni) {
-        const int f = tn * (BN / 2) + wn * 64 + ni * 32 + col_in_blk;
+      for (int ni = 0; ni < NI / 2; ++ni) {
+        const int f = tn * (BN / 2) + wn * (16 * NI) + ni * 32 + col_in_blk;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int m = row_base + mi * 32 + 8 * (e >> 2) + (e & 3);
           if (m < p.M) {
             const float g = acc[mi][ni][e];
-            const float u = acc[mi][ni + NB / 2][e];
+            const float u = acc[mi][ni + NI / 2][e];
             C[static_cast<int64_t>(m) * p.ldc + f] = F::from_f32(silu_f(g) * u);
           }
         }
       }
   } else {
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < NB; ++ni) {
-        const int n = tn * BN + wn * 32 * NB + ni * 32 + col_in_blk;
+      for (int ni = 0; ni < NI; ++ni) {
+        const int n = tn * BN + wn * 32 * NI + ni * 32 + col_in_blk;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int m = row_base + mi * 32 + 8 * (e >> 2) + (e & 3);
@@ -269,19 +258,20 @@ int gemm_pick_nb(int M, int N, int epi) {
   return best;
 }
 
-template <int NB, int EPI, int OP, bool CVT>
+template <int BN, int WM, int WN, int EPI, int OP, bool CVT>
 static hipError_t launch_t(const GemmParams& p, hipStream_t s) {
-  const int tiles = ((p.M + kBM - 1) / kBM) * (p.N / (64 * NB));
-  gemm_mfma_kernel<NB, EPI, OP, CVT><<<tiles, kGemmThreads, 0, s>>>(p);
+  const int tiles = ((p.M + kBM - 1) / kBM) * (p.N / BN);
+  gemm_mfma_kernel<BN, WM, WN, EPI, OP, CVT><<<tiles, 64 * WM * WN, 0, s>>>(p);
   return hipGetLastError();
 }
 
+// nb selects the tile width 64*nb: 256 (8 waves, 2 x 4), 192 (8 waves, 4 x 2), 128 (8 waves, 4 x 2)
 template <int EPI, int OP, bool CVT>
 static hipError_t launch_nb(const GemmParams& p, int nb, hipStream_t s) {
-  if (EPI == EPI_SWIGLU_16) return nb == 4 ? launch_t<4, EPI, OP, CVT>(p, s) : hipErrorInvalidValue;
-  if (nb == 4) return launch_t<4, EPI, OP, CVT>(p, s);
-  if (nb == 3) return launch_t<3, EPI, OP, CVT>(p, s);
-  if (nb == 2) return launch_t<2, EPI, OP, CVT>(p, s);
+  if (nb == 4) return launch_t<256, 2, 4, EPI, OP, CVT>(p, s);
+  if (EPI == EPI_SWIGLU_16) return hipErrorInvalidValue;
+  if (nb == 3) return launch_t<192, 4, 2, EPI, OP, CVT>(p, s);
+  if (nb == 2) return launch_t<128, 4, 2, EPI, OP, CVT>(p, s);
   return hipErrorInvalidValue;
 }
 
