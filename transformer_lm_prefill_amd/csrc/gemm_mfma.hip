@@ -28,6 +28,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <type_traits>
+
 #ifndef Q3_GEMM_SCHED
 #define Q3_GEMM_SCHED 0
 #endif
@@ -77,6 +79,58 @@ __device__ __forceinline__ const uint16_t* b_row(const GemmParams& p, int tn, in
 }
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
+
+// Epilogue shared by the kernels: stores a wave's accumulators. Accumulator element e of
+// block (mi, ni) in lane l holds row 8*(e/4) + 4*(l/32) + e%4 and column l%32 of that block.
+template <int BN, int WM, int WN, int EPI, int OP>
+__device__ __forceinline__ void gemm_epilogue(const GemmParams& p,
+                                              f32x16 (&acc)[kBM / WM / 32][BN / WN / 32], int tm,
+                                              int tn, int wm, int wn, int lane) {
+  using F = Fmt<OP>;
+  constexpr int MI = kBM / WM / 32;
+  constexpr int NI = BN / WN / 32;
+  const int col_in_blk = lane & 31;
+  const int row_base = tm * kBM + wm * (32 * MI) + 4 * (lane >> 5);
+  if (EPI == EPI_SWIGLU_16) {
+    uint16_t* C = static_cast<uint16_t*>(p.C);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI / 2; ++ni) {
+        const int f = tn * (BN / 2) + wn * (16 * NI) + ni * 32 + col_in_blk;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int m = row_base + mi * 32 + 8 * (e >> 2) + (e & 3);
+          if (m < p.M) {
+            const float g = acc[mi][ni][e];
+            const float u = acc[mi][ni + NI / 2][e];
+            C[static_cast<int64_t>(m) * p.ldc + f] = F::from_f32(silu_f(g) * u);
+          }
+        }
+      }
+  } else {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        const int n = tn * BN + wn * 32 * NI + ni * 32 + col_in_blk;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int m = row_base + mi * 32 + 8 * (e >> 2) + (e & 3);
+          if (m < p.M) {
+            const float v = acc[mi][ni][e];
+            if (EPI == EPI_STORE_16) {
+              static_cast<uint16_t*>(p.C)[static_cast<int64_t>(m) * p.ldc + n] = F::from_f32(v);
+            } else {
+              float r = 0.f;
+              if (p.R) r = p.R[static_cast<int64_t>(m) * p.ldr + n];
+              static_cast<float*>(p.C)[static_cast<int64_t>(m) * p.ldc + n] = r + v;
+            }
+          }
+        }
+      }
+  }
+}
 
 // BN: tile width; WM x WN waves (two or four along each side), each owning a wave tile of
 // (256/WM) x (BN/WN) = MI x NI MFMA blocks of 32 x 32.
@@ -192,49 +246,312 @@ void gemm_mfma_kernel(const GemmParams p) {
     __syncthreads();
   }
 
-  // Epilogue. Accumulator element e of block (mi, ni) in lane l holds
-  // row 8*(e/4) + 4*(l/32) + e%4 and column l%32 of that 32x32 block.
-  const int col_in_blk = lane & 31;
-  const int row_base = tm * kBM + wm * (32 * MI) + 4 * (lane >> 5);
-  if (EPI == EPI_SWIGLU_16) {
-    uint16_t* C = static_cast<uint16_t*>(p.C);
+  gemm_epilogue<BN, WM, WN, EPI, OP>(p, acc, tm, tn, wm, wn, lane);
+}
+
+// ---------------------------------------------------------------------------------------
+// Direct-to-LDS variant: tiles go from global memory straight into LDS with
+// global_load_lds_dwordx4 (lane i of a wave instruction fills the i-th 16-byte slot of a
+// contiguous 1 KiB block), through a 4-stage ring of 32-wide K steps, so each tile is requested
+// three K steps before its MFMAs and no registers hold staged data. A row of a stage is 64 bytes
+// (4 chunks); the chunk a slot holds is XOR-permuted by row so that the 32-row fragment reads hit
+// distinct banks. bf16 weights feeding fp16 products are converted after the fragment read.
+constexpr int kBK2 = 32;
+constexpr int kStages = 4;
+
+__device__ __forceinline__ int swz4(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void gbl_void_t;
+
+__device__ __forceinline__ void g2lds(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)l, 16, 0, 0);
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+#define Q3_WAIT_VMCNT(N) \
+  __builtin_amdgcn_s_waitcnt(((N) & 0xF) | (0x7 << 4) | (0xF << 8) | (((N) >> 4) << 14))
+
+template <int BN, int WM, int WN, int EPI, int OP, bool CVT>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * WM * WN, 64 * WM * WN),
+                          amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4)))
+void gemm_d2l_kernel(const GemmParams p) {
+  using F = Fmt<OP>;
+  constexpr int THREADS = 64 * WM * WN;
+  constexpr int MI = kBM / WM / 32;
+  constexpr int NI = BN / WN / 32;
+  constexpr int ASLOT = kBM * 4;              // 16-byte slots per stage, A
+  constexpr int BSLOT = BN * 4;               // 16-byte slots per stage, B
+  constexpr int WAVES = THREADS / 64;
+  constexpr int AJ = ASLOT / THREADS;         // loads per thread per stage, A
+  constexpr int BJ = (BSLOT + THREADS - 1) / THREADS;  // loads per thread per stage, B
+  constexpr int LPS = AJ + BJ;                // loads per thread per stage (equal in every wave)
+  static_assert(ASLOT % THREADS == 0 && BSLOT % 64 == 0, "tile shape");
+  __shared__ u32x4 sA0[ASLOT], sA1[ASLOT], sA2[ASLOT], sA3[ASLOT];
+  __shared__ u32x4 sB0[BSLOT], sB1[BSLOT], sB2[BSLOT], sB3[BSLOT];
+  // When BSLOT is not a multiple of THREADS, the waves past the last B block repeat a valid
+  // load into this never-read block, so every wave issues LPS loads per stage and one
+  // s_waitcnt immediate fits all of them.
+  __shared__ u32x4 sSink[(BSLOT % THREADS) ? 64 : 1];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WN;
+  const int wn = wave % WN;
+  const int tiles_m = (p.M + kBM - 1) / kBM;
+  const int tiles_n = p.N / BN;
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+
+  // Load slot of this lane in pass j: the wave's 64 consecutive slots starting at
+  // (wave + j*waves)*64; slot -> tile row slot/4, stored chunk slot%4, global chunk
+  // (slot%4) ^ swz4(row).
+  const uint16_t* a_src[AJ];
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+  for (int j = 0; j < AJ; ++j) {
+    const int slot = (wave + j * WAVES) * 64 + lane;
+    const int row = slot >> 2;
+    const int r = min(tm * kBM + row, p.M - 1);  // rows past M are read, never stored
+    a_src[j] = p.A + static_cast<int64_t>(r) * p.lda + ((slot & 3) ^ swz4(row)) * 8;
+  }
+  const uint16_t* b_src[BJ];
 #pragma unroll
-      for (int ni = 0; ni < NI / 2; ++ni) {
-        const int f = tn * (BN / 2) + wn * (16 * NI) + ni * 32 + col_in_blk;
+  for (int j = 0; j < BJ; ++j) {
+    int slot = (wave + j * WAVES) * 64 + lane;
+    if (slot >= BSLOT) slot = lane;  // sink load: a valid row
+    const int row = slot >> 2;
+    b_src[j] = b_row<BN, WN, EPI>(p, tn, row) + ((slot & 3) ^ swz4(row)) * 8;
+  }
+
+  f32x16 acc[MI][NI];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int m = row_base + mi * 32 + 8 * (e >> 2) + (e & 3);
-          if (m < p.M) {
-            const float g = acc[mi][ni][e];
-            const float u = acc[mi][ni + NI / 2][e];
-            C[static_cast<int64_t>(m) * p.ldc + f] = F::from_f32(silu_f(g) * u);
-          }
-        }
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.f;
+
+  const int nk = p.K / kBK2;
+  auto stage_a = [&](int st) -> u32x4* { return st == 0 ? sA0 : st == 1 ? sA1 : st == 2 ? sA2 : sA3; };
+  auto stage_b = [&](int st) -> u32x4* { return st == 0 ? sB0 : st == 1 ? sB1 : st == 2 ? sB2 : sB3; };
+  auto issue = [&](int st, int kt) {
+    const int k0 = min(kt, nk - 1) * kBK2;  // past the end: reload the last tile (never read)
+    u32x4* a = stage_a(st);
+    u32x4* b = stage_b(st);
+#pragma unroll
+    for (int j = 0; j < AJ; ++j) g2lds(a_src[j] + k0, a + (wave + j * WAVES) * 64);
+#pragma unroll
+    for (int j = 0; j < BJ; ++j) {
+      const int blk = wave + j * WAVES;
+      g2lds(b_src[j] + k0, blk * 64 < BSLOT ? b + blk * 64 : sSink);
+    }
+  };
+  const int fr = lane & 31;
+  const int fh = lane >> 5;
+  // Fragment sets: set 0 holds sub-step 0 of a K step, set 1 sub-step 1.
+  u32x4 fa[2][MI], fb[2][NI];
+  auto fread = [&](int st, int ks, int set) {
+    const u32x4* a = stage_a(st);
+    const u32x4* b = stage_b(st);
+    const int ch = ks * 2 + fh;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      const int row = wm * (32 * MI) + mi * 32 + fr;
+      fa[set][mi] = a[row * 4 + (ch ^ swz4(row))];
+    }
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      const int row = wn * (32 * NI) + ni * 32 + fr;
+      fb[set][ni] = b[row * 4 + (ch ^ swz4(row))];
+    }
+  };
+  auto mfmas = [&](int set) {
+    u32x4 bv[NI];
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      bv[ni] = fb[set][ni];
+      if (CVT) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bv[ni][e] = bf16x2_to_f16x2(bv[ni][e]);
       }
-  } else {
+    }
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = F::mfma(fa[set][mi], bv[ni], acc[mi][ni]);
+  };
+  // s_waitcnt vmcnt(N) lgkmcnt(0), then the workgroup barrier; the empty asm statements keep
+  // the compiler from moving memory accesses across it.
+  auto sync = [&](auto n_vm) {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((decltype(n_vm)::value & 0xF) | (0x7 << 4) | ((decltype(n_vm)::value >> 4) << 14));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  issue(0, 0);
+  issue(1, 1);
+  issue(2, 2);
+  sync(std::integral_constant<int, 2 * LPS>{});  // stage 0 landed everywhere
+  fread(0, 0, 0);
+  // Step kt (stage kt % 4): wait until stage kt+1 has landed everywhere (only kt+2 may still be
+  // in flight), barrier (every wave is also past its reads of stage kt-1), refill stage kt-1's
+  // buffer with step kt+3, then the two 16-wide sub-steps; the second one reads sub-step 0 of
+  // step kt+1, so the MFMAs after the next barrier start on operands already in registers.
+  // nk is a multiple of kStages (the launcher routes other K to the register-staged kernel).
+  for (int kt = 0; kt < nk; kt += kStages) {
+#pragma unroll
+    for (int u = 0; u < kStages; ++u) {
+      sync(std::integral_constant<int, LPS>{});
+      issue((u + 3) & 3, kt + u + 3);
+      fread(u, 1, 1);
+      mfmas(0);
+      fread((u + 1) & 3, 0, 0);
+      mfmas(1);
+    }
+  }
+
+  // the trailing reloads of the last tile must land before this workgroup's LDS is released
+  Q3_WAIT_VMCNT(0);
+  gemm_epilogue<BN, WM, WN, EPI, OP>(p, acc, tm, tn, wm, wn, lane);
+}
+
+// ---------------------------------------------------------------------------------------
+// Ping-pong variant of the direct-to-LDS kernel (256 x 256 tiles, 2 x 4 waves). Waves 0-3 and
+// 4-7 (one of each per SIMD) run one barrier apart: every K step of a wave is a memory phase
+// (wait for its own loads of the next stage, read all fragments of this step from LDS,
+// convert bf16 weights, issue the loads three stages ahead) followed, after a barrier, by an
+// MFMA phase. Group 1 starts one barrier late, so while one group's wave on a SIMD runs its
+// MFMAs the other group's wave on that SIMD does its memory work.
+template <int EPI, int OP, bool CVT>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void gemm_pp_kernel(const GemmParams p) {
+  using F = Fmt<OP>;
+  constexpr int BN = 256, WM = 2, WN = 4;
+  constexpr int THREADS = 512, WAVES = 8;
+  constexpr int MI = kBM / WM / 32;            // 4
+  constexpr int NI = BN / WN / 32;             // 2
+  constexpr int ASLOT = kBM * 4, BSLOT = BN * 4;
+  constexpr int AJ = ASLOT / THREADS, BJ = BSLOT / THREADS;
+  constexpr int LPS = AJ + BJ;
+  __shared__ u32x4 sA0[ASLOT], sA1[ASLOT], sA2[ASLOT], sA3[ASLOT];
+  __shared__ u32x4 sB0[BSLOT], sB1[BSLOT], sB2[BSLOT], sB3[BSLOT];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WN;
+  const int wn = wave % WN;
+  const bool late = wm == 1;  // group 1 runs one barrier behind group 0
+  const int tiles_m = (p.M + kBM - 1) / kBM;
+  const int tiles_n = p.N / BN;
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+
+  const uint16_t* a_src[AJ];
+#pragma unroll
+  for (int j = 0; j < AJ; ++j) {
+    const int slot = (wave + j * WAVES) * 64 + lane;
+    const int row = slot >> 2;
+    const int r = min(tm * kBM + row, p.M - 1);
+    a_src[j] = p.A + static_cast<int64_t>(r) * p.lda + ((slot & 3) ^ swz4(row)) * 8;
+  }
+  const uint16_t* b_src[BJ];
+#pragma unroll
+  for (int j = 0; j < BJ; ++j) {
+    const int slot = (wave + j * WAVES) * 64 + lane;
+    const int row = slot >> 2;
+    b_src[j] = b_row<BN, WN, EPI>(p, tn, row) + ((slot & 3) ^ swz4(row)) * 8;
+  }
+
+  f32x16 acc[MI][NI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.f;
+
+  const int nk = p.K / kBK2;
+  auto stage_a = [&](int st) -> u32x4* { return st == 0 ? sA0 : st == 1 ? sA1 : st == 2 ? sA2 : sA3; };
+  auto stage_b = [&](int st) -> u32x4* { return st == 0 ? sB0 : st == 1 ? sB1 : st == 2 ? sB2 : sB3; };
+  auto issue = [&](int st, int kt) {
+    const int k0 = min(kt, nk - 1) * kBK2;
+    u32x4* a = stage_a(st);
+    u32x4* b = stage_b(st);
+#pragma unroll
+    for (int j = 0; j < AJ; ++j) g2lds(a_src[j] + k0, a + (wave + j * WAVES) * 64);
+#pragma unroll
+    for (int j = 0; j < BJ; ++j) g2lds(b_src[j] + k0, b + (wave + j * WAVES) * 64);
+  };
+  const int fr = lane & 31;
+  const int fh = lane >> 5;
+  u32x4 fa[2][MI], fb[2][NI];
+  auto fread = [&](int st) {
+    const u32x4* a = stage_a(st);
+    const u32x4* b = stage_b(st);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int ch = ks * 2 + fh;
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        const int row = wm * (32 * MI) + mi * 32 + fr;
+        fa[ks][mi] = a[row * 4 + (ch ^ swz4(row))];
+      }
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) {
-        const int n = tn * BN + wn * 32 * NI + ni * 32 + col_in_blk;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int m = row_base + mi * 32 + 8 * (e >> 2) + (e & 3);
-          if (m < p.M) {
-            const float v = acc[mi][ni][e];
-            if (EPI == EPI_STORE_16) {
-              static_cast<uint16_t*>(p.C)[static_cast<int64_t>(m) * p.ldc + n] = F::from_f32(v);
-            } else {
-              float r = 0.f;
-              if (p.R) r = p.R[static_cast<int64_t>(m) * p.ldr + n];
-              static_cast<float*>(p.C)[static_cast<int64_t>(m) * p.ldc + n] = r + v;
-            }
-          }
-        }
+        const int row = wn * (32 * NI) + ni * 32 + fr;
+        fb[ks][ni] = b[row * 4 + (ch ^ swz4(row))];
       }
+    }
+    if (CVT) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) fb[ks][ni][e] = bf16x2_to_f16x2(fb[ks][ni][e]);
+    }
+  };
+  auto barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0x3F & 0xF) | ((0x3F >> 4) << 14));  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  issue(0, 0);
+  issue(1, 1);
+  issue(2, 2);
+  Q3_WAIT_VMCNT(LPS);  // own loads of stages 0 and 1 landed
+  barrier();           // stages 0 and 1 complete for every wave
+  if (late) barrier();
+
+  for (int kt = 0; kt < nk; kt += kStages) {
+#pragma unroll
+    for (int u = 0; u < kStages; ++u) {
+      // memory phase of step kt+u
+      Q3_WAIT_VMCNT(LPS);  // own loads of stage kt+u+1 landed (kt+u+2 may be in flight)
+      fread(u);
+      issue((u + 3) & 3, kt + u + 3);
+      barrier();
+      // MFMA phase
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = F::mfma(fa[ks][mi], fb[ks][ni], acc[mi][ni]);
+      barrier();
+    }
   }
+  if (!late) barrier();
+
+  Q3_WAIT_VMCNT(0);
+  gemm_epilogue<BN, WM, WN, EPI, OP>(p, acc, tm, tn, wm, wn, lane);
 }
 
 int gemm_pick_nb(int M, int N, int epi) {
@@ -258,17 +575,34 @@ int gemm_pick_nb(int M, int N, int epi) {
   return best;
 }
 
+#ifndef Q3_GEMM_D2L
+#define Q3_GEMM_D2L 1
+#endif
+#ifndef Q3_GEMM_PP
+#define Q3_GEMM_PP 0
+#endif
+#ifndef Q3_GEMM_W4
+#define Q3_GEMM_W4 0
+#endif
+
 template <int BN, int WM, int WN, int EPI, int OP, bool CVT>
 static hipError_t launch_t(const GemmParams& p, hipStream_t s) {
   const int tiles = ((p.M + kBM - 1) / kBM) * (p.N / BN);
-  gemm_mfma_kernel<BN, WM, WN, EPI, OP, CVT><<<tiles, 64 * WM * WN, 0, s>>>(p);
+  if (Q3_GEMM_PP && BN == 256 && WM == 2 && WN == 4 && p.K % (kBK2 * kStages) == 0)
+    gemm_pp_kernel<EPI, OP, CVT><<<tiles, 512, 0, s>>>(p);
+  else if (Q3_GEMM_D2L && p.K % (kBK2 * kStages) == 0)
+    gemm_d2l_kernel<BN, WM, WN, EPI, OP, CVT><<<tiles, 64 * WM * WN, 0, s>>>(p);
+  else gemm_mfma_kernel<BN, WM, WN, EPI, OP, CVT><<<tiles, 64 * WM * WN, 0, s>>>(p);
   return hipGetLastError();
 }
 
 // nb selects the tile width 64*nb: 256 (8 waves, 2 x 4), 192 (8 waves, 4 x 2), 128 (8 waves, 4 x 2)
 template <int EPI, int OP, bool CVT>
 static hipError_t launch_nb(const GemmParams& p, int nb, hipStream_t s) {
-  if (nb == 4) return launch_t<256, 2, 4, EPI, OP, CVT>(p, s);
+  if (nb == 4) {
+    if (Q3_GEMM_W4) return launch_t<256, 2, 2, EPI, OP, CVT>(p, s);
+    return launch_t<256, 2, 4, EPI, OP, CVT>(p, s);
+  }
   if (EPI == EPI_SWIGLU_16) return hipErrorInvalidValue;
   if (nb == 3) return launch_t<192, 4, 2, EPI, OP, CVT>(p, s);
   if (nb == 2) return launch_t<128, 4, 2, EPI, OP, CVT>(p, s);
