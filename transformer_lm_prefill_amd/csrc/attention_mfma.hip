@@ -24,6 +24,10 @@
 #include "common.h"
 #include "kernels.h"
 
+#ifndef Q3_ATTN_LAZY
+#define Q3_ATTN_LAZY 0
+#endif
+
 namespace q3 {
 
 constexpr int kHD = 128;
@@ -46,7 +50,7 @@ void attn_fwd_kernel(const AttnParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform by construction
   const int nblk = (p.S + TOK - 1) / TOK;
   const int g = blockIdx.x % p.nkv;
   const int blk = nblk - 1 - blockIdx.x / p.nkv;
@@ -75,7 +79,7 @@ void attn_fwd_kernel(const AttnParams p) {
   for (int d = 0; d < 4; ++d)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[d][e] = 0.f;
-  float m_run = -1e30f;  // running max of scaled scores (base-2 units)
+  float m_run = -INFINITY;  // exponent offset: running max of scaled scores (base 2)
   float l_run = 0.f;
 
   const int wg_end = min(p.S, t0 + TOK);        // keys this workgroup needs
@@ -117,15 +121,15 @@ void attn_fwd_kernel(const AttnParams p) {
       }
     } else {
       const int kg = lt >> 4, hc = lt & 15;
-      // st[r] holds v[key 4kg+r][hd 8hc .. 8hc+7] as 4 words of two bf16 each.
+      // st[r] holds v[key 4kg+r][hd 8hc .. 8hc+7] as 4 words of two 16-bit values each; the
+      // granule for hd row 8hc+e gathers the e-th value of the four keys (byte permutes).
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int w = e >> 1;
-        const int sh = (e & 1) * 16;
-        const uint32_t v0 = (st[0][w] >> sh) & 0xFFFF, v1 = (st[1][w] >> sh) & 0xFFFF;
-        const uint32_t v2 = (st[2][w] >> sh) & 0xFFFF, v3 = (st[3][w] >> sh) & 0xFFFF;
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
         const int hd = hc * 8 + e;
-        Vts[buf][hd * 16 + (kg ^ swz_v(hd))] = u32x2{v0 | (v1 << 16), v2 | (v3 << 16)};
+        Vts[buf][hd * 16 + (kg ^ swz_v(hd))] =
+            u32x2{__builtin_amdgcn_perm(st[1][w], st[0][w], sel), __builtin_amdgcn_perm(st[3][w], st[2][w], sel)};
       }
     }
   };
@@ -141,53 +145,64 @@ void attn_fwd_kernel(const AttnParams p) {
     if (more) gload(kb + kKT);
 
     if (wave_live && kb < wave_end) {
-      // ---- S^T = K Q^T for two 32-key blocks
+      // ---- S^T = K Q^T for two 32-key blocks (the two accumulation chains interleaved)
       f32x16 s[2];
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) s[b][e] = 0.f;
-        const int key = b * 32 + qrow;
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          const int ch = 2 * ks + hi;
-          s[b] = F::mfma(Ks[buf][key * 16 + (ch ^ swz_k(key))], qf[ks], s[b]);
-        }
-      }
-      // ---- scale, causal mask, online softmax (base 2)
-      const bool need_mask = kb + kKT - 1 > wt0 || kb + kKT > p.S;
-      float mt = -1e30f;
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          float z = s[b][e] * p.scale_log2;
-          if (need_mask) {
-            const int key = kb + b * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
-            if (key > my_t || key >= p.S) z = -INFINITY;
-          }
-          s[b][e] = z;
-          mt = fmaxf(mt, z);
+        for (int e = 0; e < 16; ++e) s[b][e] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const int ch = 2 * ks + hi;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const int key = b * 32 + qrow;
+          s[b] = F::mfma(Ks[buf][key * 16 + (ch ^ swz_k(key))], qf[ks], s[b]);
         }
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = fast_exp2(m_run - m_new);
+      }
+      // ---- causal mask, online softmax (base 2). The exponent offset m_run moves only when a
+      // row's maximum exceeds it by more than Q3_ATTN_LAZY (then O and the running sum are
+      // rescaled, skipped for the whole wave when no row needs it); probabilities formed
+      // against a stale offset stay below 2^Q3_ATTN_LAZY, so the 16-bit P operand cannot
+      // overflow. The result is the same softmax: numerator and denominator share the offset.
+      // With 0 the row maximum's probability is exactly 1, the most precise choice.
+      if (kb + kKT - 1 > wt0 || kb + kKT > p.S) {  // wave-uniform: only diagonal / tail tiles
+        const int lim = min(my_t, p.S - 1);          // last live key of this lane's row
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = kb + b * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
+            s[b][e] = key > lim ? -INFINITY : s[b][e];
+          }
+      }
+      float mt = -INFINITY;
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mt = fmaxf(mt, s[b][e]);
+      mt = fmaxf(mt, __shfl_xor(mt, 32)) * p.scale_log2;  // scaled row maximum of this tile
+      if (__builtin_amdgcn_ballot_w64(mt > m_run + static_cast<float>(Q3_ATTN_LAZY))) {
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = fast_exp2(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
+        m_run = m_new;
+      }
+      const float neg_m = -m_run;
       float ls = 0.f;
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float pe = fast_exp2(s[b][e] - m_new);
+          const float pe = fast_exp2(fmaf(s[b][e], p.scale_log2, neg_m));
           s[b][e] = pe;
           ls += pe;
         }
-      ls += __shfl_xor(ls, 32);
-      l_run = l_run * alpha + ls;
-      m_run = m_new;
-#pragma unroll
-      for (int d = 0; d < 4; ++d)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
+      l_run += ls + __shfl_xor(ls, 32);
 
       // ---- O^T += V^T P^T, four 16-key steps
 #pragma unroll

@@ -33,6 +33,27 @@
 #ifndef Q3_GEMM_SCHED
 #define Q3_GEMM_SCHED 0
 #endif
+#ifndef Q3_GEMM_D2L
+#define Q3_GEMM_D2L 1
+#endif
+#ifndef Q3_GEMM_PP
+#define Q3_GEMM_PP 0
+#endif
+// LDS ring depth of the direct-to-LDS kernel (stages of 32-wide K steps; tiles that would not
+// fit in 160 KiB use 4)
+#ifndef Q3_GEMM_STAGES
+#define Q3_GEMM_STAGES 4
+#endif
+#ifndef Q3_GEMM_W4
+#define Q3_GEMM_W4 0
+#endif
+// Where bf16 weights become fp16 in the direct-to-LDS kernel: 2: always in LDS, once per
+// workgroup, by the thread whose load brought them (after its own wait, before the barrier
+// that publishes the stage); 0: always per fragment, by every wave after its read; 1: in LDS
+// for tiles whose B fragments are read by four or more waves, per fragment otherwise.
+#ifndef Q3_GEMM_CVT_LDS
+#define Q3_GEMM_CVT_LDS 1
+#endif
 
 namespace q3 {
 
@@ -272,7 +293,7 @@ __device__ __forceinline__ void g2lds(const void* g, void* l) {
 #define Q3_WAIT_VMCNT(N) \
   __builtin_amdgcn_s_waitcnt(((N) & 0xF) | (0x7 << 4) | (0xF << 8) | (((N) >> 4) << 14))
 
-template <int BN, int WM, int WN, int EPI, int OP, bool CVT>
+template <int BN, int WM, int WN, int EPI, int OP, bool CVT, int NS>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WM * WN, 64 * WM * WN),
                           amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4)))
 void gemm_d2l_kernel(const GemmParams p) {
@@ -286,17 +307,27 @@ void gemm_d2l_kernel(const GemmParams p) {
   constexpr int AJ = ASLOT / THREADS;         // loads per thread per stage, A
   constexpr int BJ = (BSLOT + THREADS - 1) / THREADS;  // loads per thread per stage, B
   constexpr int LPS = AJ + BJ;                // loads per thread per stage (equal in every wave)
+  constexpr bool SINK = (BSLOT % THREADS) != 0;
   static_assert(ASLOT % THREADS == 0 && BSLOT % 64 == 0, "tile shape");
-  __shared__ u32x4 sA0[ASLOT], sA1[ASLOT], sA2[ASLOT], sA3[ASLOT];
-  __shared__ u32x4 sB0[BSLOT], sB1[BSLOT], sB2[BSLOT], sB3[BSLOT];
-  // When BSLOT is not a multiple of THREADS, the waves past the last B block repeat a valid
-  // load into this never-read block, so every wave issues LPS loads per stage and one
-  // s_waitcnt immediate fits all of them.
-  __shared__ u32x4 sSink[(BSLOT % THREADS) ? 64 : 1];
+  static_assert(NS >= 4 && NS * (ASLOT + BSLOT) * 16 + (SINK ? 1024 : 0) <= 160 * 1024, "LDS");
+  // NS stages of the A and B tiles; with SINK, the waves past the last B block repeat a valid
+  // load into one extra block that is never read, so every wave issues LPS loads per stage
+  // and one s_waitcnt immediate fits all of them.
+  // One array per stage (not one 2-D array): the compiler can then tell the stage a DMA
+  // writes from the stages being read, and adds no wait of its own before the reads.
+  constexpr int BSZ = BSLOT + (SINK ? 64 : 0);
+  __shared__ u32x4 sA0[ASLOT], sA1[ASLOT], sA2[ASLOT], sA3[ASLOT], sA4[NS > 4 ? ASLOT : 1];
+  __shared__ u32x4 sB0[BSZ], sB1[BSZ], sB2[BSZ], sB3[BSZ], sB4[NS > 4 ? BSZ : 1];
+  auto stA = [&](int st) -> u32x4* {
+    return st == 0 ? sA0 : st == 1 ? sA1 : st == 2 ? sA2 : st == 3 ? sA3 : sA4;
+  };
+  auto stB = [&](int st) -> u32x4* {
+    return st == 0 ? sB0 : st == 1 ? sB1 : st == 2 ? sB2 : st == 3 ? sB3 : sB4;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN;
   const int wn = wave % WN;
   const int tiles_m = (p.M + kBM - 1) / kBM;
@@ -333,18 +364,14 @@ void gemm_d2l_kernel(const GemmParams p) {
       for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.f;
 
   const int nk = p.K / kBK2;
-  auto stage_a = [&](int st) -> u32x4* { return st == 0 ? sA0 : st == 1 ? sA1 : st == 2 ? sA2 : sA3; };
-  auto stage_b = [&](int st) -> u32x4* { return st == 0 ? sB0 : st == 1 ? sB1 : st == 2 ? sB2 : sB3; };
   auto issue = [&](int st, int kt) {
-    const int k0 = min(kt, nk - 1) * kBK2;  // past the end: reload the last tile (never read)
-    u32x4* a = stage_a(st);
-    u32x4* b = stage_b(st);
+    const int k0 = min(kt, nk - 1) * kBK2;  // past the end: reload the last tile (never used)
 #pragma unroll
-    for (int j = 0; j < AJ; ++j) g2lds(a_src[j] + k0, a + (wave + j * WAVES) * 64);
+    for (int j = 0; j < AJ; ++j) g2lds(a_src[j] + k0, stA(st) + (wave + j * WAVES) * 64);
 #pragma unroll
     for (int j = 0; j < BJ; ++j) {
       const int blk = wave + j * WAVES;
-      g2lds(b_src[j] + k0, blk * 64 < BSLOT ? b + blk * 64 : sSink);
+      g2lds(b_src[j] + k0, stB(st) + (blk * 64 < BSLOT ? blk : BSLOT / 64) * 64);
     }
   };
   const int fr = lane & 31;
@@ -352,26 +379,28 @@ void gemm_d2l_kernel(const GemmParams p) {
   // Fragment sets: set 0 holds sub-step 0 of a K step, set 1 sub-step 1.
   u32x4 fa[2][MI], fb[2][NI];
   auto fread = [&](int st, int ks, int set) {
-    const u32x4* a = stage_a(st);
-    const u32x4* b = stage_b(st);
     const int ch = ks * 2 + fh;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
       const int row = wm * (32 * MI) + mi * 32 + fr;
-      fa[set][mi] = a[row * 4 + (ch ^ swz4(row))];
+      fa[set][mi] = stA(st)[row * 4 + (ch ^ swz4(row))];
     }
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
       const int row = wn * (32 * NI) + ni * 32 + fr;
-      fb[set][ni] = b[row * 4 + (ch ^ swz4(row))];
+      fb[set][ni] = stB(st)[row * 4 + (ch ^ swz4(row))];
     }
   };
+  // Where the bf16 -> fp16 weight conversion happens: in LDS once per workgroup when four or
+  // more waves share each B fragment (WM >= 4), else per fragment after the read.
+  constexpr bool CVT_IN_LDS = CVT && (Q3_GEMM_CVT_LDS == 1 ? WM >= 4 : Q3_GEMM_CVT_LDS == 2);
+  constexpr bool CVT_FRAG = CVT && !CVT_IN_LDS;
   auto mfmas = [&](int set) {
     u32x4 bv[NI];
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
       bv[ni] = fb[set][ni];
-      if (CVT) {
+      if (CVT_FRAG) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) bv[ni][e] = bf16x2_to_f16x2(bv[ni][e]);
       }
@@ -381,36 +410,68 @@ void gemm_d2l_kernel(const GemmParams p) {
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = F::mfma(fa[set][mi], bv[ni], acc[mi][ni]);
   };
-  // s_waitcnt vmcnt(N) lgkmcnt(0), then the workgroup barrier; the empty asm statements keep
-  // the compiler from moving memory accesses across it.
-  auto sync = [&](auto n_vm) {
+  // In-LDS conversion of the B slots this thread loaded into stage st (its own loads of that
+  // stage must have landed).
+  auto convert_own = [&](int st) {
+    if (CVT_IN_LDS) {
+#pragma unroll
+      for (int j = 0; j < BJ; ++j) {
+        const int blk = wave + j * WAVES;
+        if (blk * 64 < BSLOT) {
+          u32x4 v = stB(st)[blk * 64 + lane];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = bf16x2_to_f16x2(v[e]);
+          stB(st)[blk * 64 + lane] = v;
+        }
+      }
+    }
+  };
+  // s_waitcnt vmcnt(N) (others unconstrained) / lgkmcnt(0) + workgroup barrier; the empty asm
+  // statements keep the compiler from moving memory accesses across them.
+  auto wait_vm = [&](auto n_vm) {
     asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt((decltype(n_vm)::value & 0xF) | (0x7 << 4) | ((decltype(n_vm)::value >> 4) << 14));
+    __builtin_amdgcn_s_waitcnt((decltype(n_vm)::value & 0xF) | (0x7 << 4) | (0xF << 8) |
+                               ((decltype(n_vm)::value >> 4) << 14));
+    asm volatile("" ::: "memory");
+  };
+  auto barrier = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((0x7 << 4) | 0xF | (0x3 << 14));  // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
 
-  issue(0, 0);
-  issue(1, 1);
-  issue(2, 2);
-  sync(std::integral_constant<int, 2 * LPS>{});  // stage 0 landed everywhere
-  fread(0, 0, 0);
-  // Step kt (stage kt % 4): wait until stage kt+1 has landed everywhere (only kt+2 may still be
-  // in flight), barrier (every wave is also past its reads of stage kt-1), refill stage kt-1's
-  // buffer with step kt+3, then the two 16-wide sub-steps; the second one reads sub-step 0 of
-  // step kt+1, so the MFMAs after the next barrier start on operands already in registers.
-  // nk is a multiple of kStages (the launcher routes other K to the register-staged kernel).
-  for (int kt = 0; kt < nk; kt += kStages) {
 #pragma unroll
-    for (int u = 0; u < kStages; ++u) {
-      sync(std::integral_constant<int, LPS>{});
-      issue((u + 3) & 3, kt + u + 3);
-      fread(u, 1, 1);
-      mfmas(0);
-      fread((u + 1) & 3, 0, 0);
-      mfmas(1);
-    }
+  for (int st = 0; st < NS - 1; ++st) issue(st, st);
+  wait_vm(std::integral_constant<int, (NS - 2) * LPS>{});  // own loads of stage 0 landed
+  convert_own(0);
+  barrier();  // stage 0 complete (and converted) everywhere
+  fread(0, 0, 0);
+  // Step kt (stage kt % NS): wait for this thread's loads of stage kt+1 (later stages may still
+  // be in flight) and convert them, barrier (stage kt+1 complete everywhere; every wave is past
+  // its reads of stage kt-1), refill stage kt-1's buffer with step kt+NS-1, then the two
+  // 16-wide sub-steps; the second one reads sub-step 0 of step kt+1, so the MFMAs after the
+  // next barrier start on operands already in registers.
+  auto step = [&](int u, int kt) {
+    wait_vm(std::integral_constant<int, (NS - 3) * LPS>{});
+    convert_own((u + 1) % NS);
+    barrier();
+    issue((u + NS - 1) % NS, kt + NS - 1);
+    fread(u, 1, 1);
+    mfmas(0);
+    fread((u + 1) % NS, 0, 0);
+    mfmas(1);
+  };
+  // Whole groups of NS steps without any branch (stage indices are constants after unrolling),
+  // then the remaining steps.
+  int kt = 0;
+  for (; kt + NS <= nk; kt += NS) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u) step(u, kt + u);
   }
+#pragma unroll
+  for (int u = 0; u < NS - 1; ++u)
+    if (kt + u < nk) step(u, kt + u);
 
   // the trailing reloads of the last tile must land before this workgroup's LDS is released
   Q3_WAIT_VMCNT(0);
@@ -575,23 +636,16 @@ int gemm_pick_nb(int M, int N, int epi) {
   return best;
 }
 
-#ifndef Q3_GEMM_D2L
-#define Q3_GEMM_D2L 1
-#endif
-#ifndef Q3_GEMM_PP
-#define Q3_GEMM_PP 0
-#endif
-#ifndef Q3_GEMM_W4
-#define Q3_GEMM_W4 0
-#endif
 
 template <int BN, int WM, int WN, int EPI, int OP, bool CVT>
 static hipError_t launch_t(const GemmParams& p, hipStream_t s) {
   const int tiles = ((p.M + kBM - 1) / kBM) * (p.N / BN);
+  constexpr int NS = (Q3_GEMM_STAGES * (kBM + BN) * 64 + (BN % 128 ? 1024 : 0) <= 160 * 1024)
+                         ? Q3_GEMM_STAGES : 4;
   if (Q3_GEMM_PP && BN == 256 && WM == 2 && WN == 4 && p.K % (kBK2 * kStages) == 0)
     gemm_pp_kernel<EPI, OP, CVT><<<tiles, 512, 0, s>>>(p);
-  else if (Q3_GEMM_D2L && p.K % (kBK2 * kStages) == 0)
-    gemm_d2l_kernel<BN, WM, WN, EPI, OP, CVT><<<tiles, 64 * WM * WN, 0, s>>>(p);
+  else if (Q3_GEMM_D2L && p.K % kBK2 == 0)
+    gemm_d2l_kernel<BN, WM, WN, EPI, OP, CVT, NS><<<tiles, 64 * WM * WN, 0, s>>>(p);
   else gemm_mfma_kernel<BN, WM, WN, EPI, OP, CVT><<<tiles, 64 * WM * WN, 0, s>>>(p);
   return hipGetLastError();
 }
