@@ -195,7 +195,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f16",
+        "weights_dtype": "bf16 (converted to fp16 on the way into LDS)",
         "data": "synthetic (seeded N(0,1) inputs, N(0,0.02) weights, 1+N(0,0.1) norms; random-init)",
         "config": {"workload": f"{cfg.name}: {L} decoder layers, hidden {cfg.hidden}, "
                                f"{cfg.n_heads}/{cfg.n_kv_heads} heads, head_dim {cfg.head_dim}, "
