@@ -118,6 +118,22 @@ def test_attention_f32(s, nh, nkv, hd):
     assert rel_err(host(o), oracle.causal_gqa_attention(q, k, v)) <= 1e-5
 
 
+@pytest.mark.parametrize("fmt,s,nh,nkv", [("f16", 333, 16, 4), ("bf16", 97, 8, 8)])
+def test_attention_64bit_address_path(monkeypatch, fmt, s, nh, nkv):
+    """K/V fetched through 64-bit addresses (the path taken when an operand's byte extent
+    exceeds the 32-bit range of buffer loads) give the same bits as the buffer-load path."""
+    hd = 128
+    q, k, v = (dev(_normal(70 + i, (s, n, hd)) * 2.0, fmt) for i, n in enumerate((nh, nkv, nkv)))
+    o_buf = q3.gqa_causal_attention(q, k, v)
+    torch.cuda.synchronize()
+    monkeypatch.setenv("Q3_ATTN_ADDR64", "1")
+    o_64 = q3.gqa_causal_attention(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(o_buf, o_64)
+    ref = oracle.causal_gqa_attention(host(q), host(k), host(v))
+    assert err16(host(o_64), ref, fmt) <= ALLOW16[fmt]
+
+
 def test_attention_gqa_equals_mha_with_repeated_kv():
     s, nh, nkv, hd = 200, 8, 2, 128
     q, k, v = (dev(_normal(30 + i, (s, n, hd)), "bf16") for i, n in enumerate((nh, nkv, nkv)))

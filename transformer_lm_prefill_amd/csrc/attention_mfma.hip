@@ -12,18 +12,43 @@
 // token blocks) are dispatched first, and with nkv = 8 the workgroups of one KV head land on
 // one XCD (ids congruent mod 8), so that head's K/V stays in that XCD's L2.
 //
-// Per wave and 64-key tile, with v_mfma_f32_32x32x16_bf16:
+// Per wave and 64-key tile, with v_mfma_f32_32x32x16_{f16,bf16}:
 //   S^T = K Q^T     (A = K from LDS, B = Q^T held in registers)  -> lane l holds query row
-//                   l%32 and 16 of the 32 keys of each 32-key block, so the row maximum and
-//                   sum need one cross-lane exchange (lanes l and l^32);
+//                   l%32 and 16 of the 32 keys of each 32-key block, so the row maximum
+//                   needs one cross-lane exchange (lanes l and l^32, v_permlane32_swap);
 //   O^T += V^T P^T  (A = V^T from a transposed LDS copy, B = P^T straight from the S^T
-//                   accumulators converted to bf16) -> lane l keeps query row l%32 of the
+//                   accumulators converted to 16 bits) -> lane l keeps query row l%32 of the
 //                   output, so the rescale by exp2(m_old - m_new) and the final 1/sum are
 //                   lane-local. The K index of this product enumerates the tile's keys in the
 //                   order the S^T accumulators hold them; V^T is read in that same order.
+//
+// Software pipelining. On CDNA the MFMA unit and the VALU overlap well within one wave's
+// instruction stream and much less across the two waves of a SIMD, so every wave overlaps
+// its own MFMAs with its own softmax arithmetic. Iteration t, one barrier per iteration:
+//   A  S^T(t) = K(t) Q^T                  || P(t-1) = exp2(S(t-1) c - m), row sums, packing
+//   B  O^T += V^T(t-1) P^T(t-1)           || row maxima of S(t) (after the causal mask)
+//   C  running maximum update; O and the sums rescaled when it moved
+// S(t) and S(t-1) live in two register sets that swap roles every iteration.
+//
+// LDS: K and V^T tiles, two slots each. Rows are padded instead of XOR-swizzled, so every
+// fragment address is a per-lane base plus a compile-time offset:
+//   K   [64 keys][17 x 16 B]  16 chunks of 8 hd + 1 pad; a 16-lane read of one chunk column
+//                             touches 16 distinct 16-byte bank groups;
+//   V^T [128 hd][18 x 8 B]    16 granules of 4 keys + 2 pad. Within each 32-key block the
+//                             granules are stored in the order 0,2,1,3,4,6,5,7, so the two
+//                             granules an MFMA lane needs (4-key groups i and i+2 of the S^T
+//                             accumulator order) are adjacent: one 16-byte read.
+// Waves 0-3 stage K tiles, waves 4-7 V tiles (transposed on the way into LDS); the global
+// loads of tile t+1 (K) and t (V) are issued at the top of iteration t and written to LDS at
+// its end, into slots last read in iteration t-1.
+#include <cstdlib>
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
+// Exponent-offset slack (log2 units): the running maximum moves only when a row's maximum
+// exceeds it by more than this. 0 keeps the row maximum's probability exactly 1.
 #ifndef Q3_ATTN_LAZY
 #define Q3_ATTN_LAZY 0
 #endif
@@ -31,37 +56,48 @@
 namespace q3 {
 
 constexpr int kHD = 128;
-constexpr int kKT = 64;          // keys per tile
+constexpr int kKT = 64;    // keys per tile
 constexpr int kAttnWaves = 8;
 constexpr int kAttnThreads = 64 * kAttnWaves;
+constexpr int kKRow = 17;  // u32x4 per padded K row
+constexpr int kVRow = 18;  // u32x2 per padded V^T row
 
-// K tile in LDS: [64 keys][16 chunks of 8 hd], chunk index XOR-swizzled by key.
-__device__ __forceinline__ int swz_k(int key) { return key & 15; }
-// V^T tile in LDS: [128 hd][16 granules of 4 keys], granule index XOR-swizzled by hd row.
-__device__ __forceinline__ int swz_v(int hd) { return (hd ^ (hd >> 4)) & 15; }
+// position of 4-key granule gi (0..15 within the tile) in a V^T row: 4h+2x+s -> 4h+2s+x
+__device__ __forceinline__ int vt_pos(int gi) {
+  return (gi & 12) | ((gi & 1) << 1) | ((gi >> 1) & 1);
+}
 
-template <int G, int OP>
+// max(x[l], x[l ^ 32]) for every lane l: v_permlane32_swap exchanges the two lane halves
+// between its two operands, so the pair it returns holds x[l] and x[l ^ 32] in some order
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+template <int G, int OP, bool BUF>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(const AttnParams p) {
   using F = Fmt<OP>;
-  constexpr int TOK = 32 * kAttnWaves / G;  // tokens per workgroup
-  __shared__ u32x4 Ks[2][kKT * 16];
-  __shared__ u32x2 Vts[2][kHD * 16];
+  constexpr int NB = 8 / G;
+  constexpr int TOK = 32 * NB;
+  __shared__ __attribute__((aligned(16))) u32x4 Ks[2][kKT * kKRow];
+  __shared__ __attribute__((aligned(16))) u32x2 Vts[2][kHD * kVRow];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform by construction
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nblk = (p.S + TOK - 1) / TOK;
   const int g = blockIdx.x % p.nkv;
   const int blk = nblk - 1 - blockIdx.x / p.nkv;
   const int t0 = blk * TOK;
-  const int hq = g * G + wave % G;
-  const int wt0 = t0 + (wave / G) * 32;  // this wave's first query token
   const int qrow = lane & 31;
   const int hi = lane >> 5;
-  const int my_t = wt0 + qrow;
+  const int bt = wave % NB, hl = wave / NB;
+  const int hq = g * G + hl;
+  const int my_t = t0 + 32 * bt + qrow;
+  const int lim = min(my_t, p.S - 1);
+  const int ntiles = (min(p.S, t0 + TOK) + kKT - 1) / kKT;
 
-  // Q^T operand: lane holds q[my_t, hq, 16*ks + 8*hi .. +8] for ks = 0..7.
   u32x4 qf[8];
   {
     const bool ok = my_t < p.S;
@@ -79,164 +115,209 @@ void attn_fwd_kernel(const AttnParams p) {
   for (int d = 0; d < 4; ++d)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[d][e] = 0.f;
-  float m_run = -INFINITY;  // exponent offset: running max of scaled scores (base 2)
-  float l_run = 0.f;
+  f32x16 sa[2], sb[2];
+  u32x4 pf[4];
+  float m_run = -INFINITY;
+  float l_part = 0.f;
 
-  const int wg_end = min(p.S, t0 + TOK);        // keys this workgroup needs
-  const int wave_end = min(p.S, wt0 + 32);      // keys this wave needs
-  const bool wave_live = wt0 < p.S;
-  const int ntiles = (wg_end + kKT - 1) / kKT;
-
-  // Global -> register staging. Waves 0-3 fetch K (4 chunks of 16 B each), waves 4-7 fetch
-  // V as 4 consecutive keys x 8 hd values per thread, to be written transposed.
-  const bool k_loader = tid < 256;
-  const int lt = tid & 255;
+  // staging: waves 0-3 carry K chunks tv + 256 i; waves 4-7 carry hd chunk vc of keys 4vg..+3
+  const bool k_loader = wave < 4;  // wave-uniform (the buffer descriptor depends on it)
+  const int tv = tid & 255;
+  const int vg = tv & 15, vc = tv >> 4;
+  const int vpos = vt_pos(vg);
   u32x4 st[4];
-  auto gload = [&](int kb) {
-    if (k_loader) {
+  // K / V rows come in through buffer loads when the operand's byte extent fits the 32-bit
+  // range (BUF): a per-thread byte offset within the tile plus the tile's row offset in a
+  // scalar register, rows at or past S reading as zeros through the range check (those keys
+  // are masked), so the loop carries no 64-bit address arithmetic. Otherwise through 64-bit
+  // addresses with the row index clamped to S - 1.
+  const int64_t row_elems = k_loader ? p.k_stride : p.v_stride;
+  const uint16_t* gbase = (k_loader ? p.k : p.v) + g * kHD;
+  int trow[4], tcol[4];  // row within the tile and element column of this thread's chunks
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tv + 256 * i;
+    trow[i] = k_loader ? c >> 4 : 4 * vg + i;
+    tcol[i] = k_loader ? (c & 15) * 8 : vc * 8;
+  }
+  const int row_bytes = static_cast<int>(2 * row_elems);  // used only when BUF
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(gbase), static_cast<short>(0), p.S * row_bytes, 0x00020000);
+  int voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) voff[i] = trow[i] * row_bytes + 2 * tcol[i];
+  auto gload = [&](int tile) {
+    if constexpr (BUF) {
+      const int soff = tile * kKT * row_bytes;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int c = lt + 256 * i;
-        const int key = min(kb + (c >> 4), p.S - 1);
-        st[i] = *reinterpret_cast<const u32x4*>(p.k + static_cast<int64_t>(key) * p.k_stride +
-                                                 g * kHD + (c & 15) * 8);
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff[i], soff, 0);
+        st[i] = u32x4{v[0], v[1], v[2], v[3]};
       }
     } else {
-      const int kg = lt >> 4, hc = lt & 15;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = min(kb + 4 * kg + r, p.S - 1);
-        st[r] = *reinterpret_cast<const u32x4*>(p.v + static_cast<int64_t>(key) * p.v_stride +
-                                                 g * kHD + hc * 8);
+      for (int i = 0; i < 4; ++i) {
+        const int row = min(tile * kKT + trow[i], p.S - 1);
+        st[i] = *reinterpret_cast<const u32x4*>(gbase + row * row_elems + tcol[i]);
       }
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](int tile) {
     if (k_loader) {
+      u32x4* dst = Ks[tile & 1];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int c = lt + 256 * i;
-        const int key = c >> 4;
-        Ks[buf][key * 16 + ((c & 15) ^ swz_k(key))] = st[i];
+        const int c = tv + 256 * i;
+        dst[(c >> 4) * kKRow + (c & 15)] = st[i];
       }
     } else {
-      const int kg = lt >> 4, hc = lt & 15;
-      // st[r] holds v[key 4kg+r][hd 8hc .. 8hc+7] as 4 words of two 16-bit values each; the
-      // granule for hd row 8hc+e gathers the e-th value of the four keys (byte permutes).
+      u32x2* dst = Vts[tile & 1];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int w = e >> 1;
         const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        const int hd = hc * 8 + e;
-        Vts[buf][hd * 16 + (kg ^ swz_v(hd))] =
+        dst[(vc * 8 + e) * kVRow + vpos] =
             u32x2{__builtin_amdgcn_perm(st[1][w], st[0][w], sel), __builtin_amdgcn_perm(st[3][w], st[2][w], sel)};
       }
     }
   };
+  auto barrier = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((0x7 << 4) | 0xF | (0x3 << 14));  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
+  const int kbase = qrow * kKRow + hi;
+  const int vbase = qrow * kVRow + 2 * hi;
 
-  for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
-    const int kb = it * kKT;
-    const bool more = it + 1 < ntiles;
-    if (more) gload(kb + kKT);
+  auto exp_part = [&](f32x16 (&sp)[2]) {
+    const float neg_m = -m_run;
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float pe = fast_exp2(fmaf(sp[b][e], p.scale_log2, neg_m));
+        sp[b][e] = pe;
+        ls[e & 3] += pe;
+      }
+    l_part += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+#pragma unroll
+    for (int st16 = 0; st16 < 4; ++st16) {
+      const int b = st16 >> 1, half = st16 & 1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pf[st16][e] = F::pack2(sp[b][half * 8 + 2 * e], sp[b][half * 8 + 2 * e + 1]);
+    }
+  };
+  auto pv_all = [&](int tile) {
+    const u32x2* vp = Vts[tile & 1] + vbase;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int st16 = i >> 2, d = i & 3, b = st16 >> 1, half = st16 & 1;
+      const u32x4 vv = *reinterpret_cast<const u32x4*>(vp + d * 32 * kVRow + 8 * b + 4 * half);
+      o[d] = F::mfma(vv, pf[st16], o[d]);
+    }
+  };
 
-    if (wave_live && kb < wave_end) {
-      // ---- S^T = K Q^T for two 32-key blocks (the two accumulation chains interleaved)
-      f32x16 s[2];
+  // one iteration: tile t into sc; sp holds S(t-1) (unless first)
+  auto iter = [&](int t, f32x16 (&sc)[2], f32x16 (&sp)[2], auto first) {
+    constexpr bool FIRST = decltype(first)::value;
+    const int kb = t * kKT;
+    const bool next = t + 1 < ntiles;
+    if (k_loader) {
+      if (next) gload(t + 1);
+    } else {
+      gload(t);
+    }
+    // A
+    const u32x4* kp = Ks[t & 1] + kbase;
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) s[b][e] = 0.f;
+      for (int e = 0; e < 16; ++e) sc[b][e] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const int ch = 2 * ks + hi;
+    for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          const int key = b * 32 + qrow;
-          s[b] = F::mfma(Ks[buf][key * 16 + (ch ^ swz_k(key))], qf[ks], s[b]);
-        }
-      }
-      // ---- causal mask, online softmax (base 2). The exponent offset m_run moves only when a
-      // row's maximum exceeds it by more than Q3_ATTN_LAZY (then O and the running sum are
-      // rescaled, skipped for the whole wave when no row needs it); probabilities formed
-      // against a stale offset stay below 2^Q3_ATTN_LAZY, so the 16-bit P operand cannot
-      // overflow. The result is the same softmax: numerator and denominator share the offset.
-      // With 0 the row maximum's probability is exactly 1, the most precise choice.
-      if (kb + kKT - 1 > wt0 || kb + kKT > p.S) {  // wave-uniform: only diagonal / tail tiles
-        const int lim = min(my_t, p.S - 1);          // last live key of this lane's row
+      for (int b = 0; b < 2; ++b) sc[b] = F::mfma(kp[b * 32 * kKRow + 2 * ks], qf[ks], sc[b]);
+    if (!FIRST) {
+      exp_part(sp);
+      // anchor P^T here, so that the exponentials are scheduled among the S^T MFMAs above
+      // instead of being sunk past the mask branch
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int key = kb + b * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
-            s[b][e] = key > lim ? -INFINITY : s[b][e];
-          }
-      }
-      float mt = -INFINITY;
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mt = fmaxf(mt, s[b][e]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32)) * p.scale_log2;  // scaled row maximum of this tile
-      if (__builtin_amdgcn_ballot_w64(mt > m_run + static_cast<float>(Q3_ATTN_LAZY))) {
-        const float m_new = fmaxf(m_run, mt);
-        const float alpha = fast_exp2(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int d = 0; d < 4; ++d)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
-        m_run = m_new;
-      }
-      const float neg_m = -m_run;
-      float ls = 0.f;
+      for (int st16 = 0; st16 < 4; ++st16) asm volatile("" ::"v"(pf[st16]));
+    }
+    // causal mask on diagonal / tail tiles (wave-uniform branch)
+    if (kb + kKT - 1 > t0 + 32 * bt || kb + kKT > p.S) {
+      asm volatile("");
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float pe = fast_exp2(fmaf(s[b][e], p.scale_log2, neg_m));
-          s[b][e] = pe;
-          ls += pe;
+          const int key = kb + b * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
+          sc[b][e] = key > lim ? -INFINITY : sc[b][e];
         }
-      l_run += ls + __shfl_xor(ls, 32);
-
-      // ---- O^T += V^T P^T, four 16-key steps
-#pragma unroll
-      for (int st16 = 0; st16 < 4; ++st16) {
-        const int b = st16 >> 1, half = st16 & 1;
-        u32x4 pf;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pf[e] = F::pack2(s[b][half * 8 + 2 * e], s[b][half * 8 + 2 * e + 1]);
-        // this lane's 8 K-slots are keys 32b + 16half + 4hi + {0..3} and the same + 8
-        const int gA = (b * 32 + half * 16) / 4 + hi;
-        const int gB = gA + 2;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const int hd = d * 32 + qrow;
-          const u32x2 lo = Vts[buf][hd * 16 + (gA ^ swz_v(hd))];
-          const u32x2 hi2 = Vts[buf][hd * 16 + (gB ^ swz_v(hd))];
-          const u32x4 vv = {lo[0], lo[1], hi2[0], hi2[1]};
-          o[d] = F::mfma(vv, pf, o[d]);
-        }
-      }
     }
+    // B
+    if (!FIRST) pv_all(t - 1);
+    float mt = sc[0][0];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mt = fmaxf(mt, sc[b][e]);
+    mt = max_halves(mt) * p.scale_log2;
+    // C
+    if (__builtin_amdgcn_ballot_w64(mt > m_run + static_cast<float>(Q3_ATTN_LAZY))) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = fast_exp2(m_run - m_new);
+      l_part *= alpha;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
+      m_run = m_new;
+    }
+    // stage K(t+1) / V(t)
+    __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0)
+    if (k_loader) {
+      if (next) lstore(t + 1);
+    } else {
+      lstore(t);
+    }
+    barrier();
+  };
 
-    if (more) lstore(buf ^ 1);
-    __syncthreads();
+  // prologue: K(0)
+  if (k_loader) {
+    gload(0);
+    lstore(0);
   }
+  barrier();
 
-  if (wave_live && my_t < p.S) {
+  using T_ = std::integral_constant<bool, true>;
+  using F_ = std::integral_constant<bool, false>;
+  iter(0, sa, sb, T_{});
+  int t = 1;
+  for (; t + 1 < ntiles; t += 2) {
+    iter(t, sb, sa, F_{});
+    iter(t + 1, sa, sb, F_{});
+  }
+  if (t < ntiles) {
+    iter(t, sb, sa, F_{});
+    exp_part(sb);
+  } else {
+    exp_part(sa);
+  }
+  pv_all(ntiles - 1);
+
+  const float l_run = l_part + __shfl_xor(l_part, 32);
+  if (my_t < p.S) {
     const float inv = 1.0f / l_run;
     uint16_t* op = p.o + static_cast<int64_t>(my_t) * p.o_stride + hq * kHD;
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        // elements e = 4*q4 .. 4*q4+3 are hd rows d*32 + 8*q4 + 4*hi + 0..3
         const int hd0 = d * 32 + 8 * q4 + 4 * hi;
         u32x2 w;
         w[0] = F::pack2(o[d][4 * q4 + 0] * inv, o[d][4 * q4 + 1] * inv);
@@ -250,7 +331,15 @@ template <int G, int OP>
 static hipError_t launch_g(const AttnParams& p, hipStream_t s) {
   constexpr int TOK = 32 * kAttnWaves / G;
   const int nblk = (p.S + TOK - 1) / TOK;
-  attn_fwd_kernel<G, OP><<<nblk * p.nkv, kAttnThreads, 0, s>>>(p);
+  // Buffer loads address K and V with 32-bit byte offsets from the head's column; the extent
+  // covers the rows a last partial tile reaches past S. Q3_ATTN_ADDR64 (environment) forces
+  // the 64-bit address path, so that it can be tested at small sizes.
+  const int64_t extent =
+      2 * (static_cast<int64_t>(p.S) + kKT) * (p.k_stride > p.v_stride ? p.k_stride : p.v_stride);
+  if (extent <= 0x7fffffff && std::getenv("Q3_ATTN_ADDR64") == nullptr)
+    attn_fwd_kernel<G, OP, true><<<nblk * p.nkv, kAttnThreads, 0, s>>>(p);
+  else
+    attn_fwd_kernel<G, OP, false><<<nblk * p.nkv, kAttnThreads, 0, s>>>(p);
   return hipGetLastError();
 }
 
