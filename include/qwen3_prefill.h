@@ -24,6 +24,8 @@
  * Conventions shared by every entry point:
  *   - Every tensor pointer is a DEVICE pointer owned by the caller. The library never allocates
  *     or frees device memory inside these calls and keeps no pointer after a call returns.
+ *     Tensor pointers must be 16-byte aligned (rows move in 16-byte vectors); a misaligned one
+ *     returns QWEN3_ERR_INVALID_ARG. Allocator-returned buffers (hipMalloc, torch) satisfy this.
  *   - Matrices are row-major. Weights use the torch nn.Linear layout [out_features, in_features].
  *     Activations are token-major: [seq_len, ...]; q/k/v/attention outputs are [seq_len, heads,
  *     head_dim] contiguous.

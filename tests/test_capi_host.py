@@ -131,6 +131,24 @@ def test_partial_overlap_rejected(lib):
     assert "overlap" in lib.qwen3_last_error().decode()
 
 
+def test_misaligned_pointers_rejected(lib):
+    odd = ctypes.c_void_p(0x1008)   # 8-byte aligned only
+    c = _cfg()
+    rc = lib.qwen3_layer_prefill(ctypes.byref(c), ctypes.byref(_weights()), odd, odd, 16, FAKE,
+                                 None, 0, None, ctypes.c_void_p(0x100000),
+                                 lib.qwen3_layer_workspace_bytes(ctypes.byref(c), 16), None)
+    assert rc == 1 and "16-byte" in lib.qwen3_last_error().decode()
+    w = _weights()
+    w.w_down = odd
+    assert _call_layer(lib, c, weights=w) == 1
+    assert lib.gqa_causal_attention(FAKE, odd, FAKE, FAKE, 8, 4, 2, 128, 0.1, 1, None) == 1
+    assert "16-byte" in lib.qwen3_last_error().decode()
+    assert lib.swiglu_ffn(FAKE, FAKE, odd, FAKE, None, FAKE, 8, 2048, 6144, 1, 2, 0, FAKE, 1 << 30, None) == 1
+    assert lib.rms_norm_rows(FAKE, FAKE, odd, 4, 256, 1e-6, 1, 1, None) == 1
+    sec = (ctypes.c_int32 * 3)(24, 20, 20)
+    assert lib.qk_norm_mrope(odd, FAKE, 4, 4, 2, 128, FAKE, FAKE, 1e-6, FAKE, 5e6, sec, 1, 1, None) == 1
+
+
 def test_sub_op_argument_checks(lib):
     sec = (ctypes.c_int32 * 3)(24, 20, 20)
     assert lib.qk_norm_mrope(FAKE, FAKE, 0, 4, 2, 128, FAKE, FAKE, 1e-6, FAKE, 5e6, sec, 1, 1, None) == 1

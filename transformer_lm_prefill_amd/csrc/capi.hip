@@ -11,6 +11,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 #include <map>
 #include <mutex>
 #include <string>
@@ -93,6 +94,13 @@ int check_formats(qwen3_dtype w, qwen3_dtype a) {
   return QWEN3_OK;
 }
 size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+
+// Kernels move rows in 16-byte vectors: every tensor pointer must be 16-byte aligned.
+bool misaligned16(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (p && reinterpret_cast<uintptr_t>(p) % 16 != 0) return true;
+  return false;
+}
 
 int check_heads(int32_t nh, int32_t nkv, int32_t hd, qwen3_dtype dt) {
   const char* dname = dt == QWEN3_F16 ? "f16" : "bf16";
@@ -269,6 +277,9 @@ int qwen3_layer_prefill(const qwen3_layer_cfg* cfg, const qwen3_layer_weights* w
     if (!wp[i]) return fail(QWEN3_ERR_INVALID_ARG, "weight %s is NULL", wn[i]);
   if (!x_in || !x_out) return fail(QWEN3_ERR_INVALID_ARG, "x_in / x_out is NULL");
   if (!positions) return fail(QWEN3_ERR_INVALID_ARG, "positions is NULL");
+  if (misaligned16({x_in, x_out, ds, w->attn_norm, w->wq, w->wk, w->wv, w->q_norm, w->k_norm, w->wo,
+                    w->ffn_norm, w->w_gate, w->w_up, w->w_down}))
+    return fail(QWEN3_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
   if (n_ds < 0 || n_ds > seq_len)
     return fail(QWEN3_ERR_INVALID_ARG, "n_ds (%d) must be in [0, seq_len = %d]", n_ds, seq_len);
   if (n_ds == 0 && ds) return fail(QWEN3_ERR_INVALID_ARG, "a DeepStack slab was given with n_ds == 0");
@@ -354,6 +365,8 @@ int qk_norm_mrope(void* q, void* k, int32_t seq_len, int32_t n_heads, int32_t n_
   if (st) return st;
   if ((n_heads > 0 && (!q || !q_norm)) || (n_kv_heads > 0 && (!k || !k_norm)) || !positions)
     return fail(QWEN3_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (misaligned16({q, k, q_norm, k_norm}))
+    return fail(QWEN3_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
   if (!(eps >= 0.f) || !(theta > 1.f)) return fail(QWEN3_ERR_INVALID_ARG, "eps must be >= 0 and theta > 1");
   q3::RopeParams p{q, k, static_cast<int64_t>(n_heads) * head_dim, static_cast<int64_t>(n_kv_heads) * head_dim,
                    seq_len, n_heads, n_kv_heads, q_norm, k_norm, norm_dtype, positions, eps,
@@ -369,6 +382,7 @@ int gqa_causal_attention(const void* q, const void* k, const void* v, void* out,
   int st = check_heads(n_heads, n_kv_heads, head_dim, dtype);
   if (st) return st;
   if (!q || !k || !v || !out) return fail(QWEN3_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (misaligned16({q, k, v, out})) return fail(QWEN3_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
   if (!(scale > 0.f) || !std::isfinite(scale)) return fail(QWEN3_ERR_INVALID_ARG, "scale must be finite and > 0");
   return run_attention(q, k, v, out, static_cast<int64_t>(n_heads) * head_dim,
                        static_cast<int64_t>(n_kv_heads) * head_dim, static_cast<int64_t>(n_kv_heads) * head_dim,
@@ -388,6 +402,8 @@ int swiglu_ffn(const void* x_normed, const void* w_gate, const void* w_up, const
     return fail(QWEN3_ERR_UNSUPPORTED, "hidden (%d) must be a positive multiple of 256", hidden);
   if (ffn < 128 || ffn % 128 != 0) return fail(QWEN3_ERR_UNSUPPORTED, "ffn (%d) must be a positive multiple of 128", ffn);
   if (!x_normed || !w_gate || !w_up || !w_down || !out) return fail(QWEN3_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (misaligned16({x_normed, w_gate, w_up, w_down, residual, out, workspace}))
+    return fail(QWEN3_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
   if (out_dtype != QWEN3_F32 && (residual || out_dtype != x_dtype))
     return fail(QWEN3_ERR_UNSUPPORTED, "a 16-bit output must have x_dtype and no residual");
   const size_t need = swiglu_ffn_workspace_bytes(seq_len, ffn, x_dtype);
@@ -404,6 +420,7 @@ int rms_norm_rows(const float* x, const void* w, void* y, int32_t rows, int32_t 
   if (hidden < 256 || hidden % 256 != 0 || hidden > 16384)
     return fail(QWEN3_ERR_UNSUPPORTED, "hidden (%d) must be a multiple of 256 in [256, 16384]", hidden);
   if (!x || !w || !y) return fail(QWEN3_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (misaligned16({x, w, y})) return fail(QWEN3_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
   if (!(eps >= 0.f)) return fail(QWEN3_ERR_INVALID_ARG, "eps must be >= 0");
   return run_rmsnorm(x, w, w_dtype, y, y_dtype, rows, hidden, eps, static_cast<hipStream_t>(stream));
 }

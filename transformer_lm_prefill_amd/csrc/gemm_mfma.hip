@@ -54,6 +54,14 @@
 #ifndef Q3_GEMM_CVT_LDS
 #define Q3_GEMM_CVT_LDS 1
 #endif
+// 1: for fp32 outputs (with residual), the direct-to-LDS kernel computes C^T blocks (weight
+// fragment as the MFMA A operand), so each lane ends up with runs of 4 consecutive output
+// columns of one row: one 16-byte residual load and store per run instead of four 4-byte ones.
+// (For 16-bit outputs the untransposed layout, 64 contiguous bytes per row and store, measured
+// faster.)
+#ifndef Q3_GEMM_TRANS
+#define Q3_GEMM_TRANS 1
+#endif
 
 namespace q3 {
 
@@ -103,13 +111,59 @@ __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)
 
 // Epilogue shared by the kernels: stores a wave's accumulators. Accumulator element e of
 // block (mi, ni) in lane l holds row 8*(e/4) + 4*(l/32) + e%4 and column l%32 of that block.
-template <int BN, int WM, int WN, int EPI, int OP>
+template <int BN, int WM, int WN, int EPI, int OP, bool TRANS = false>
 __device__ __forceinline__ void gemm_epilogue(const GemmParams& p,
                                               f32x16 (&acc)[kBM / WM / 32][BN / WN / 32], int tm,
                                               int tn, int wm, int wn, int lane) {
   using F = Fmt<OP>;
   constexpr int MI = kBM / WM / 32;
   constexpr int NI = BN / WN / 32;
+  if (TRANS) {
+    // acc[mi][ni] holds the transposed block: lane l has row m = l%32 of block mi and, in
+    // elements 4q..4q+3, the four consecutive columns 8q + 4*(l/32) + 0..3 of block ni
+    const int m = tm * kBM + wm * (32 * MI) + (lane & 31);
+    const int c4 = 4 * (lane >> 5);
+    if (m >= p.M) return;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      const int row = m + mi * 32;
+      if (row >= p.M) break;
+      if (EPI == EPI_SWIGLU_16) {
+        uint16_t* C = static_cast<uint16_t*>(p.C) + static_cast<int64_t>(row) * p.ldc;
+#pragma unroll
+        for (int ni = 0; ni < NI / 2; ++ni)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int f = tn * (BN / 2) + wn * (16 * NI) + ni * 32 + 8 * q + c4;
+            float h[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) h[r] = silu_f(acc[mi][ni][4 * q + r]) * acc[mi][ni + NI / 2][4 * q + r];
+            *reinterpret_cast<u32x2*>(C + f) = u32x2{F::pack2(h[0], h[1]), F::pack2(h[2], h[3])};
+          }
+      } else {
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int n = tn * BN + wn * 32 * NI + ni * 32 + 8 * q + c4;
+            const f32x16& a = acc[mi][ni];
+            if (EPI == EPI_STORE_16) {
+              uint16_t* C = static_cast<uint16_t*>(p.C) + static_cast<int64_t>(row) * p.ldc + n;
+              *reinterpret_cast<u32x2*>(C) =
+                  u32x2{F::pack2(a[4 * q], a[4 * q + 1]), F::pack2(a[4 * q + 2], a[4 * q + 3])};
+            } else {
+              f32x4 v = {a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+              if (p.R) {
+                const f32x4 r = *reinterpret_cast<const f32x4*>(p.R + static_cast<int64_t>(row) * p.ldr + n);
+                v += r;
+              }
+              *reinterpret_cast<f32x4*>(static_cast<float*>(p.C) + static_cast<int64_t>(row) * p.ldc + n) = v;
+            }
+          }
+      }
+    }
+    return;
+  }
   const int col_in_blk = lane & 31;
   const int row_base = tm * kBM + wm * (32 * MI) + 4 * (lane >> 5);
   if (EPI == EPI_SWIGLU_16) {
@@ -308,6 +362,7 @@ void gemm_d2l_kernel(const GemmParams p) {
   constexpr int BJ = (BSLOT + THREADS - 1) / THREADS;  // loads per thread per stage, B
   constexpr int LPS = AJ + BJ;                // loads per thread per stage (equal in every wave)
   constexpr bool SINK = (BSLOT % THREADS) != 0;
+  constexpr bool TRANS = Q3_GEMM_TRANS && EPI == EPI_STORE_F32;  // accumulators hold C^T blocks
   static_assert(ASLOT % THREADS == 0 && BSLOT % 64 == 0, "tile shape");
   static_assert(NS >= 4 && NS * (ASLOT + BSLOT) * 16 + (SINK ? 1024 : 0) <= 160 * 1024, "LDS");
   // NS stages of the A and B tiles; with SINK, the waves past the last B block repeat a valid
@@ -408,7 +463,9 @@ void gemm_d2l_kernel(const GemmParams p) {
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = F::mfma(fa[set][mi], bv[ni], acc[mi][ni]);
+      for (int ni = 0; ni < NI; ++ni)
+        acc[mi][ni] = TRANS ? F::mfma(bv[ni], fa[set][mi], acc[mi][ni])
+                            : F::mfma(fa[set][mi], bv[ni], acc[mi][ni]);
   };
   // In-LDS conversion of the B slots this thread loaded into stage st (its own loads of that
   // stage must have landed).
@@ -475,7 +532,7 @@ void gemm_d2l_kernel(const GemmParams p) {
 
   // the trailing reloads of the last tile must land before this workgroup's LDS is released
   Q3_WAIT_VMCNT(0);
-  gemm_epilogue<BN, WM, WN, EPI, OP>(p, acc, tm, tn, wm, wn, lane);
+  gemm_epilogue<BN, WM, WN, EPI, OP, TRANS>(p, acc, tm, tn, wm, wn, lane);
 }
 
 // ---------------------------------------------------------------------------------------
