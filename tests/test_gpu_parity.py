@@ -184,6 +184,23 @@ def test_swiglu_ffn(wdt, xdt, s, h, f, resid):
     assert err <= (TOL["f32"] if wdt == "f32" else TOL["bf16"])
 
 
+@pytest.mark.parametrize("wdt,out_dtype", [("bf16", None), ("f16", torch.float16)])
+def test_swiglu_ffn_64bit_address_path(monkeypatch, wdt, out_dtype):
+    """GEMM operands fetched through 64-bit addresses (taken when an operand's byte extent
+    exceeds the 32-bit range of buffer loads) give the same bits as the buffer-load path."""
+    s, h, f = 300, 512, 640
+    x = dev(_normal(80, (s, h)), "f16")
+    wg, wu, wd = (dev(_normal(81 + i, sh, std=0.02), wdt) for i, sh in enumerate(((f, h), (f, h), (h, f))))
+    r = None if out_dtype is not None else dev(_normal(84, (s, h), dtype="f32"))
+    kw = dict(residual=r) if out_dtype is None else dict(out_dtype=out_dtype)
+    o_buf = q3.swiglu_ffn(x, wg, wu, wd, **kw)
+    torch.cuda.synchronize()
+    monkeypatch.setenv("Q3_GEMM_ADDR64", "1")
+    o_64 = q3.swiglu_ffn(x, wg, wu, wd, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o_buf, o_64)
+
+
 def test_swiglu_ffn_bf16_out():
     s, h, f = 100, 512, 384
     x = _normal(60, (s, h))

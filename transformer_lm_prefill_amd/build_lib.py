@@ -56,7 +56,8 @@ def build(verbose=False, jobs=None, defines=(), lib_path=LIB, build_dir=BUILD):
             if verbose and out.strip():
                 print(out)
     tmp = lib_path + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
+    # --no-undefined: a kernel whose host-side launch stub was not emitted fails here, not at load
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", *objs, "-o", tmp])
     os.replace(tmp, lib_path)
     if verbose:
         print(f"built {lib_path}")

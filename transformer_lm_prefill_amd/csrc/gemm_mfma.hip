@@ -25,10 +25,12 @@
 //   and the tile stores are free of bank conflicts (rocprofv3 SQ_LDS_BANK_CONFLICT reads 0);
 //   workgroup ids remapped so each XCD (ids congruent mod 8) owns a compact band of tiles
 //   sharing A rows and B columns in its own L2.
+#include <algorithm>
+#include <cstdlib>
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
-
-#include <type_traits>
 
 #ifndef Q3_GEMM_SCHED
 #define Q3_GEMM_SCHED 0
@@ -59,6 +61,13 @@
 // columns of one row: one 16-byte residual load and store per run instead of four 4-byte ones.
 // (For 16-bit outputs the untransposed layout, 64 contiguous bytes per row and store, measured
 // faster.)
+// 1: direct-to-LDS loads through buffer descriptors where the operands fit 32-bit offsets
+#ifndef Q3_GEMM_BUF
+#define Q3_GEMM_BUF 1
+#endif
+#ifndef Q3_GEMM_SB
+#define Q3_GEMM_SB 0
+#endif
 #ifndef Q3_GEMM_TRANS
 #define Q3_GEMM_TRANS 1
 #endif
@@ -104,6 +113,29 @@ __device__ __forceinline__ const uint16_t* b_row(const GemmParams& p, int tn, in
     if (n < p.nseg0) return p.B0 + static_cast<int64_t>(n) * p.ldb;
     if (n < p.nseg1) return p.B1 + static_cast<int64_t>(n - p.nseg0) * p.ldb;
     return p.B2 + static_cast<int64_t>(n - p.nseg1) * p.ldb;
+  }
+}
+
+// Segment of B holding LDS tile row r of tile column tn (the same rows b_row reads): base
+// pointer, row index within the segment, and the segment's row count.
+template <int BN, int WN, int EPI>
+__device__ __forceinline__ void b_seg(const GemmParams& p, int tn, int r, const uint16_t*& base,
+                                      int& idx, int& rows) {
+  if (EPI == EPI_SWIGLU_16) {
+    constexpr int SEG = BN / WN / 2;
+    const int seg = r / SEG;
+    base = (seg & 1) ? p.B1 : p.B0;
+    idx = tn * (BN / 2) + (seg >> 1) * SEG + (r % SEG);
+    rows = p.N / 2;
+  } else {
+    const int n = tn * BN + r;
+    if (n < p.nseg0) {
+      base = p.B0; idx = n; rows = p.nseg0;
+    } else if (n < p.nseg1) {
+      base = p.B1; idx = n - p.nseg0; rows = p.nseg1 - p.nseg0;
+    } else {
+      base = p.B2; idx = n - p.nseg1; rows = p.N - p.nseg1;
+    }
   }
 }
 
@@ -342,12 +374,17 @@ typedef __attribute__((address_space(1))) const void gbl_void_t;
 __device__ __forceinline__ void g2lds(const void* g, void* l) {
   __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)l, 16, 0, 0);
 }
+// The same 16-byte direct-to-LDS load through a buffer descriptor: byte offset voff (per lane)
+// plus soff (scalar).
+__device__ __forceinline__ void buf2lds(__amdgpu_buffer_rsrc_t r, void* l, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)l, 16, voff, soff, 0, 0);
+}
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
 #define Q3_WAIT_VMCNT(N) \
   __builtin_amdgcn_s_waitcnt(((N) & 0xF) | (0x7 << 4) | (0xF << 8) | (((N) >> 4) << 14))
 
-template <int BN, int WM, int WN, int EPI, int OP, bool CVT, int NS>
+template <int BN, int WM, int WN, int EPI, int OP, bool CVT, int NS, bool BUF>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WM * WN, 64 * WM * WN),
                           amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4)))
 void gemm_d2l_kernel(const GemmParams p) {
@@ -409,6 +446,34 @@ void gemm_d2l_kernel(const GemmParams p) {
     const int row = slot >> 2;
     b_src[j] = b_row<BN, WN, EPI>(p, tn, row) + ((slot & 3) ^ swz4(row)) * 8;
   }
+  // BUF: the same loads through buffer descriptors. A load instruction covers 16 tile rows
+  // (one B segment: the host checks segment bounds are multiples of 16), so its descriptor is
+  // uniform; per-lane byte offsets are loop invariant and the K step goes into the scalar
+  // offset, which leaves no address arithmetic in the loop.
+  __amdgpu_buffer_rsrc_t rsrc_a, rsrc_b[BJ];
+  uint32_t voff_a[AJ], voff_b[BJ];
+  if constexpr (BUF) {
+    rsrc_a = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.A), static_cast<short>(0),
+                                               static_cast<int>(2 * static_cast<int64_t>(p.M) * p.lda), 0x00020000);
+#pragma unroll
+    for (int j = 0; j < AJ; ++j)
+      voff_a[j] = static_cast<uint32_t>(2 * (a_src[j] - p.A));
+#pragma unroll
+    for (int j = 0; j < BJ; ++j) {
+      const int blk = wave + j * WAVES;
+      const int row0 = blk * 64 < BSLOT ? blk * 16 : 0;  // first tile row of this load (uniform)
+      int slot = blk * 64 + lane;
+      if (slot >= BSLOT) slot = lane;
+      const int row = slot >> 2;
+      const uint16_t* base;
+      int idx0, rows;
+      b_seg<BN, WN, EPI>(p, tn, row0, base, idx0, rows);
+      rsrc_b[j] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), static_cast<short>(0),
+                                                    static_cast<int>(2 * static_cast<int64_t>(rows) * p.ldb), 0x00020000);
+      voff_b[j] = static_cast<uint32_t>(2 * ((static_cast<int64_t>(idx0) + (row - row0)) * p.ldb +
+                                             ((slot & 3) ^ swz4(row)) * 8));
+    }
+  }
 
   f32x16 acc[MI][NI];
 #pragma unroll
@@ -421,12 +486,23 @@ void gemm_d2l_kernel(const GemmParams p) {
   const int nk = p.K / kBK2;
   auto issue = [&](int st, int kt) {
     const int k0 = min(kt, nk - 1) * kBK2;  // past the end: reload the last tile (never used)
+    if constexpr (BUF) {
 #pragma unroll
-    for (int j = 0; j < AJ; ++j) g2lds(a_src[j] + k0, stA(st) + (wave + j * WAVES) * 64);
+      for (int j = 0; j < AJ; ++j)
+        buf2lds(rsrc_a, stA(st) + (wave + j * WAVES) * 64, voff_a[j], 2 * k0);
 #pragma unroll
-    for (int j = 0; j < BJ; ++j) {
-      const int blk = wave + j * WAVES;
-      g2lds(b_src[j] + k0, stB(st) + (blk * 64 < BSLOT ? blk : BSLOT / 64) * 64);
+      for (int j = 0; j < BJ; ++j) {
+        const int blk = wave + j * WAVES;
+        buf2lds(rsrc_b[j], stB(st) + (blk * 64 < BSLOT ? blk : BSLOT / 64) * 64, voff_b[j], 2 * k0);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < AJ; ++j) g2lds(a_src[j] + k0, stA(st) + (wave + j * WAVES) * 64);
+#pragma unroll
+      for (int j = 0; j < BJ; ++j) {
+        const int blk = wave + j * WAVES;
+        g2lds(b_src[j] + k0, stB(st) + (blk * 64 < BSLOT ? blk : BSLOT / 64) * 64);
+      }
     }
   };
   const int fr = lane & 31;
@@ -509,15 +585,24 @@ void gemm_d2l_kernel(const GemmParams p) {
   // its reads of stage kt-1), refill stage kt-1's buffer with step kt+NS-1, then the two
   // 16-wide sub-steps; the second one reads sub-step 0 of step kt+1, so the MFMAs after the
   // next barrier start on operands already in registers.
+  // With Q3_GEMM_SB the fragment reads of a sub-step are fenced off as one burst ahead of the
+  // MFMAs they overlap, instead of being interleaved (and waited for) among them.
+  auto fence = [&]() {
+    if (Q3_GEMM_SB) __builtin_amdgcn_sched_barrier(0);
+  };
   auto step = [&](int u, int kt) {
     wait_vm(std::integral_constant<int, (NS - 3) * LPS>{});
     convert_own((u + 1) % NS);
     barrier();
     issue((u + NS - 1) % NS, kt + NS - 1);
     fread(u, 1, 1);
+    fence();
     mfmas(0);
+    fence();
     fread((u + 1) % NS, 0, 0);
+    fence();
     mfmas(1);
+    fence();
   };
   // Whole groups of NS steps without any branch (stage indices are constants after unrolling),
   // then the remaining steps.
@@ -672,6 +757,19 @@ void gemm_pp_kernel(const GemmParams p) {
   gemm_epilogue<BN, WM, WN, EPI, OP>(p, acc, tm, tn, wm, wn, lane);
 }
 
+// Buffer-descriptor loads address A and each B segment with 32-bit byte offsets, and one load
+// instruction covers 16 consecutive B rows of a single segment. Q3_GEMM_ADDR64 (environment)
+// forces the 64-bit address path, so that it can be tested at small sizes.
+static bool gemm_buffer_ok(const GemmParams& p, int epi) {
+  if (!Q3_GEMM_BUF || std::getenv("Q3_GEMM_ADDR64") != nullptr) return false;
+  const int64_t lim = 0x7fffffff;
+  if (2 * static_cast<int64_t>(p.M) * p.lda > lim) return false;
+  if (epi == EPI_SWIGLU_16) return 2 * static_cast<int64_t>(p.N / 2) * p.ldb <= lim;
+  if (p.nseg0 % 16 != 0 || p.nseg1 % 16 != 0) return false;
+  const int64_t rows = std::max<int64_t>(p.nseg0, std::max<int64_t>(p.nseg1 - p.nseg0, p.N - p.nseg1));
+  return 2 * rows * p.ldb <= lim;
+}
+
 int gemm_pick_nb(int M, int N, int epi) {
   if (epi == EPI_SWIGLU_16) return 4;
   // Relative per-tile efficiency of the wider tiles (operand reuse), weighed against how
@@ -701,8 +799,12 @@ static hipError_t launch_t(const GemmParams& p, hipStream_t s) {
                          ? Q3_GEMM_STAGES : 4;
   if (Q3_GEMM_PP && BN == 256 && WM == 2 && WN == 4 && p.K % (kBK2 * kStages) == 0)
     gemm_pp_kernel<EPI, OP, CVT><<<tiles, 512, 0, s>>>(p);
-  else if (Q3_GEMM_D2L && p.K % kBK2 == 0)
-    gemm_d2l_kernel<BN, WM, WN, EPI, OP, CVT, NS><<<tiles, 64 * WM * WN, 0, s>>>(p);
+  else if (Q3_GEMM_D2L && p.K % kBK2 == 0) {
+    if (gemm_buffer_ok(p, EPI))
+      gemm_d2l_kernel<BN, WM, WN, EPI, OP, CVT, NS, true><<<tiles, 64 * WM * WN, 0, s>>>(p);
+    else
+      gemm_d2l_kernel<BN, WM, WN, EPI, OP, CVT, NS, false><<<tiles, 64 * WM * WN, 0, s>>>(p);
+  }
   else gemm_mfma_kernel<BN, WM, WN, EPI, OP, CVT><<<tiles, 64 * WM * WN, 0, s>>>(p);
   return hipGetLastError();
 }
