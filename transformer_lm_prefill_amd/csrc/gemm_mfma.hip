@@ -2,8 +2,8 @@
 // B [N, K] weights in torch nn.Linear layout, fp32 accumulation on the gfx950 32x32x16 MFMA.
 //
 // Operand formats: A and the MFMA run in one 16-bit format (fp16 or bf16). B is stored in
-// that format, or in bf16 while A is fp16: then each B chunk is converted to fp16 in
-// registers between its global load and its LDS store (exact for |w| in [2^-17, 65504]).
+// that format, or in bf16 while A is fp16: then B is converted to fp16 between LDS and the
+// MFMA (exact for |w| in [2^-17, 65504]).
 //
 // Uses (hf2q 0.1.1, qwen3vl_text/forward.rs, module doc; cortiq-engine 0.8.21, qwen3te.rs,
 // `encode_with_images`):
@@ -12,19 +12,22 @@
 //   gate/up  EPI_SWIGLU_16: a = silu(yn Wg^T) * (yn Wu^T), the two products in one tile
 //   down     EPI_STORE_F32 with the residual: y2 = y1 + a Wd^T
 //
-// Tiling for gfx950 (256 CUs in 8 XCDs, 160 KiB LDS per CU):
-//   workgroup tile 256 x BN (BN = 256, 192 or 128), K step 64, 8 waves (two per SIMD, so one
-//   wave's LDS and memory waits overlap the other's MFMAs), each wave a (256/WM) x (BN/WN)
-//   block of 32x32 MFMA tiles with fp32 accumulators;
-//   A and B tiles staged through a double-buffered LDS ring (global -> registers -> LDS): the
-//   next K step's global loads are issued before this step's MFMAs and stored to the other
-//   LDS buffer after them, one barrier per K step;
-//   MFMA operand fragments are read from LDS one 16-wide K sub-step ahead of the MFMAs that
-//   use them;
-//   16-byte LDS chunks XOR-swizzled by row, so the fragment reads (32 rows, one chunk each)
-//   and the tile stores are free of bank conflicts (rocprofv3 SQ_LDS_BANK_CONFLICT reads 0);
+// Main kernel (gemm_d2l_kernel), tiled for gfx950 (256 CUs in 8 XCDs, 160 KiB LDS per CU):
+//   workgroup tile 256 x BN (BN = 256, 192 or 128), 8 waves (two per SIMD, so one wave's LDS
+//   and memory waits overlap the other's MFMAs), each wave a (256/WM) x (BN/WN) block of
+//   32x32 MFMA tiles with fp32 accumulators;
+//   tiles go from global memory straight into LDS (direct-to-LDS buffer loads, no staging
+//   registers) through a 4-stage ring of 32-wide K steps, each requested three steps before
+//   its MFMAs, one barrier per step;
+//   MFMA operand fragments are read from LDS one 16-wide K sub-step ahead of their MFMAs;
+//   16-byte LDS chunks XOR-permuted by row, so the fragment reads are free of bank conflicts
+//   (rocprofv3 SQ_LDS_BANK_CONFLICT reads 0);
 //   workgroup ids remapped so each XCD (ids congruent mod 8) owns a compact band of tiles
-//   sharing A rows and B columns in its own L2.
+//   sharing A rows and B columns in its own L2;
+//   for fp32 outputs the accumulators hold C^T blocks, so the residual epilogue moves 16-byte
+//   runs of one row.
+// A register-staged kernel (gemm_mfma_kernel: K step 64, double-buffered LDS) serves K that
+// is not a multiple of 32.
 #include <algorithm>
 #include <cstdlib>
 #include <type_traits>
@@ -32,14 +35,8 @@
 #include "common.h"
 #include "kernels.h"
 
-#ifndef Q3_GEMM_SCHED
-#define Q3_GEMM_SCHED 0
-#endif
 #ifndef Q3_GEMM_D2L
 #define Q3_GEMM_D2L 1
-#endif
-#ifndef Q3_GEMM_PP
-#define Q3_GEMM_PP 0
 #endif
 // LDS ring depth of the direct-to-LDS kernel (stages of 32-wide K steps; tiles that would not
 // fit in 160 KiB use 4)
@@ -64,9 +61,6 @@
 // 1: direct-to-LDS loads through buffer descriptors where the operands fit 32-bit offsets
 #ifndef Q3_GEMM_BUF
 #define Q3_GEMM_BUF 1
-#endif
-#ifndef Q3_GEMM_SB
-#define Q3_GEMM_SB 0
 #endif
 #ifndef Q3_GEMM_TRANS
 #define Q3_GEMM_TRANS 1
@@ -364,7 +358,6 @@ void gemm_mfma_kernel(const GemmParams p) {
 // (4 chunks); the chunk a slot holds is XOR-permuted by row so that the 32-row fragment reads hit
 // distinct banks. bf16 weights feeding fp16 products are converted after the fragment read.
 constexpr int kBK2 = 32;
-constexpr int kStages = 4;
 
 __device__ __forceinline__ int swz4(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
 
@@ -585,24 +578,15 @@ void gemm_d2l_kernel(const GemmParams p) {
   // its reads of stage kt-1), refill stage kt-1's buffer with step kt+NS-1, then the two
   // 16-wide sub-steps; the second one reads sub-step 0 of step kt+1, so the MFMAs after the
   // next barrier start on operands already in registers.
-  // With Q3_GEMM_SB the fragment reads of a sub-step are fenced off as one burst ahead of the
-  // MFMAs they overlap, instead of being interleaved (and waited for) among them.
-  auto fence = [&]() {
-    if (Q3_GEMM_SB) __builtin_amdgcn_sched_barrier(0);
-  };
   auto step = [&](int u, int kt) {
     wait_vm(std::integral_constant<int, (NS - 3) * LPS>{});
     convert_own((u + 1) % NS);
     barrier();
     issue((u + NS - 1) % NS, kt + NS - 1);
     fread(u, 1, 1);
-    fence();
     mfmas(0);
-    fence();
     fread((u + 1) % NS, 0, 0);
-    fence();
     mfmas(1);
-    fence();
   };
   // Whole groups of NS steps without any branch (stage indices are constants after unrolling),
   // then the remaining steps.
@@ -618,143 +602,6 @@ void gemm_d2l_kernel(const GemmParams p) {
   // the trailing reloads of the last tile must land before this workgroup's LDS is released
   Q3_WAIT_VMCNT(0);
   gemm_epilogue<BN, WM, WN, EPI, OP, TRANS>(p, acc, tm, tn, wm, wn, lane);
-}
-
-// ---------------------------------------------------------------------------------------
-// Ping-pong variant of the direct-to-LDS kernel (256 x 256 tiles, 2 x 4 waves). Waves 0-3 and
-// 4-7 (one of each per SIMD) run one barrier apart: every K step of a wave is a memory phase
-// (wait for its own loads of the next stage, read all fragments of this step from LDS,
-// convert bf16 weights, issue the loads three stages ahead) followed, after a barrier, by an
-// MFMA phase. Group 1 starts one barrier late, so while one group's wave on a SIMD runs its
-// MFMAs the other group's wave on that SIMD does its memory work.
-template <int EPI, int OP, bool CVT>
-__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
-void gemm_pp_kernel(const GemmParams p) {
-  using F = Fmt<OP>;
-  constexpr int BN = 256, WM = 2, WN = 4;
-  constexpr int THREADS = 512, WAVES = 8;
-  constexpr int MI = kBM / WM / 32;            // 4
-  constexpr int NI = BN / WN / 32;             // 2
-  constexpr int ASLOT = kBM * 4, BSLOT = BN * 4;
-  constexpr int AJ = ASLOT / THREADS, BJ = BSLOT / THREADS;
-  constexpr int LPS = AJ + BJ;
-  __shared__ u32x4 sA0[ASLOT], sA1[ASLOT], sA2[ASLOT], sA3[ASLOT];
-  __shared__ u32x4 sB0[BSLOT], sB1[BSLOT], sB2[BSLOT], sB3[BSLOT];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave / WN;
-  const int wn = wave % WN;
-  const bool late = wm == 1;  // group 1 runs one barrier behind group 0
-  const int tiles_m = (p.M + kBM - 1) / kBM;
-  const int tiles_n = p.N / BN;
-  int tm, tn;
-  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
-
-  const uint16_t* a_src[AJ];
-#pragma unroll
-  for (int j = 0; j < AJ; ++j) {
-    const int slot = (wave + j * WAVES) * 64 + lane;
-    const int row = slot >> 2;
-    const int r = min(tm * kBM + row, p.M - 1);
-    a_src[j] = p.A + static_cast<int64_t>(r) * p.lda + ((slot & 3) ^ swz4(row)) * 8;
-  }
-  const uint16_t* b_src[BJ];
-#pragma unroll
-  for (int j = 0; j < BJ; ++j) {
-    const int slot = (wave + j * WAVES) * 64 + lane;
-    const int row = slot >> 2;
-    b_src[j] = b_row<BN, WN, EPI>(p, tn, row) + ((slot & 3) ^ swz4(row)) * 8;
-  }
-
-  f32x16 acc[MI][NI];
-#pragma unroll
-  for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.f;
-
-  const int nk = p.K / kBK2;
-  auto stage_a = [&](int st) -> u32x4* { return st == 0 ? sA0 : st == 1 ? sA1 : st == 2 ? sA2 : sA3; };
-  auto stage_b = [&](int st) -> u32x4* { return st == 0 ? sB0 : st == 1 ? sB1 : st == 2 ? sB2 : sB3; };
-  auto issue = [&](int st, int kt) {
-    const int k0 = min(kt, nk - 1) * kBK2;
-    u32x4* a = stage_a(st);
-    u32x4* b = stage_b(st);
-#pragma unroll
-    for (int j = 0; j < AJ; ++j) g2lds(a_src[j] + k0, a + (wave + j * WAVES) * 64);
-#pragma unroll
-    for (int j = 0; j < BJ; ++j) g2lds(b_src[j] + k0, b + (wave + j * WAVES) * 64);
-  };
-  const int fr = lane & 31;
-  const int fh = lane >> 5;
-  u32x4 fa[2][MI], fb[2][NI];
-  auto fread = [&](int st) {
-    const u32x4* a = stage_a(st);
-    const u32x4* b = stage_b(st);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int ch = ks * 2 + fh;
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
-        const int row = wm * (32 * MI) + mi * 32 + fr;
-        fa[ks][mi] = a[row * 4 + (ch ^ swz4(row))];
-      }
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni) {
-        const int row = wn * (32 * NI) + ni * 32 + fr;
-        fb[ks][ni] = b[row * 4 + (ch ^ swz4(row))];
-      }
-    }
-    if (CVT) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) fb[ks][ni][e] = bf16x2_to_f16x2(fb[ks][ni][e]);
-    }
-  };
-  auto barrier = [&]() {
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0x3F & 0xF) | ((0x3F >> 4) << 14));  // lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  issue(0, 0);
-  issue(1, 1);
-  issue(2, 2);
-  Q3_WAIT_VMCNT(LPS);  // own loads of stages 0 and 1 landed
-  barrier();           // stages 0 and 1 complete for every wave
-  if (late) barrier();
-
-  for (int kt = 0; kt < nk; kt += kStages) {
-#pragma unroll
-    for (int u = 0; u < kStages; ++u) {
-      // memory phase of step kt+u
-      Q3_WAIT_VMCNT(LPS);  // own loads of stage kt+u+1 landed (kt+u+2 may be in flight)
-      fread(u);
-      issue((u + 3) & 3, kt + u + 3);
-      barrier();
-      // MFMA phase
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-          for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = F::mfma(fa[ks][mi], fb[ks][ni], acc[mi][ni]);
-      barrier();
-    }
-  }
-  if (!late) barrier();
-
-  Q3_WAIT_VMCNT(0);
-  gemm_epilogue<BN, WM, WN, EPI, OP>(p, acc, tm, tn, wm, wn, lane);
 }
 
 // Buffer-descriptor loads address A and each B segment with 32-bit byte offsets, and one load
@@ -797,9 +644,7 @@ static hipError_t launch_t(const GemmParams& p, hipStream_t s) {
   const int tiles = ((p.M + kBM - 1) / kBM) * (p.N / BN);
   constexpr int NS = (Q3_GEMM_STAGES * (kBM + BN) * 64 + (BN % 128 ? 1024 : 0) <= 160 * 1024)
                          ? Q3_GEMM_STAGES : 4;
-  if (Q3_GEMM_PP && BN == 256 && WM == 2 && WN == 4 && p.K % (kBK2 * kStages) == 0)
-    gemm_pp_kernel<EPI, OP, CVT><<<tiles, 512, 0, s>>>(p);
-  else if (Q3_GEMM_D2L && p.K % kBK2 == 0) {
+  if (Q3_GEMM_D2L && p.K % kBK2 == 0) {
     if (gemm_buffer_ok(p, EPI))
       gemm_d2l_kernel<BN, WM, WN, EPI, OP, CVT, NS, true><<<tiles, 64 * WM * WN, 0, s>>>(p);
     else
