@@ -191,24 +191,25 @@ void attn_fwd_kernel(const AttnParams p) {
   const int kbase = qrow * kKRow + hi;
   const int vbase = qrow * kVRow + 2 * hi;
 
+  // P = exp2(S c - m), packed to 16 bits for the PV product; the row sum is taken over the
+  // packed values (one v_dot2 per pair), i.e. over exactly the P that multiplies V.
   auto exp_part = [&](f32x16 (&sp)[2]) {
     const float neg_m = -m_run;
-    float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float pe = fast_exp2(fmaf(sp[b][e], p.scale_log2, neg_m));
-        sp[b][e] = pe;
-        ls[e & 3] += pe;
-      }
-    l_part += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+      for (int e = 0; e < 16; ++e) sp[b][e] = fast_exp2(fmaf(sp[b][e], p.scale_log2, neg_m));
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int st16 = 0; st16 < 4; ++st16) {
       const int b = st16 >> 1, half = st16 & 1;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) pf[st16][e] = F::pack2(sp[b][half * 8 + 2 * e], sp[b][half * 8 + 2 * e + 1]);
+      for (int e = 0; e < 4; ++e) {
+        pf[st16][e] = F::pack2(sp[b][half * 8 + 2 * e], sp[b][half * 8 + 2 * e + 1]);
+        ls[e] = F::sum2(pf[st16][e], ls[e]);
+      }
     }
+    l_part += (ls[0] + ls[1]) + (ls[2] + ls[3]);
   };
   auto pv_all = [&](int tile) {
     const u32x2* vp = Vts[tile & 1] + vbase;

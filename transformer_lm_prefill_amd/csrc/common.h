@@ -73,6 +73,12 @@ struct Fmt<OP_BF16> {
   static __device__ __forceinline__ float to_f32(uint16_t h) { return bf2f(h); }
   static __device__ __forceinline__ uint16_t from_f32(float f) { return f2bf(f); }
   static __device__ __forceinline__ uint32_t pack2(float lo, float hi) { return pack2bf(lo, hi); }
+  // acc + lo + hi of a packed pair (one v_dot2 against (1, 1), fp32 accumulation)
+  static __device__ __forceinline__ float sum2(uint32_t w, float acc) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w),
+                                           __builtin_bit_cast(bf16x2_t, 0x3f803f80u), acc, false);
+  }
 };
 
 template <>
@@ -87,6 +93,12 @@ struct Fmt<OP_F16> {
     f32x2 v = {lo, hi};
     typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+  }
+  // acc + lo + hi of a packed pair (one v_dot2 against (1, 1), fp32 accumulation)
+  static __device__ __forceinline__ float sum2(uint32_t w, float acc) {
+    typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, w), __builtin_bit_cast(f16x2_t, 0x3c003c00u), acc,
+                                  false);
   }
 };
 
