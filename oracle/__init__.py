@@ -16,7 +16,8 @@ Sources (web pages, cited by title and item):
     causal attention loop and ``attention_gemm``, ``mrope_positions``,
     ``encode_with_images``.
   * hf2q 0.1.1, ``qwen3vl_text/forward.rs``: module doc (per-layer graph of
-    the peer reference), the DeepStack residual injection (Phase D).
+    the peer reference, final norm and LM head), the DeepStack residual
+    injection (Phase D), ``forward_text_prefill_logits_last`` (model.py).
   * inferencelayer 0.2.3, ``vision.rs``: ``mrope_positions`` (M-RoPE
     positions) and ``act_inplace`` (SiLU).
 
@@ -39,3 +40,4 @@ from .qwen3_layer import (  # noqa: F401
     stack_prefill,
     swiglu_ffn,
 )
+from .model import embed_tokens, lm_head_last, model_prefill_logits_last  # noqa: F401,E402

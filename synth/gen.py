@@ -123,3 +123,31 @@ def make_deepstack(cfg):
     slab = normal(cfg.seed, "deepstack", (len(rows), cfg.hidden), std=cfg.deepstack_std,
                   dtype=cfg.dtype)
     return rows, slab
+
+
+def make_model_weights(cfg, vocab, tied=False):
+    """Whole-model tensors besides the layers: token_embd [vocab, H] ~ N(0, 0.02),
+    output_norm [H] ~ 1 + N(0, 0.1) and lm_head [vocab, H] ~ N(0, 0.02) (None when the
+    embeddings are tied)."""
+    h = cfg.hidden
+    emb = normal(cfg.seed, "token_embd", (vocab, h), std=0.02, dtype=cfg.dtype)
+    norm = normal(cfg.seed, "output_norm", (h,), mean=1.0, std=0.1, dtype=cfg.dtype)
+    head = None if tied else normal(cfg.seed, "lm_head", (vocab, h), std=0.02, dtype=cfg.dtype)
+    return emb, norm, head
+
+
+def make_tokens(cfg, vocab, name="tokens"):
+    """[S] int32 token ids drawn uniformly from [0, vocab)."""
+    g = np.random.Generator(np.random.SFC64(np.random.SeedSequence([cfg.seed, _key(name), 0])))
+    return g.integers(0, vocab, size=cfg.seq_len, dtype=np.int64).astype(np.int32)
+
+
+def make_deepstack_layers(cfg, n_layers):
+    """One DeepStack slab per layer for the first `n_layers` layers, on the workload's
+    DeepStack rows: (rows, [slab_0, ...]); (None, None) when the workload has none."""
+    rows, _ = make_deepstack(cfg)
+    if rows is None:
+        return None, None
+    slabs = [normal(cfg.seed, f"deepstack.L{li}", (len(rows), cfg.hidden), std=cfg.deepstack_std,
+                    dtype=cfg.dtype) for li in range(n_layers)]
+    return rows, slabs

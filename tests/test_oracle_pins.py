@@ -385,6 +385,92 @@ def test_stack_feeds_each_layer_the_previous_output():
     assert np.array_equal(y, ref)
 
 
+# ---------------------------------------------------------------- whole-model prefill (f1)
+
+def _tiny_model(vocab=11, seed=60):
+    cfg = _tiny_cfg()
+    r = _rng(seed)
+    emb = 0.5 * r.standard_normal((vocab, cfg.hidden))
+    norm = 1 + 0.1 * r.standard_normal(cfg.hidden)
+    head = 0.5 * r.standard_normal((vocab, cfg.hidden))
+    return cfg, emb, norm, head
+
+
+def _brute_logits(h_last, norm, head, eps):
+    """RMSNorm and the LM head product written as loops."""
+    n = len(h_last)
+    ms = sum(v * v for v in h_last) / n
+    inv = 1.0 / math.sqrt(ms + eps)
+    y = [h_last[k] * inv * norm[k] for k in range(n)]
+    return [sum(y[k] * head[v][k] for k in range(n)) for v in range(len(head))]
+
+
+def test_embedding_lookup_is_one_hot_product_and_checks_ids():
+    _, emb, _, _ = _tiny_model()
+    tokens = np.array([3, 0, 10, 3, 7])
+    one_hot = np.eye(emb.shape[0])[tokens]
+    assert np.array_equal(oracle.embed_tokens(tokens, emb), one_hot @ emb)
+    with pytest.raises(ValueError):
+        oracle.embed_tokens(np.array([1, 11]), emb)
+    with pytest.raises(ValueError):
+        oracle.embed_tokens(np.array([-1]), emb)
+    with pytest.raises(ValueError):
+        oracle.embed_tokens(np.array([], dtype=np.int64), emb)
+
+
+def test_model_without_layers_is_norm_and_head_of_last_embedding():
+    cfg, emb, norm, head = _tiny_model()
+    tokens = np.array([4, 9, 2])
+    pos = oracle.mrope_positions(3, [])
+    got = oracle.model_prefill_logits_last(tokens, emb, [], norm, head, cfg, pos)
+    ref = _brute_logits(emb[2].tolist(), norm.tolist(), head.tolist(), cfg.eps)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_model_zero_projection_layers_carry_embedding_plus_deepstack_per_layer():
+    """With Wo = Wd = 0 every layer passes the residual through, so the last row is the
+    embedding plus the DeepStack slabs of the layers il < len(slabs) that reach it."""
+    cfg, emb, norm, head = _tiny_model()
+    layers = []
+    for li in range(3):
+        w = _tiny_weights(cfg, 61 + li)
+        w["wo"] = np.zeros_like(w["wo"]); w["w_down"] = np.zeros_like(w["w_down"])
+        layers.append(w)
+    tokens = np.array([1, 5, 8, 6])
+    pos = oracle.mrope_positions(4, [])
+    ds_rows = np.array([1, 3])
+    slabs = [_rng(70 + i).standard_normal((2, cfg.hidden)) for i in range(2)]
+    got = oracle.model_prefill_logits_last(tokens, emb, layers, norm, head, cfg, pos, ds_rows, slabs)
+    last = emb[6] + slabs[0][1] + slabs[1][1]    # row 3 = DeepStack row 1, layers 0 and 1 only
+    ref = _brute_logits(last.tolist(), norm.tolist(), head.tolist(), cfg.eps)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-13)
+    got1 = oracle.model_prefill_logits_last(tokens, emb, layers, norm, head, cfg, pos, ds_rows, slabs[:1])
+    ref1 = _brute_logits((emb[6] + slabs[0][1]).tolist(), norm.tolist(), head.tolist(), cfg.eps)
+    assert np.allclose(got1, ref1, rtol=1e-12, atol=1e-13)
+
+
+def test_model_tied_head_scale_and_vocab_permutation():
+    cfg, emb, norm, head = _tiny_model()
+    layers = [_tiny_weights(cfg, 80), _tiny_weights(cfg, 81)]
+    tokens = np.array([2, 7, 7, 0, 10])
+    pos = oracle.mrope_positions(5, [(1, 2, 2)])
+    base = oracle.model_prefill_logits_last(tokens, emb, layers, norm, head, cfg, pos)
+    # tied embeddings: the head is the embedding table itself
+    assert np.array_equal(oracle.model_prefill_logits_last(tokens, emb, layers, norm, None, cfg, pos),
+                          oracle.model_prefill_logits_last(tokens, emb, layers, norm, emb, cfg, pos))
+    # the final norm weight scales the logits linearly
+    scaled = oracle.model_prefill_logits_last(tokens, emb, layers, 3.0 * norm, head, cfg, pos)
+    assert np.allclose(scaled, 3.0 * base, rtol=1e-12, atol=1e-13)
+    # renumbering the vocabulary renumbers the logits
+    perm = _rng(82).permutation(emb.shape[0])
+    inv = np.argsort(perm)
+    got = oracle.model_prefill_logits_last(inv[tokens], emb[perm], layers, norm, head[perm], cfg, pos)
+    assert np.allclose(got, base[perm], rtol=1e-12, atol=1e-13)
+    # the last-row restriction of the final layer equals the full stack's last row
+    full = oracle.stack_prefill(oracle.embed_tokens(tokens, emb), layers, cfg, pos)
+    assert np.allclose(oracle.lm_head_last(full[-1], norm, head, cfg.eps), base, rtol=1e-12, atol=1e-13)
+
+
 # ---------------------------------------------------------------- generator
 
 def test_generator_deterministic_and_distributions():
@@ -400,6 +486,16 @@ def test_generator_deterministic_and_distributions():
     x = synth.make_x(cfg)
     assert abs(x.std() - 1.0) < 0.01
     assert not np.array_equal(synth.make_layer_weights(cfg, 1)["wq"], w1["wq"])
+
+
+def test_model_generators_deterministic():
+    cfg = synth.get_config("tiny_f32")
+    t1, t2 = synth.make_tokens(cfg, 1000), synth.make_tokens(cfg, 1000)
+    assert np.array_equal(t1, t2) and t1.dtype == np.int32 and t1.min() >= 0 and t1.max() < 1000
+    e1, n1, h1 = synth.make_model_weights(cfg, 50)
+    e2, _, h2 = synth.make_model_weights(cfg, 50, tied=True)
+    assert np.array_equal(e1, e2) and h2 is None and h1.shape == e1.shape == (50, cfg.hidden)
+    assert not np.array_equal(e1, h1)
 
 
 def test_bf16_rounding_ties_to_even():
