@@ -31,6 +31,9 @@ def parse():
     ap.add_argument("--config", default="qwen3vl_8b_stack4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
+    ap.add_argument("--no-model", action="store_true",
+                    help="skip the whole-model (embedding + stack + LM head) measurement")
+    ap.add_argument("--vocab", type=int, default=151936)
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (the reference "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -82,6 +85,54 @@ def cpu_baseline(cfg, w0, x, pos, n_tok):
     return {"value": n_tok / dt, "unit": "tokens/s/layer", "cores": cores, "kind": "oracle",
             "sample": f"layer 1 of the stack on its first {n_tok} tokens (float64 numpy oracle, "
                       f"{dt:.1f} s)"}
+
+
+def model_prefill_extra(cfg, layers, pos, stream, vocab):
+    """The whole-model path on the same layers: embedding lookup, the layer stack, final
+    RMSNorm and an untied LM head over `vocab` rows, for the last position's logits. Weights of
+    the embedding table and head are seeded random (torch generator) of the layer dtype."""
+    import torch
+
+    import transformer_lm_prefill_amd as q3
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(1234)
+    wdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    emb = (torch.randn(vocab, cfg.hidden, device=dev, generator=g) * 0.02).to(wdt)
+    head = (torch.randn(vocab, cfg.hidden, device=dev, generator=g) * 0.02).to(wdt)
+    norm = (1 + 0.1 * torch.randn(cfg.hidden, device=dev, generator=g)).to(wdt)
+    tokens = torch.randint(0, vocab, (cfg.seq_len,), generator=torch.Generator().manual_seed(5)).tolist()
+    spec = q3.LayerSpec.of(cfg)
+    ws = torch.empty(q3.model_workspace_bytes(spec, len(layers), vocab, cfg.seq_len), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty(vocab, dtype=torch.float32, device=dev)
+
+    def run():
+        q3.model_prefill_logits_last(spec, layers, emb, norm, head, tokens, pos, out=out, workspace=ws)
+
+    run()
+    torch.cuda.synchronize()
+    n = 3
+    t = time.perf_counter()
+    for _ in range(n):
+        run()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t) * 1e3 / n
+    q3.timing_enable(True)
+    run()
+    torch.cuda.synchronize()
+    kt = q3.timing_collect()
+    q3.timing_enable(False)
+    head_ms = kt["lm_head"][1] / kt["lm_head"][0]
+    head_bytes = vocab * cfg.hidden * (2 if wdt == torch.bfloat16 else 4)
+    emb_ms = kt["embed_gather"][1] / kt["embed_gather"][0]
+    return {"workload": f"{cfg.name}: {len(layers)} layers, seq {cfg.seq_len}, vocab {vocab} untied head",
+            "ms": round(ms, 4), "tokens_per_s": round(cfg.seq_len / (ms * 1e-3), 1),
+            "lm_head": {"avg_ms": round(head_ms, 4), "bound": "hbm",
+                        "GB_per_s": round(head_bytes / (head_ms * 1e-3) / 1e9, 1),
+                        "frac_of_hbm_peak": round(head_bytes / (head_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+            "embed_gather_ms": round(emb_ms, 4),
+            "finite_logits": bool(torch.isfinite(out).all().item())}
 
 
 def main():
@@ -180,6 +231,8 @@ def main():
 
     kernels = {k: {"launches": v[0], "avg_ms": round(v[1] / v[0], 4)} for k, v in kt.items()}
 
+    model = None if args.no_model else model_prefill_extra(cfg, layers, pos, stream, args.vocab)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, host_layers[0], x_host, pos_host, args.cpu_sample_tokens)
@@ -210,6 +263,7 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "model_prefill_logits_last": model,
     }
     print(json.dumps(out))
 

@@ -195,6 +195,48 @@ typedef struct {
 int qwen3_timing_enable(int enable);
 int qwen3_timing_collect(qwen3_kernel_time *out, int32_t max_entries, int32_t *n_out);
 
+/* ---- Whole-model text prefill: last position's logits --------------------------------------
+ *
+ * hf2q 0.1.1, qwen3vl_text/forward.rs: the module doc (per-layer graph; "Final": output RMSNorm,
+ * then the LM head, which is the token embedding table when the embeddings are tied) and
+ * `forward_text_prefill_logits_last` (embedding lookup, the layers in order with DeepStack slab
+ * il added after layer il for il < n_deepstack_layers, final RMSNorm and LM head on the last
+ * position only; an empty prompt and out-of-range token ids are errors).
+ */
+typedef struct {
+  qwen3_layer_cfg layer;        /* shared by every decoder layer                                */
+  int32_t n_layers;             /* >= 0                                                         */
+  int32_t vocab;                /* rows of the embedding table and of the LM head, >= 1         */
+  int32_t n_deepstack_layers;   /* layers 0 .. n-1 receive DeepStack slab il; 0 <= n <= n_layers */
+} qwen3_model_cfg;
+
+typedef struct {
+  const void* token_embd;              /* device [vocab, hidden], layer.wdtype                  */
+  const qwen3_layer_weights* layers;   /* HOST array of n_layers entries (device pointers)      */
+  const void* output_norm;             /* device [hidden], layer.wdtype                         */
+  const void* lm_head;                 /* device [vocab, hidden], layer.wdtype; NULL = tied      */
+} qwen3_model_weights;
+
+/* Workspace for qwen3_model_prefill_logits_last: the token ids, the fp32 residual stream
+ * [S, hidden], the last row's normalized state and one layer's workspace. 0 for invalid input. */
+size_t qwen3_model_workspace_bytes(const qwen3_model_cfg* cfg, int32_t seq_len);
+
+/* logits[v] for v < vocab: the LM head applied to RMSNorm(output_norm) of the last position's
+ * hidden state after all layers.
+ *   tokens     HOST array [seq_len] of ids in [0, vocab), checked on the host before anything is
+ *              enqueued and copied into the workspace during the call.
+ *   positions  device [3][seq_len] int32 (t, h, w rows), as for qwen3_layer_prefill.
+ *   ds_rows, n_ds  device DeepStack rows shared by the first n_deepstack_layers layers (rules as
+ *              for qwen3_layer_prefill); ds is a HOST array of n_deepstack_layers device slabs
+ *              [n_ds, hidden] (layer.wdtype), or NULL when n_ds == 0.
+ *   logits     device [vocab] fp32, written.
+ * Every layer uses the same workspace region in turn; the residual stream stays in fp32. */
+int qwen3_model_prefill_logits_last(const qwen3_model_cfg* cfg, const qwen3_model_weights* w,
+                                    const int32_t* tokens, int32_t seq_len, const int32_t* positions,
+                                    const int32_t* ds_rows, int32_t n_ds, const void* const* ds,
+                                    float* logits, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -165,6 +165,51 @@ def test_sub_op_argument_checks(lib):
     assert lib.rms_norm_rows(FAKE, FAKE, FAKE, 0, 256, 1e-6, 1, 1, None) == 1
 
 
+def _model_cfg(n_layers=2, vocab=100, n_ds_layers=0, **kw):
+    m = L.ModelCfg()
+    m.layer = _cfg(**kw)
+    m.n_layers, m.vocab, m.n_deepstack_layers = n_layers, vocab, n_ds_layers
+    return m
+
+
+def _call_model(lib, m, tokens, ws_bytes=None, n_ds=0, ds_rows=None, slabs=None):
+    s = len(tokens)
+    if ws_bytes is None:
+        ws_bytes = lib.qwen3_model_workspace_bytes(ctypes.byref(m), max(s, 1))
+    lw = (L.LayerWeights * max(m.n_layers, 1))(*([_weights()] * max(m.n_layers, 1)))
+    mw = L.ModelWeights(FAKE, lw, FAKE, None)
+    tok = (ctypes.c_int32 * max(s, 1))(*tokens)
+    return lib.qwen3_model_prefill_logits_last(ctypes.byref(m), ctypes.byref(mw), tok, s, FAKE, ds_rows,
+                                               n_ds, slabs, FAKE, ctypes.c_void_p(0x100000), ws_bytes, None)
+
+
+def test_model_workspace_formula(lib):
+    m = _model_cfg(n_layers=4, vocab=1000, hidden=4096, n_heads=32, n_kv_heads=8, ffn=12288)
+    s = 300
+    layer = lib.qwen3_layer_workspace_bytes(ctypes.byref(m.layer), s)
+    def a256(b):
+        return (b + 255) // 256 * 256
+    assert lib.qwen3_model_workspace_bytes(ctypes.byref(m), s) == a256(4 * s) + a256(4 * s * 4096) + a256(4 * 4096) + layer
+    assert lib.qwen3_model_workspace_bytes(ctypes.byref(m), 0) == 0
+    assert lib.qwen3_model_workspace_bytes(None, 16) == 0
+
+
+def test_model_argument_checks(lib):
+    m = _model_cfg()
+    assert _call_model(lib, m, [1, 100, 3]) == 1
+    assert "outside [0, vocab = 100)" in lib.qwen3_last_error().decode()
+    assert _call_model(lib, m, [-1]) == 1
+    assert _call_model(lib, m, []) == 1 and "empty" in lib.qwen3_last_error().decode()
+    assert _call_model(lib, _model_cfg(n_layers=2, n_ds_layers=3), [1, 2]) == 1
+    assert "n_deepstack_layers" in lib.qwen3_last_error().decode()
+    assert _call_model(lib, _model_cfg(vocab=0), [0]) == 1
+    assert _call_model(lib, _model_cfg(n_layers=-1), [0]) == 1
+    assert _call_model(lib, _model_cfg(n_ds_layers=1), [1, 2], n_ds=1, ds_rows=None) == 1
+    m2 = _model_cfg()
+    need = lib.qwen3_model_workspace_bytes(ctypes.byref(m2), 3)
+    assert _call_model(lib, m2, [1, 2, 3], ws_bytes=need - 1) == 3
+
+
 def test_timing_collect_empty(lib):
     n = ctypes.c_int32(-1)
     assert lib.qwen3_timing_collect(None, 0, ctypes.byref(n)) == 0 and n.value == 0

@@ -1,4 +1,5 @@
-"""MI355X (gfx950) prefill of one Qwen3/Qwen3-VL text decoder layer.
+"""MI355X (gfx950) prefill of Qwen3/Qwen3-VL text decoder layers (and of the whole text model
+to its last position's logits).
 
 The computation runs in libqwen3_prefill.so (hand-written HIP kernels behind a C ABI, see
 include/qwen3_prefill.h). This package is the thin Python binding: it passes torch device
@@ -11,6 +12,8 @@ from .ops import (  # noqa: F401
     gqa_causal_attention,
     layer_prefill,
     layer_workspace_bytes,
+    model_prefill_logits_last,
+    model_workspace_bytes,
     qk_norm_mrope,
     rms_norm_rows,
     swiglu_ffn,

@@ -14,6 +14,7 @@ STATUS = {0: "QWEN3_OK", 1: "QWEN3_ERR_INVALID_ARG", 2: "QWEN3_ERR_UNSUPPORTED",
 # Every symbol the header declares.
 EXPORTS = ("qwen3_layer_workspace_bytes", "qwen3_layer_prefill", "qk_norm_mrope",
            "gqa_causal_attention", "swiglu_ffn", "swiglu_ffn_workspace_bytes", "rms_norm_rows",
+           "qwen3_model_workspace_bytes", "qwen3_model_prefill_logits_last",
            "qwen3_last_error", "qwen3_timing_enable", "qwen3_timing_collect")
 
 
@@ -29,6 +30,16 @@ class LayerCfg(ctypes.Structure):
 class LayerWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("attn_norm", "wq", "wk", "wv", "q_norm", "k_norm",
                                                "wo", "ffn_norm", "w_gate", "w_up", "w_down")]
+
+
+class ModelCfg(ctypes.Structure):
+    _fields_ = [("layer", LayerCfg), ("n_layers", ctypes.c_int32), ("vocab", ctypes.c_int32),
+                ("n_deepstack_layers", ctypes.c_int32)]
+
+
+class ModelWeights(ctypes.Structure):
+    _fields_ = [("token_embd", ctypes.c_void_p), ("layers", ctypes.POINTER(LayerWeights)),
+                ("output_norm", ctypes.c_void_p), ("lm_head", ctypes.c_void_p)]
 
 
 class KernelTime(ctypes.Structure):
@@ -72,6 +83,12 @@ def load():
     lib.swiglu_ffn_workspace_bytes.restype = sz
     lib.rms_norm_rows.argtypes = [vp, vp, vp, i32, i32, f32, ctypes.c_int, ctypes.c_int, vp]
     lib.rms_norm_rows.restype = ctypes.c_int
+    lib.qwen3_model_workspace_bytes.argtypes = [ctypes.POINTER(ModelCfg), i32]
+    lib.qwen3_model_workspace_bytes.restype = sz
+    lib.qwen3_model_prefill_logits_last.argtypes = [ctypes.POINTER(ModelCfg), ctypes.POINTER(ModelWeights),
+                                                    ctypes.POINTER(i32), i32, vp, vp, i32,
+                                                    ctypes.POINTER(vp), vp, vp, sz, vp]
+    lib.qwen3_model_prefill_logits_last.restype = ctypes.c_int
     lib.qwen3_last_error.argtypes = []
     lib.qwen3_last_error.restype = ctypes.c_char_p
     lib.qwen3_timing_enable.argtypes = [ctypes.c_int]

@@ -352,6 +352,97 @@ int qwen3_layer_prefill(const qwen3_layer_cfg* cfg, const qwen3_layer_weights* w
   return QWEN3_OK;
 }
 
+// ---- whole-model prefill to the last position's logits --------------------------------------
+struct ModelWorkspace {
+  size_t tokens, x, xlast, layer, total;
+};
+
+static ModelWorkspace model_layout(const qwen3_model_cfg* c, int32_t S) {
+  ModelWorkspace m{};
+  const int H = c->layer.hidden;
+  m.tokens = 0;
+  m.x = align256(static_cast<size_t>(S) * 4);
+  m.xlast = m.x + align256(static_cast<size_t>(S) * H * 4);
+  m.layer = m.xlast + align256(static_cast<size_t>(H) * 4);
+  m.total = m.layer + qwen3_layer_workspace_bytes(&c->layer, S);
+  return m;
+}
+
+size_t qwen3_model_workspace_bytes(const qwen3_model_cfg* cfg, int32_t seq_len) {
+  if (!cfg || seq_len < 1 || qwen3_layer_workspace_bytes(&cfg->layer, seq_len) == 0) return 0;
+  return model_layout(cfg, seq_len).total;
+}
+
+int qwen3_model_prefill_logits_last(const qwen3_model_cfg* cfg, const qwen3_model_weights* w,
+                                    const int32_t* tokens, int32_t seq_len, const int32_t* positions,
+                                    const int32_t* ds_rows, int32_t n_ds, const void* const* ds, float* logits,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (!cfg) return fail(QWEN3_ERR_INVALID_ARG, "cfg is NULL");
+  int st = check_cfg(&cfg->layer);
+  if (st) return st;
+  if (cfg->n_layers < 0) return fail(QWEN3_ERR_INVALID_ARG, "n_layers (%d) must be >= 0", cfg->n_layers);
+  if (cfg->vocab < 1) return fail(QWEN3_ERR_INVALID_ARG, "vocab (%d) must be >= 1", cfg->vocab);
+  if (cfg->n_deepstack_layers < 0 || cfg->n_deepstack_layers > cfg->n_layers)
+    return fail(QWEN3_ERR_INVALID_ARG, "n_deepstack_layers (%d) must be in [0, n_layers = %d]",
+                cfg->n_deepstack_layers, cfg->n_layers);
+  if (seq_len < 1) return fail(QWEN3_ERR_INVALID_ARG, "seq_len must be >= 1 (got %d): empty prompt", seq_len);
+  if (!tokens) return fail(QWEN3_ERR_INVALID_ARG, "tokens is NULL");
+  if (!w || !w->token_embd || !w->output_norm || (cfg->n_layers > 0 && !w->layers))
+    return fail(QWEN3_ERR_INVALID_ARG, "model weights (token_embd, output_norm, layers) must not be NULL");
+  if (!positions || !logits) return fail(QWEN3_ERR_INVALID_ARG, "positions / logits is NULL");
+  if (misaligned16({w->token_embd, w->output_norm, w->lm_head, logits}))
+    return fail(QWEN3_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  const int nds = cfg->n_deepstack_layers;
+  if (n_ds < 0 || n_ds > seq_len)
+    return fail(QWEN3_ERR_INVALID_ARG, "n_ds (%d) must be in [0, seq_len = %d]", n_ds, seq_len);
+  if (n_ds > 0 && nds > 0) {
+    if (!ds_rows || !ds) return fail(QWEN3_ERR_INVALID_ARG, "n_ds = %d needs ds_rows and the slab array", n_ds);
+    for (int l = 0; l < nds; ++l)
+      if (!ds[l]) return fail(QWEN3_ERR_INVALID_ARG, "DeepStack slab %d is NULL", l);
+  }
+  for (int32_t i = 0; i < seq_len; ++i)
+    if (tokens[i] < 0 || tokens[i] >= cfg->vocab)
+      return fail(QWEN3_ERR_INVALID_ARG, "token id %d at position %d is outside [0, vocab = %d)", tokens[i], i,
+                  cfg->vocab);
+  const ModelWorkspace L = model_layout(cfg, seq_len);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(QWEN3_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", L.total, workspace_bytes,
+                workspace ? "" : ", NULL pointer");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(QWEN3_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int S = seq_len, H = cfg->layer.hidden;
+  const qwen3_dtype wdt = cfg->layer.wdtype;
+  char* ws = static_cast<char*>(workspace);
+  int32_t* tok = reinterpret_cast<int32_t*>(ws + L.tokens);
+  float* x = reinterpret_cast<float*>(ws + L.x);
+  float* xlast = reinterpret_cast<float*>(ws + L.xlast);
+  hipError_t e = hipMemcpyAsync(tok, tokens, static_cast<size_t>(S) * 4, hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return hip_fail(e, "token upload");
+  {
+    KTimer t("embed_gather", s);
+    e = q3::launch_embed_gather(tok, w->token_embd, wdt, x, S, H, s);
+    if (e != hipSuccess) return hip_fail(e, "embed_gather launch");
+  }
+  const size_t lbytes = L.total - L.layer;
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    const bool with_ds = l < nds && n_ds > 0;
+    st = qwen3_layer_prefill(&cfg->layer, &w->layers[l], x, x, S, positions, with_ds ? ds_rows : nullptr,
+                             with_ds ? n_ds : 0, with_ds ? ds[l] : nullptr, ws + L.layer, lbytes, stream);
+    if (st) return st;
+  }
+  if ((st = run_rmsnorm(x + static_cast<size_t>(S - 1) * H, w->output_norm, wdt, xlast, QWEN3_F32, 1, H,
+                        cfg->layer.rms_eps, s)))
+    return st;
+  {
+    KTimer t("lm_head", s);
+    e = q3::launch_gemv_rows(w->lm_head ? w->lm_head : w->token_embd, wdt, xlast, logits, cfg->vocab, H, s);
+    if (e != hipSuccess) return hip_fail(e, "lm_head launch");
+  }
+  return QWEN3_OK;
+}
+
 int qk_norm_mrope(void* q, void* k, int32_t seq_len, int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
                   const void* q_norm, const void* k_norm, float eps, const int32_t* positions, float theta,
                   const int32_t mrope_section[3], qwen3_dtype dtype, qwen3_dtype norm_dtype, void* stream) {

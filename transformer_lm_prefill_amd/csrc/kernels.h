@@ -22,6 +22,13 @@ hipError_t launch_rmsnorm(const float* x, const void* w, int w_dt, void* y, int 
 hipError_t launch_deepstack_add(float* y, const int32_t* rows, const void* ds, int ds_dt, int n,
                                 int S, int hidden, hipStream_t s);
 
+// ---- whole-model steps around the layers (model_head.hip) ---------------------------------
+// x[s, :] = table[tokens[s], :] as fp32 (tokens are device int32, already in range).
+hipError_t launch_embed_gather(const int32_t* tokens, const void* table, int dt, float* x, int S, int hidden,
+                               hipStream_t s);
+// y[r] = sum_k W[r, k] x[k], W [rows, hidden] of dt, x and y fp32 (hidden % 8 == 0).
+hipError_t launch_gemv_rows(const void* W, int dt, const float* x, float* y, int rows, int hidden, hipStream_t s);
+
 // ---- per-head RMSNorm + interleaved MRoPE, in place ---------------------------------------
 struct RopeParams {
   void* q;            // token t, head h at q + t*q_stride + h*hd

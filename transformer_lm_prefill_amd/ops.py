@@ -112,6 +112,54 @@ def layer_prefill(spec, weights, x, positions, ds_rows=None, ds=None, out=None, 
     return out
 
 
+def _model_cfg(spec, n_layers, vocab, n_deepstack_layers):
+    m = _lib.ModelCfg()
+    m.layer = _cfg(spec)
+    m.n_layers, m.vocab, m.n_deepstack_layers = int(n_layers), int(vocab), int(n_deepstack_layers)
+    return m
+
+
+def model_workspace_bytes(spec, n_layers, vocab, seq_len, n_deepstack_layers=0):
+    m = _model_cfg(spec, n_layers, vocab, n_deepstack_layers)
+    return int(_lib.load().qwen3_model_workspace_bytes(ctypes.byref(m), int(seq_len)))
+
+
+def model_prefill_logits_last(spec, layers, token_embd, output_norm, lm_head, tokens, positions,
+                              ds_rows=None, ds=None, out=None, workspace=None):
+    """qwen3_model_prefill_logits_last: logits [vocab] float32 of the last prompt position.
+
+    layers: list of weight mappings (one per decoder layer); token_embd [vocab, H],
+    output_norm [H], lm_head [vocab, H] or None (tied) on the GPU in spec's dtype; tokens: a
+    host sequence of int token ids; positions [3, S] int32 on the GPU; ds_rows [n] int32 and ds
+    a list of [n, H] slabs (one per DeepStack layer, the first len(ds) layers) or None.
+    """
+    lib = _lib.load()
+    vocab = int(token_embd.shape[0])
+    n_dsl = 0 if ds is None else len(ds)
+    m = _model_cfg(spec, len(layers), vocab, n_dsl)
+    tok = (ctypes.c_int32 * len(tokens))(*[int(t) for t in tokens])
+    s = len(tokens)
+    if out is None:
+        out = torch.empty(vocab, dtype=torch.float32, device=token_embd.device)
+    need = int(lib.qwen3_model_workspace_bytes(ctypes.byref(m), int(s)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=token_embd.device)
+    lw = (_lib.LayerWeights * max(len(layers), 1))()
+    for i, w in enumerate(layers):
+        lw[i] = _lib.LayerWeights(*[_ptr(w[n]) for n in WEIGHT_NAMES])
+    mw = _lib.ModelWeights(_ptr(token_embd), lw if layers else None, _ptr(output_norm), _ptr(lm_head))
+    slabs = None
+    if ds is not None:
+        slabs = (ctypes.c_void_p * len(ds))(*[t.data_ptr() if t is not None else None for t in ds])
+        for t in ds:
+            _ptr(t)  # device and contiguity checks
+    n_ds = 0 if ds_rows is None else int(ds_rows.numel())
+    _lib.check(lib.qwen3_model_prefill_logits_last(
+        ctypes.byref(m), ctypes.byref(mw), tok, int(s), _ptr(positions), _ptr(ds_rows), n_ds, slabs,
+        _ptr(out), _ptr(workspace), int(workspace.numel()), _stream()))
+    return out
+
+
 def qk_norm_mrope(q, k, q_norm, k_norm, positions, eps, theta, sections):
     """In place on q [S, nh, hd] and k [S, nkv, hd]; returns (q, k)."""
     lib = _lib.load()
