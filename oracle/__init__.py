@@ -19,7 +19,10 @@ Sources (web pages, cited by title and item):
     the peer reference, final norm and LM head), the DeepStack residual
     injection (Phase D), ``forward_text_prefill_logits_last`` (model.py).
   * inferencelayer 0.2.3, ``vision.rs``: ``mrope_positions`` (M-RoPE
-    positions) and ``act_inplace`` (SiLU).
+    positions), ``act_inplace`` (SiLU), ``rope_tables_2d`` and the vision block's
+    ``attention`` (vision.py).
+  * cortiq-engine 0.8.51, ``onevision2.rs``: three-axis vision rope tables, the
+    adjacent-lane rotation and bidirectional ``attend`` (vision.py).
 
 Parity pins: every function here is pinned by the ``-m "not gpu"`` tests
 against closed forms, invariants, textbook formulations and brute force; no
@@ -41,3 +44,11 @@ from .qwen3_layer import (  # noqa: F401
     swiglu_ffn,
 )
 from .model import embed_tokens, lm_head_last, model_prefill_logits_last  # noqa: F401,E402
+from .vision import (  # noqa: F401,E402
+    bidirectional_attention,
+    merge_block_positions,
+    rope_adjacent,
+    rope_split_half,
+    rope_tables_2d,
+    rope_tables_3axis,
+)

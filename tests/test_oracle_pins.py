@@ -471,6 +471,108 @@ def test_model_tied_head_scale_and_vocab_permutation():
     assert np.allclose(oracle.lm_head_last(full[-1], norm, head, cfg.eps), base, rtol=1e-12, atol=1e-13)
 
 
+# ---------------------------------------------------------------- vision rope + bidirectional attention (f2)
+
+def test_merge_block_order_matches_hand_example():
+    got = oracle.merge_block_positions(1, 4, 4, 2)
+    assert np.array_equal(got.reshape(-1), _golden_ints("vision_merge_blocks_1x4x4_m2.txt"))
+    two = oracle.merge_block_positions(2, 2, 4, 2)
+    assert np.array_equal(two[:8, 1:], got[:8, 1:]) and np.array_equal(two[8:, 1:], got[:8, 1:])
+    assert np.array_equal(two[:, 0], [0] * 8 + [1] * 8)
+
+
+def test_rope_tables_2d_structure():
+    hd, theta = 32, 10000.0
+    half, nf = hd // 2, hd // 4
+    c0, s0 = oracle.rope_tables_2d((1, 1, 1), hd, theta, 1)
+    assert np.array_equal(c0, np.ones((1, hd))) and np.array_equal(s0, np.zeros((1, hd)))
+    cos, sin = oracle.rope_tables_2d((1, 4, 6), hd, theta, 2)
+    pos = oracle.merge_block_positions(1, 4, 6, 2)
+    assert np.array_equal(cos[:, :half], cos[:, half:]) and np.array_equal(sin[:, :half], sin[:, half:])
+    # frequency 0 is 1: slot 0 rotates by the row, slot nf by the column
+    assert np.allclose(np.arctan2(sin[:, 0], cos[:, 0]), pos[:, 1], atol=1e-14)
+    assert np.allclose(cos[:, nf], np.cos(pos[:, 2]), atol=1e-15) and np.allclose(sin[:, nf], np.sin(pos[:, 2]), atol=1e-15)
+    # slot i of a patch in row 1 turns by theta^(-2i/half)
+    k = int(np.nonzero((pos[:, 1] == 1) & (pos[:, 2] == 0))[0][0])
+    for i in range(nf):
+        assert abs(np.arctan2(sin[k, i], cos[k, i]) - theta ** (-2.0 * i / half)) < 1e-14
+        assert abs(sin[k, nf + i]) == 0.0
+
+
+def test_rope_tables_3axis_structure():
+    hd, theta = 64, 10000.0
+    half = hd // 2
+    nt, nh, nw = 8, 12, 12        # 4:6:6 of the 32 angles
+    cos, sin = oracle.rope_tables_3axis((2, 4, 4), hd, theta, 2)
+    pos = oracle.merge_block_positions(2, 4, 4, 2)
+    assert np.array_equal(cos[:, :half], cos[:, half:])
+    for slot, axis in ((0, 0), (nt, 1), (nt + nh, 2)):
+        assert np.allclose(np.arctan2(sin[:, slot], cos[:, slot]), pos[:, axis], atol=1e-14)
+    k = int(np.nonzero((pos[:, 0] == 1) & (pos[:, 1] == 1) & (pos[:, 2] == 1))[0][0])
+    ang = np.arctan2(sin[k, :half], cos[k, :half])
+    for n, lo in ((nt, 0), (nh, nt), (nw, nt + nh)):
+        assert np.allclose(ang[lo:lo + n], theta ** (-np.arange(n) / n), atol=1e-14)
+    assert nt + nh + nw == half
+
+
+def test_rope_split_half_is_textbook_rotation():
+    r = _rng(90)
+    n, heads, hd = 5, 3, 16
+    x = r.standard_normal((n, heads, hd))
+    phi = r.uniform(-3, 3, (n, hd // 2))
+    cos = np.cos(np.concatenate([phi, phi], axis=1)); sin = np.sin(np.concatenate([phi, phi], axis=1))
+    y = oracle.rope_split_half(x, cos, sin)
+    z = (x[..., :hd // 2] + 1j * x[..., hd // 2:]) * np.exp(1j * phi)[:, None, :]
+    assert np.allclose(y[..., :hd // 2], z.real, atol=1e-14) and np.allclose(y[..., hd // 2:], z.imag, atol=1e-14)
+
+
+def test_rope_adjacent_lanes():
+    r = _rng(91)
+    n, heads, hd = 4, 2, 8
+    x = r.standard_normal((n, heads, hd))
+    # equal angles on each pair: a rotation of (x_2i, x_2i+1)
+    phi = r.uniform(-3, 3, (n, hd // 2))
+    ang = np.repeat(phi, 2, axis=1)
+    y = oracle.rope_adjacent(x, np.cos(ang), np.sin(ang))
+    z = (x[..., 0::2] + 1j * x[..., 1::2]) * np.exp(1j * phi)[:, None, :]
+    assert np.allclose(y[..., 0::2], z.real, atol=1e-14) and np.allclose(y[..., 1::2], z.imag, atol=1e-14)
+    # different angles on the two lanes of a pair: lane 1 of e_0 takes the sine of its own angle
+    e0 = np.zeros((1, 1, 4)); e0[0, 0, 0] = 1.0
+    a = np.array([[0.3, 1.1, 0.0, 0.0]])
+    y0 = oracle.rope_adjacent(e0, np.cos(a), np.sin(a))[0, 0]
+    assert np.allclose(y0, [math.cos(0.3), math.sin(1.1), 0.0, 0.0], atol=1e-15)
+
+
+def _brute_attention_full(q, k, v):
+    s, nh, hd = q.shape
+    group = nh // k.shape[1]
+    out = np.zeros_like(q)
+    for h in range(nh):
+        g = h // group
+        for i in range(s):
+            z = [sum(q[i, h, e] * k[j, g, e] for e in range(hd)) / math.sqrt(hd) for j in range(s)]
+            m = max(z)
+            p = [math.exp(t - m) for t in z]
+            tot = sum(p)
+            for e in range(hd):
+                out[i, h, e] = sum(p[j] * v[j, g, e] for j in range(s)) / tot
+    return out
+
+
+def test_bidirectional_attention_pins():
+    r = _rng(92)
+    s, nh, nkv, hd = 6, 4, 2, 4
+    q, k, v = r.standard_normal((s, nh, hd)), r.standard_normal((s, nkv, hd)), r.standard_normal((s, nkv, hd))
+    o = oracle.bidirectional_attention(q, k, v)
+    assert np.allclose(o, _brute_attention_full(q, k, v), rtol=1e-12, atol=1e-13)
+    perm = r.permutation(s)
+    assert np.allclose(oracle.bidirectional_attention(q[perm], k[perm], v[perm]), o[perm], rtol=1e-12, atol=1e-13)
+    # the last query sees every key, as in causal attention
+    assert np.allclose(o[-1], oracle.causal_gqa_attention(q, k, v)[-1], rtol=1e-12, atol=1e-13)
+    assert np.allclose(o, oracle.bidirectional_attention(q, np.repeat(k, 2, axis=1), np.repeat(v, 2, axis=1)),
+                       rtol=1e-12, atol=1e-13)
+
+
 # ---------------------------------------------------------------- generator
 
 def test_generator_deterministic_and_distributions():
