@@ -150,13 +150,46 @@ int qk_norm_mrope(void *q, void *k, int32_t seq_len, int32_t n_heads, int32_t n_
 /* Causal grouped-query attention (cortiq-engine qwen3te.rs, per-pair loop / `attention_gemm`):
  *   out[s, h] = sum_{j<=s} softmax_j(scale * q[s,h] . k[j,g]) v[j,g],  g = h / (nh / nkv).
  *   q, out [S, n_heads, head_dim]; k, v [S, n_kv_heads, head_dim]; all `dtype`, contiguous.
- *   scale is normally 1/sqrt(head_dim). bf16 / f16: head_dim 128, nh/nkv in {1,2,4,8}, 16-bit
- *   products with fp32 accumulation and fp32 online softmax. f32: head_dim 64 or 128, fp32
- *   throughout.
+ *   scale is normally 1/sqrt(head_dim). head_dim 64 or 128. bf16 / f16: nh/nkv in {1,2,4,8},
+ *   16-bit products with fp32 accumulation and fp32 online softmax. f32: fp32 throughout.
  *   out must not overlap q, k or v. */
 int gqa_causal_attention(const void *q, const void *k, const void *v, void *out,
                          int32_t seq_len, int32_t n_heads, int32_t n_kv_heads,
                          int32_t head_dim, float scale, qwen3_dtype dtype, void *stream);
+
+/* Bidirectional (non-causal) attention of a vision-tower block (inferencelayer 0.2.3 vision.rs,
+ * the block's `attention`; cortiq-engine 0.8.51 onevision2.rs, `attend`): as
+ * gqa_causal_attention with every key visible to every query,
+ *   out[s, h] = sum_{j<S} softmax_j(scale * q[s,h] . k[j,g]) v[j,g].
+ *   Same layouts, types, limits and errors. */
+int gqa_bidirectional_attention(const void *q, const void *k, const void *v, void *out,
+                                int32_t seq_len, int32_t n_heads, int32_t n_kv_heads,
+                                int32_t head_dim, float scale, qwen3_dtype dtype, void *stream);
+
+/* Rotary tables of a vision-tower patch grid (frames x grid_h x grid_w patches, merge x merge
+ * merge blocks): cos_out, sin_out device fp32 [frames*grid_h*grid_w, head_dim], patches in
+ * merge-block order (frames in order; within a frame the blocks row-major, each block's patches
+ * row-major), entries j and j + head_dim/2 equal.
+ *   layout 0 (inferencelayer 0.2.3 vision.rs, `rope_tables_2d`): with half = head_dim/2 and
+ *     nf = half/2, angle j < nf = row * theta^(-2j/half), angle nf + j = col * theta^(-2j/half);
+ *     head_dim a multiple of 4.
+ *   layout 1 (cortiq-engine 0.8.51 onevision2.rs, `rope_tables`): the half angles split 4:6:6
+ *     between frame, row and column (unit = half/16), an axis with n slots turning by
+ *     theta^(-i/n); head_dim a multiple of 32.
+ * Angles are formed in fp64. grid_h and grid_w must be multiples of merge. */
+int vision_rope_tables(int32_t frames, int32_t grid_h, int32_t grid_w, int32_t merge, int32_t head_dim,
+                       float theta, int32_t layout, float *cos_out, float *sin_out, void *stream);
+
+/* Applies rotary tables in place to x [n, heads, head_dim] of `dtype` (row r of head h at
+ * x + r*row_stride + h*head_dim), cos_tab / sin_tab fp32 [n, head_dim], fp32 arithmetic:
+ *   pairing 0 (inferencelayer vision.rs, the block's `attention`): rotate_half on split halves,
+ *     y_i = x_i c_i - x_{i+half} s_i, y_{i+half} = x_{i+half} c_{i+half} + x_i s_{i+half};
+ *   pairing 1 (onevision2.rs, `split_rope`): adjacent lanes,
+ *     y_2i = x_2i c_2i - x_2i+1 s_2i, y_2i+1 = x_2i+1 c_2i+1 + x_2i s_2i+1 (each lane takes its
+ *     own table entry, so the two lanes of a pair turn by different angles). */
+int apply_rope_tables(void *x, int32_t n, int32_t heads, int32_t head_dim, int64_t row_stride,
+                      const float *cos_tab, const float *sin_tab, int32_t pairing, qwen3_dtype dtype,
+                      void *stream);
 
 /* SwiGLU feed-forward with optional residual (cortiq-engine qwen3te.rs, gate/up/act/down):
  *   out = [residual +] (silu(x W_gate^T) * (x W_up^T)) W_down^T,  silu(z) = z / (1 + e^-z).

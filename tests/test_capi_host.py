@@ -81,7 +81,7 @@ def test_workspace_size_formula(lib):
 @pytest.mark.parametrize("kw,status,needle", [
     (dict(n_heads=12, n_kv_heads=8), 1, "multiple of n_kv_heads"),
     (dict(n_heads=32, n_kv_heads=2), 2, "1, 2, 4 or 8"),
-    (dict(head_dim=64, sections=(12, 10, 10)), 2, "head_dim must be 128"),
+    (dict(head_dim=96, sections=(16, 16, 16)), 2, "head_dim must be 64 or 128"),
     (dict(wdtype=0, act_dtype=2), 2, "supported pairs"),
     (dict(wdtype=2, act_dtype=1), 2, "supported pairs"),
     (dict(act_dtype=9), 1, "qwen3_dtype"),
@@ -156,7 +156,14 @@ def test_sub_op_argument_checks(lib):
     assert lib.qk_norm_mrope(FAKE, FAKE, 4, 4, 2, 128, FAKE, FAKE, 1e-6, FAKE, 5e6, sec, 1, 5, None) == 1
     assert lib.gqa_causal_attention(FAKE, FAKE, FAKE, FAKE, 8, 6, 4, 128, 0.1, 1, None) == 1
     assert lib.gqa_causal_attention(FAKE, FAKE, FAKE, FAKE, 8, 4, 2, 128, 0.0, 1, None) == 1
-    assert lib.gqa_causal_attention(FAKE, FAKE, FAKE, FAKE, 8, 4, 2, 64, 0.1, 1, None) == 2
+    assert lib.gqa_causal_attention(FAKE, FAKE, FAKE, FAKE, 8, 4, 2, 96, 0.1, 1, None) == 2
+    assert lib.gqa_bidirectional_attention(FAKE, FAKE, FAKE, FAKE, 8, 6, 4, 128, 0.1, 1, None) == 1
+    assert lib.gqa_bidirectional_attention(FAKE, FAKE, FAKE, FAKE, 0, 4, 2, 128, 0.1, 1, None) == 1
+    assert lib.vision_rope_tables(1, 4, 6, 4, 64, 1e4, 0, FAKE, FAKE, None) == 1      # 6 % merge
+    assert lib.vision_rope_tables(1, 4, 4, 2, 48, 1e4, 1, FAKE, FAKE, None) == 1      # 3-axis needs hd % 32
+    assert lib.vision_rope_tables(1, 4, 4, 2, 64, 1e4, 2, FAKE, FAKE, None) == 1      # layout
+    assert lib.apply_rope_tables(FAKE, 4, 2, 64, 100, FAKE, FAKE, 0, 1, None) == 1    # stride < heads*hd
+    assert lib.apply_rope_tables(FAKE, 4, 2, 64, 128, FAKE, FAKE, 3, 1, None) == 1    # pairing
     assert lib.swiglu_ffn(FAKE, FAKE, FAKE, FAKE, None, FAKE, 8, 2048, 6144, 1, 2, 0, FAKE, 10, None) == 3
     assert lib.swiglu_ffn(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 2048, 6144, 1, 2, 2, FAKE, 1 << 30, None) == 2
     assert lib.swiglu_ffn(FAKE, FAKE, FAKE, FAKE, None, FAKE, 8, 2048, 6144, 1, 2, 1, FAKE, 1 << 30, None) == 2

@@ -9,6 +9,8 @@ pointers and the current HIP stream to the library and does no arithmetic of its
 from .ops import (  # noqa: F401
     LayerSpec,
     Qwen3Error,
+    apply_rope_tables,
+    gqa_bidirectional_attention,
     gqa_causal_attention,
     layer_prefill,
     layer_workspace_bytes,
@@ -19,4 +21,5 @@ from .ops import (  # noqa: F401
     swiglu_ffn,
     timing_collect,
     timing_enable,
+    vision_rope_tables,
 )

@@ -13,7 +13,8 @@ STATUS = {0: "QWEN3_OK", 1: "QWEN3_ERR_INVALID_ARG", 2: "QWEN3_ERR_UNSUPPORTED",
 
 # Every symbol the header declares.
 EXPORTS = ("qwen3_layer_workspace_bytes", "qwen3_layer_prefill", "qk_norm_mrope",
-           "gqa_causal_attention", "swiglu_ffn", "swiglu_ffn_workspace_bytes", "rms_norm_rows",
+           "gqa_causal_attention", "gqa_bidirectional_attention", "vision_rope_tables",
+           "apply_rope_tables", "swiglu_ffn", "swiglu_ffn_workspace_bytes", "rms_norm_rows",
            "qwen3_model_workspace_bytes", "qwen3_model_prefill_logits_last",
            "qwen3_last_error", "qwen3_timing_enable", "qwen3_timing_collect")
 
@@ -76,6 +77,12 @@ def load():
     lib.qk_norm_mrope.restype = ctypes.c_int
     lib.gqa_causal_attention.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, f32, ctypes.c_int, vp]
     lib.gqa_causal_attention.restype = ctypes.c_int
+    lib.gqa_bidirectional_attention.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, f32, ctypes.c_int, vp]
+    lib.gqa_bidirectional_attention.restype = ctypes.c_int
+    lib.vision_rope_tables.argtypes = [i32, i32, i32, i32, i32, f32, i32, vp, vp, vp]
+    lib.vision_rope_tables.restype = ctypes.c_int
+    lib.apply_rope_tables.argtypes = [vp, i32, i32, i32, ctypes.c_int64, vp, vp, i32, ctypes.c_int, vp]
+    lib.apply_rope_tables.restype = ctypes.c_int
     lib.swiglu_ffn.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_int, ctypes.c_int,
                                ctypes.c_int, vp, sz, vp]
     lib.swiglu_ffn.restype = ctypes.c_int

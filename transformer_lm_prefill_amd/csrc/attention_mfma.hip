@@ -55,12 +55,10 @@
 
 namespace q3 {
 
-constexpr int kHD = 128;
 constexpr int kKT = 64;    // keys per tile
 constexpr int kAttnWaves = 8;
 constexpr int kAttnThreads = 64 * kAttnWaves;
-constexpr int kKRow = 17;  // u32x4 per padded K row
-constexpr int kVRow = 18;  // u32x2 per padded V^T row
+constexpr int kVRow = 18;  // u32x2 per padded V^T row (16 granules of 4 keys + 2 pad)
 
 // position of 4-key granule gi (0..15 within the tile) in a V^T row: 4h+2x+s -> 4h+2s+x
 __device__ __forceinline__ int vt_pos(int gi) {
@@ -74,14 +72,19 @@ __device__ __forceinline__ float max_halves(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-template <int G, int OP, bool BUF>
+template <int G, int OP, bool BUF, int HD>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(const AttnParams p) {
   using F = Fmt<OP>;
   constexpr int NB = 8 / G;
   constexpr int TOK = 32 * NB;
-  __shared__ __attribute__((aligned(16))) u32x4 Ks[2][kKT * kKRow];
-  __shared__ __attribute__((aligned(16))) u32x2 Vts[2][kHD * kVRow];
+  constexpr int NKS = HD / 16;     // 16-wide K steps of the S^T product
+  constexpr int ND = HD / 32;      // 32-row blocks of O^T
+  constexpr int NCH = HD / 8;      // 16-byte chunks per K / V row
+  constexpr int KROW = NCH + 1;    // u32x4 per padded K row
+  constexpr int KPT = kKT * NCH / 256;  // K chunks staged per K-loader thread
+  __shared__ __attribute__((aligned(16))) u32x4 Ks[2][kKT * KROW];
+  __shared__ __attribute__((aligned(16))) u32x2 Vts[2][HD * kVRow];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -95,24 +98,26 @@ void attn_fwd_kernel(const AttnParams p) {
   const int bt = wave % NB, hl = wave / NB;
   const int hq = g * G + hl;
   const int my_t = t0 + 32 * bt + qrow;
-  const int lim = min(my_t, p.S - 1);
-  const int ntiles = (min(p.S, t0 + TOK) + kKT - 1) / kKT;
+  // causal: keys up to the row's own token; bidirectional: every key of the sequence
+  const bool causal = p.causal != 0;
+  const int lim = causal ? min(my_t, p.S - 1) : p.S - 1;
+  const int ntiles = ((causal ? min(p.S, t0 + TOK) : p.S) + kKT - 1) / kKT;
 
-  u32x4 qf[8];
+  u32x4 qf[NKS];
   {
     const bool ok = my_t < p.S;
-    const uint16_t* qp = p.q + static_cast<int64_t>(ok ? my_t : 0) * p.q_stride + hq * kHD + 8 * hi;
+    const uint16_t* qp = p.q + static_cast<int64_t>(ok ? my_t : 0) * p.q_stride + hq * HD + 8 * hi;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
+    for (int ks = 0; ks < NKS; ++ks) {
       u32x4 v = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
       if (!ok) v = u32x4{0, 0, 0, 0};
       qf[ks] = v;
     }
   }
 
-  f32x16 o[4];
+  f32x16 o[ND];
 #pragma unroll
-  for (int d = 0; d < 4; ++d)
+  for (int d = 0; d < ND; ++d)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[d][e] = 0.f;
   f32x16 sa[2], sb[2];
@@ -124,22 +129,25 @@ void attn_fwd_kernel(const AttnParams p) {
   const bool k_loader = wave < 4;  // wave-uniform (the buffer descriptor depends on it)
   const int tv = tid & 255;
   const int vg = tv & 15, vc = tv >> 4;
+  const bool v_active = vc < NCH;  // with HD = 64 waves 6 and 7 stage nothing (wave-uniform)
   const int vpos = vt_pos(vg);
   u32x4 st[4];
+  static_assert(KPT <= 4, "head_dim");
   // K / V rows come in through buffer loads when the operand's byte extent fits the 32-bit
   // range (BUF): a per-thread byte offset within the tile plus the tile's row offset in a
   // scalar register, rows at or past S reading as zeros through the range check (those keys
   // are masked), so the loop carries no 64-bit address arithmetic. Otherwise through 64-bit
   // addresses with the row index clamped to S - 1.
   const int64_t row_elems = k_loader ? p.k_stride : p.v_stride;
-  const uint16_t* gbase = (k_loader ? p.k : p.v) + g * kHD;
+  const uint16_t* gbase = (k_loader ? p.k : p.v) + g * HD;
   int trow[4], tcol[4];  // row within the tile and element column of this thread's chunks
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int c = tv + 256 * i;
-    trow[i] = k_loader ? c >> 4 : 4 * vg + i;
-    tcol[i] = k_loader ? (c & 15) * 8 : vc * 8;
+    trow[i] = k_loader ? c / NCH : 4 * vg + i;
+    tcol[i] = k_loader ? (c % NCH) * 8 : (v_active ? vc : 0) * 8;
   }
+  const int nst = k_loader ? KPT : (v_active ? 4 : 0);  // this thread's staged chunks (uniform per wave)
   const int row_bytes = static_cast<int>(2 * row_elems);  // used only when BUF
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(gbase), static_cast<short>(0), p.S * row_bytes, 0x00020000);
@@ -151,14 +159,18 @@ void attn_fwd_kernel(const AttnParams p) {
       const int soff = tile * kKT * row_bytes;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff[i], soff, 0);
-        st[i] = u32x4{v[0], v[1], v[2], v[3]};
+        if (i < nst) {
+          const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff[i], soff, 0);
+          st[i] = u32x4{v[0], v[1], v[2], v[3]};
+        }
       }
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int row = min(tile * kKT + trow[i], p.S - 1);
-        st[i] = *reinterpret_cast<const u32x4*>(gbase + row * row_elems + tcol[i]);
+        if (i < nst) {
+          const int row = min(tile * kKT + trow[i], p.S - 1);
+          st[i] = *reinterpret_cast<const u32x4*>(gbase + row * row_elems + tcol[i]);
+        }
       }
     }
   };
@@ -166,11 +178,11 @@ void attn_fwd_kernel(const AttnParams p) {
     if (k_loader) {
       u32x4* dst = Ks[tile & 1];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < KPT; ++i) {
         const int c = tv + 256 * i;
-        dst[(c >> 4) * kKRow + (c & 15)] = st[i];
+        dst[(c / NCH) * KROW + (c % NCH)] = st[i];
       }
-    } else {
+    } else if (v_active) {
       u32x2* dst = Vts[tile & 1];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -188,7 +200,7 @@ void attn_fwd_kernel(const AttnParams p) {
     asm volatile("" ::: "memory");
   };
 
-  const int kbase = qrow * kKRow + hi;
+  const int kbase = qrow * KROW + hi;
   const int vbase = qrow * kVRow + 2 * hi;
 
   // P = exp2(S c - m), packed to 16 bits for the PV product; the row sum is taken over the
@@ -214,8 +226,8 @@ void attn_fwd_kernel(const AttnParams p) {
   auto pv_all = [&](int tile) {
     const u32x2* vp = Vts[tile & 1] + vbase;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int st16 = i >> 2, d = i & 3, b = st16 >> 1, half = st16 & 1;
+    for (int i = 0; i < 4 * ND; ++i) {
+      const int st16 = i / ND, d = i % ND, b = st16 >> 1, half = st16 & 1;
       const u32x4 vv = *reinterpret_cast<const u32x4*>(vp + d * 32 * kVRow + 8 * b + 4 * half);
       o[d] = F::mfma(vv, pf[st16], o[d]);
     }
@@ -238,9 +250,9 @@ void attn_fwd_kernel(const AttnParams p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) sc[b][e] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
+    for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-      for (int b = 0; b < 2; ++b) sc[b] = F::mfma(kp[b * 32 * kKRow + 2 * ks], qf[ks], sc[b]);
+      for (int b = 0; b < 2; ++b) sc[b] = F::mfma(kp[b * 32 * KROW + 2 * ks], qf[ks], sc[b]);
     if (!FIRST) {
       exp_part(sp);
       // anchor P^T here, so that the exponentials are scheduled among the S^T MFMAs above
@@ -248,8 +260,8 @@ void attn_fwd_kernel(const AttnParams p) {
 #pragma unroll
       for (int st16 = 0; st16 < 4; ++st16) asm volatile("" ::"v"(pf[st16]));
     }
-    // causal mask on diagonal / tail tiles (wave-uniform branch)
-    if (kb + kKT - 1 > t0 + 32 * bt || kb + kKT > p.S) {
+    // mask on diagonal (causal) and tail tiles (wave-uniform branch)
+    if ((causal && kb + kKT - 1 > t0 + 32 * bt) || kb + kKT > p.S) {
       asm volatile("");
 #pragma unroll
       for (int b = 0; b < 2; ++b)
@@ -273,7 +285,7 @@ void attn_fwd_kernel(const AttnParams p) {
       const float alpha = fast_exp2(m_run - m_new);
       l_part *= alpha;
 #pragma unroll
-      for (int d = 0; d < 4; ++d)
+      for (int d = 0; d < ND; ++d)
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
       m_run = m_new;
@@ -314,9 +326,9 @@ void attn_fwd_kernel(const AttnParams p) {
   const float l_run = l_part + __shfl_xor(l_part, 32);
   if (my_t < p.S) {
     const float inv = 1.0f / l_run;
-    uint16_t* op = p.o + static_cast<int64_t>(my_t) * p.o_stride + hq * kHD;
+    uint16_t* op = p.o + static_cast<int64_t>(my_t) * p.o_stride + hq * HD;
 #pragma unroll
-    for (int d = 0; d < 4; ++d)
+    for (int d = 0; d < ND; ++d)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int hd0 = d * 32 + 8 * q4 + 4 * hi;
@@ -328,7 +340,7 @@ void attn_fwd_kernel(const AttnParams p) {
   }
 }
 
-template <int G, int OP>
+template <int G, int OP, int HD>
 static hipError_t launch_g(const AttnParams& p, hipStream_t s) {
   constexpr int TOK = 32 * kAttnWaves / G;
   const int nblk = (p.S + TOK - 1) / TOK;
@@ -338,19 +350,19 @@ static hipError_t launch_g(const AttnParams& p, hipStream_t s) {
   const int64_t extent =
       2 * (static_cast<int64_t>(p.S) + kKT) * (p.k_stride > p.v_stride ? p.k_stride : p.v_stride);
   if (extent <= 0x7fffffff && std::getenv("Q3_ATTN_ADDR64") == nullptr)
-    attn_fwd_kernel<G, OP, true><<<nblk * p.nkv, kAttnThreads, 0, s>>>(p);
+    attn_fwd_kernel<G, OP, true, HD><<<nblk * p.nkv, kAttnThreads, 0, s>>>(p);
   else
-    attn_fwd_kernel<G, OP, false><<<nblk * p.nkv, kAttnThreads, 0, s>>>(p);
+    attn_fwd_kernel<G, OP, false, HD><<<nblk * p.nkv, kAttnThreads, 0, s>>>(p);
   return hipGetLastError();
 }
 
-template <int OP>
+template <int OP, int HD>
 static hipError_t launch_op(const AttnParams& p, hipStream_t s) {
   switch (p.nh / p.nkv) {
-    case 1: return launch_g<1, OP>(p, s);
-    case 2: return launch_g<2, OP>(p, s);
-    case 4: return launch_g<4, OP>(p, s);
-    case 8: return launch_g<8, OP>(p, s);
+    case 1: return launch_g<1, OP, HD>(p, s);
+    case 2: return launch_g<2, OP, HD>(p, s);
+    case 4: return launch_g<4, OP, HD>(p, s);
+    case 8: return launch_g<8, OP, HD>(p, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -358,8 +370,13 @@ static hipError_t launch_op(const AttnParams& p, hipStream_t s) {
 hipError_t launch_attention_mfma(const AttnParams& p, int op, hipStream_t s) {
   if (p.S <= 0) return hipSuccess;
   if (p.nkv <= 0 || p.nh % p.nkv != 0) return hipErrorInvalidValue;
-  if (op == OP_BF16) return launch_op<OP_BF16>(p, s);
-  if (op == OP_F16) return launch_op<OP_F16>(p, s);
+  if (p.head_dim == 128) {
+    if (op == OP_BF16) return launch_op<OP_BF16, 128>(p, s);
+    if (op == OP_F16) return launch_op<OP_F16, 128>(p, s);
+  } else if (p.head_dim == 64) {
+    if (op == OP_BF16) return launch_op<OP_BF16, 64>(p, s);
+    if (op == OP_F16) return launch_op<OP_F16, 64>(p, s);
+  }
   return hipErrorInvalidValue;
 }
 

@@ -109,7 +109,7 @@ int check_heads(int32_t nh, int32_t nkv, int32_t hd, qwen3_dtype dt) {
     return fail(QWEN3_ERR_INVALID_ARG, "n_heads (%d) must be a multiple of n_kv_heads (%d)", nh, nkv);
   if (dt != QWEN3_F32) {
     const int g = nh / nkv;
-    if (hd != 128) return fail(QWEN3_ERR_UNSUPPORTED, "%s head_dim must be 128 (got %d)", dname, hd);
+    if (hd != 64 && hd != 128) return fail(QWEN3_ERR_UNSUPPORTED, "%s head_dim must be 64 or 128 (got %d)", dname, hd);
     if (g != 1 && g != 2 && g != 4 && g != 8)
       return fail(QWEN3_ERR_UNSUPPORTED, "%s n_heads / n_kv_heads must be 1, 2, 4 or 8 (got %d)", dname, g);
   } else {
@@ -186,18 +186,18 @@ int run_qk_norm_mrope(const q3::RopeParams& p, int hd, qwen3_dtype dt, hipStream
 
 int run_attention(const void* q, const void* k, const void* v, void* o, int64_t qs, int64_t ks,
                   int64_t vs, int64_t os, int S, int nh, int nkv, int hd, float scale, qwen3_dtype dt,
-                  hipStream_t s) {
-  KTimer t("attention", s);
+                  int causal, hipStream_t s) {
+  KTimer t(causal ? "attention" : "attention_bidirectional", s);
   hipError_t e;
   if (dt != QWEN3_F32) {
     q3::AttnParams p{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), qs, ks, vs, os,
-                     S, nh, nkv, scale * 1.4426950408889634f};
+                     S, nh, nkv, scale * 1.4426950408889634f, hd, causal};
     e = q3::launch_attention_mfma(p, dt == QWEN3_F16 ? q3::OPH_F16 : q3::OPH_BF16, s);
   } else {
     q3::AttnF32Params p{static_cast<const float*>(q), static_cast<const float*>(k),
                         static_cast<const float*>(v), static_cast<float*>(o), qs, ks, vs, os,
-                        S, nh, nkv, scale};
+                        S, nh, nkv, scale, causal};
     e = q3::launch_attention_f32(p, hd, s);
   }
   return e == hipSuccess ? QWEN3_OK : hip_fail(e, "attention launch");
@@ -332,7 +332,7 @@ int qwen3_layer_prefill(const qwen3_layer_cfg* cfg, const qwen3_layer_weights* w
   // a5: causal GQA attention -> o [S, q_dim]
   if ((st = run_attention(qkv, qkv + static_cast<size_t>(q_dim) * e, qkv + static_cast<size_t>(q_dim + kv_dim) * e,
                           o, qkv_dim, qkv_dim, qkv_dim, q_dim, S, nh, nkv, hd,
-                          1.0f / std::sqrt(static_cast<float>(hd)), dt, s)))
+                          1.0f / std::sqrt(static_cast<float>(hd)), dt, 1, s)))
     return st;
   // a6: y1 = x + o Wo^T (fp32, into x_out)
   {
@@ -465,9 +465,9 @@ int qk_norm_mrope(void* q, void* k, int32_t seq_len, int32_t n_heads, int32_t n_
   return run_qk_norm_mrope(p, head_dim, dtype, static_cast<hipStream_t>(stream));
 }
 
-int gqa_causal_attention(const void* q, const void* k, const void* v, void* out, int32_t seq_len,
-                         int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, float scale,
-                         qwen3_dtype dtype, void* stream) {
+static int attention_entry(const void* q, const void* k, const void* v, void* out, int32_t seq_len,
+                           int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, float scale, qwen3_dtype dtype,
+                           int causal, void* stream) {
   if (!valid_dtype(dtype)) return fail(QWEN3_ERR_INVALID_ARG, "dtype %d is not a qwen3_dtype", dtype);
   if (seq_len < 1) return fail(QWEN3_ERR_INVALID_ARG, "seq_len must be >= 1 (got %d)", seq_len);
   int st = check_heads(n_heads, n_kv_heads, head_dim, dtype);
@@ -478,7 +478,62 @@ int gqa_causal_attention(const void* q, const void* k, const void* v, void* out,
   return run_attention(q, k, v, out, static_cast<int64_t>(n_heads) * head_dim,
                        static_cast<int64_t>(n_kv_heads) * head_dim, static_cast<int64_t>(n_kv_heads) * head_dim,
                        static_cast<int64_t>(n_heads) * head_dim, seq_len, n_heads, n_kv_heads, head_dim, scale,
-                       dtype, static_cast<hipStream_t>(stream));
+                       dtype, causal, static_cast<hipStream_t>(stream));
+}
+
+int gqa_causal_attention(const void* q, const void* k, const void* v, void* out, int32_t seq_len,
+                         int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, float scale,
+                         qwen3_dtype dtype, void* stream) {
+  return attention_entry(q, k, v, out, seq_len, n_heads, n_kv_heads, head_dim, scale, dtype, 1, stream);
+}
+
+int gqa_bidirectional_attention(const void* q, const void* k, const void* v, void* out, int32_t seq_len,
+                                int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, float scale,
+                                qwen3_dtype dtype, void* stream) {
+  return attention_entry(q, k, v, out, seq_len, n_heads, n_kv_heads, head_dim, scale, dtype, 0, stream);
+}
+
+int vision_rope_tables(int32_t frames, int32_t grid_h, int32_t grid_w, int32_t merge, int32_t head_dim,
+                       float theta, int32_t layout, float* cos_out, float* sin_out, void* stream) {
+  if (frames < 1 || grid_h < 1 || grid_w < 1 || merge < 1)
+    return fail(QWEN3_ERR_INVALID_ARG, "grid (%d, %d, %d) and merge (%d) must be >= 1", frames, grid_h, grid_w,
+                merge);
+  if (grid_h % merge != 0 || grid_w % merge != 0)
+    return fail(QWEN3_ERR_INVALID_ARG, "grid_h (%d) and grid_w (%d) must be multiples of merge (%d)", grid_h,
+                grid_w, merge);
+  if (layout != 0 && layout != 1) return fail(QWEN3_ERR_INVALID_ARG, "layout must be 0 (2-D) or 1 (3-axis)");
+  if (head_dim < 4 || head_dim % (layout == 0 ? 4 : 32) != 0)
+    return fail(QWEN3_ERR_INVALID_ARG, "head_dim (%d) must be a positive multiple of %d for layout %d", head_dim,
+                layout == 0 ? 4 : 32, layout);
+  if (!(theta > 1.f) || !std::isfinite(theta)) return fail(QWEN3_ERR_INVALID_ARG, "theta must be finite and > 1");
+  if (!cos_out || !sin_out) return fail(QWEN3_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (misaligned16({cos_out, sin_out})) return fail(QWEN3_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  if (static_cast<int64_t>(frames) * grid_h * grid_w > 0x7fffffff / head_dim)
+    return fail(QWEN3_ERR_UNSUPPORTED, "grid too large");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  KTimer t("vision_rope_tables", s);
+  const hipError_t e = q3::launch_vision_rope_tables(layout, frames, grid_h, grid_w, merge, head_dim,
+                                                     std::log2(static_cast<double>(theta)), cos_out, sin_out, s);
+  return e == hipSuccess ? QWEN3_OK : hip_fail(e, "vision_rope_tables launch");
+}
+
+int apply_rope_tables(void* x, int32_t n, int32_t heads, int32_t head_dim, int64_t row_stride,
+                      const float* cos_tab, const float* sin_tab, int32_t pairing, qwen3_dtype dtype,
+                      void* stream) {
+  if (!valid_dtype(dtype)) return fail(QWEN3_ERR_INVALID_ARG, "dtype %d is not a qwen3_dtype", dtype);
+  if (n < 1 || heads < 1) return fail(QWEN3_ERR_INVALID_ARG, "n (%d) and heads (%d) must be >= 1", n, heads);
+  if (head_dim < 2 || head_dim % 2 != 0) return fail(QWEN3_ERR_INVALID_ARG, "head_dim (%d) must be even", head_dim);
+  if (row_stride < static_cast<int64_t>(heads) * head_dim)
+    return fail(QWEN3_ERR_INVALID_ARG, "row_stride (%lld) must be >= heads * head_dim",
+                static_cast<long long>(row_stride));
+  if (pairing != 0 && pairing != 1) return fail(QWEN3_ERR_INVALID_ARG, "pairing must be 0 (split) or 1 (adjacent)");
+  if (!x || !cos_tab || !sin_tab) return fail(QWEN3_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (misaligned16({x, cos_tab, sin_tab})) return fail(QWEN3_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  KTimer t("apply_rope_tables", s);
+  const hipError_t e = q3::launch_apply_rope_tables(x, dtype, n, heads, head_dim, row_stride, cos_tab, sin_tab,
+                                                    pairing, s);
+  return e == hipSuccess ? QWEN3_OK : hip_fail(e, "apply_rope_tables launch");
 }
 
 int swiglu_ffn(const void* x_normed, const void* w_gate, const void* w_up, const void* w_down,

@@ -107,10 +107,11 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnF32Params p) {
   float m = -INFINITY, l = 0.f, o[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) o[r] = 0.f;
-  for (int j0 = 0; j0 <= s; j0 += 64) {
+  const int last = p.causal ? s : p.S - 1;  // last key this query sees
+  for (int j0 = 0; j0 <= last; j0 += 64) {
     const int j = j0 + lane;
     float z = -INFINITY;
-    if (j <= s) {
+    if (j <= last) {
       const float* k = p.k + static_cast<int64_t>(j) * p.k_stride + static_cast<int64_t>(g) * HD;
       float dot = 0.f;
       for (int d = 0; d < HD; ++d) dot = fmaf(qs[d], k[d], dot);
@@ -121,13 +122,13 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnF32Params p) {
     for (int off = 32; off >= 1; off >>= 1) mt = fmaxf(mt, __shfl_xor(mt, off));
     const float m_new = fmaxf(m, mt);
     const float alpha = expf(m - m_new);
-    const float pj = j <= s ? expf(z - m_new) : 0.f;
+    const float pj = j <= last ? expf(z - m_new) : 0.f;
     l = l * alpha + wave_sum(pj);
     m = m_new;
     __syncthreads();
     ps[lane] = pj;
     __syncthreads();
-    const int nj = min(64, s + 1 - j0);
+    const int nj = min(64, last + 1 - j0);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       float acc = o[r] * alpha;

@@ -29,6 +29,16 @@ hipError_t launch_embed_gather(const int32_t* tokens, const void* table, int dt,
 // y[r] = sum_k W[r, k] x[k], W [rows, hidden] of dt, x and y fp32 (hidden % 8 == 0).
 hipError_t launch_gemv_rows(const void* W, int dt, const float* x, float* y, int rows, int hidden, hipStream_t s);
 
+// ---- vision-tower rope tables and their application (vision_rope.hip) ----------------------
+// cos / sin fp32 [t*h*w, hd] of a merge-block-ordered patch grid; layout 0: 2-D row | col,
+// layout 1: 3-axis 4:6:6.
+hipError_t launch_vision_rope_tables(int layout, int t, int h, int w, int merge, int hd, double log2_theta,
+                                     float* cosv, float* sinv, hipStream_t s);
+// In place on x [n, heads, hd] (row stride in elements) of dt; pairing 0: split halves,
+// 1: adjacent lanes.
+hipError_t launch_apply_rope_tables(void* x, int dt, int n, int heads, int hd, int64_t row_stride,
+                                    const float* cosv, const float* sinv, int pairing, hipStream_t s);
+
 // ---- per-head RMSNorm + interleaved MRoPE, in place ---------------------------------------
 struct RopeParams {
   void* q;            // token t, head h at q + t*q_stride + h*hd
@@ -77,6 +87,8 @@ struct AttnParams {
   int64_t q_stride, k_stride, v_stride, o_stride;  // elements between consecutive tokens
   int S, nh, nkv;
   float scale_log2;    // softmax scale * log2(e)
+  int head_dim;        // 64 or 128
+  int causal;          // 1: key j <= query s; 0: every key (bidirectional)
 };
 hipError_t launch_attention_mfma(const AttnParams& p, int op, hipStream_t s);
 
@@ -96,6 +108,7 @@ struct AttnF32Params {
   int64_t q_stride, k_stride, v_stride, o_stride;
   int S, nh, nkv;
   float scale;
+  int causal;          // 1: key j <= query s; 0: every key
 };
 hipError_t launch_attention_f32(const AttnF32Params& p, int head_dim, hipStream_t s);
 

@@ -186,6 +186,48 @@ def gqa_causal_attention(q, k, v, scale=None, out=None):
     return out
 
 
+def gqa_bidirectional_attention(q, k, v, scale=None, out=None):
+    """out [S, nh, hd] = GQA softmax(scale q k^T) v over every key (no causal mask)."""
+    lib = _lib.load()
+    s, nh, hd = q.shape
+    nkv = k.shape[1]
+    if scale is None:
+        scale = hd ** -0.5
+    if out is None:
+        out = torch.empty_like(q)
+    _lib.check(lib.gqa_bidirectional_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(out), int(s), int(nh),
+                                               int(nkv), int(hd), float(scale), _dt(q), _stream()))
+    return out
+
+
+VISION_ROPE_LAYOUTS = {"2d": 0, "3axis": 1}
+ROPE_PAIRINGS = {"split": 0, "adjacent": 1}
+
+
+def vision_rope_tables(grid, head_dim, theta, merge, layout="2d"):
+    """(cos, sin) float32 [t*h*w, head_dim] on the GPU for a (t, h, w) patch grid."""
+    lib = _lib.load()
+    t, h, w = (int(a) for a in grid)
+    n = t * h * w
+    cos = torch.empty(n, head_dim, dtype=torch.float32, device="cuda")
+    sin = torch.empty_like(cos)
+    _lib.check(lib.vision_rope_tables(t, h, w, int(merge), int(head_dim), float(theta),
+                                      VISION_ROPE_LAYOUTS[layout], _ptr(cos), _ptr(sin), _stream()))
+    return cos, sin
+
+
+def apply_rope_tables(x, cos, sin, pairing="split"):
+    """In place on x [n, heads, head_dim] (rows may be strided views of a wider row); returns x."""
+    lib = _lib.load()
+    n, heads, hd = x.shape
+    if x.stride(2) != 1 or x.stride(1) != hd:
+        raise ValueError("heads of a row must be contiguous")
+    _lib.check(lib.apply_rope_tables(ctypes.c_void_p(x.data_ptr()), int(n), int(heads), int(hd),
+                                     int(x.stride(0)), _ptr(cos), _ptr(sin), ROPE_PAIRINGS[pairing],
+                                     _dt(x), _stream()))
+    return x
+
+
 def swiglu_ffn(x_normed, w_gate, w_up, w_down, residual=None, out_dtype=torch.float32, out=None,
                workspace=None):
     """out [S, H] = [residual +] (silu(x Wg^T) * (x Wu^T)) Wd^T."""
