@@ -573,6 +573,70 @@ def test_bidirectional_attention_pins():
                        rtol=1e-12, atol=1e-13)
 
 
+# ---------------------------------------------------------------- KV cache + decode step (f3)
+
+def test_decode_attention_brute_force_and_last_causal_row():
+    r = _rng(93)
+    L, nh, nkv, hd = 7, 4, 2, 4
+    q, k, v = r.standard_normal((nh, hd)), r.standard_normal((L, nkv, hd)), r.standard_normal((L, nkv, hd))
+    o = oracle.decode_attention(q, k, v)
+    for h in range(nh):
+        g = h // 2
+        z = [sum(q[h, e] * k[j, g, e] for e in range(hd)) / math.sqrt(hd) for j in range(L)]
+        p = [math.exp(t - max(z)) for t in z]
+        want = [sum(p[j] * v[j, g, e] for j in range(L)) / sum(p) for e in range(hd)]
+        assert np.allclose(o[h], want, rtol=1e-12, atol=1e-13)
+    # the query of the last position of a causal prefill sees exactly the cache
+    qs = np.concatenate([r.standard_normal((L - 1, nh, hd)), q[None]], axis=0)
+    assert np.allclose(o, oracle.causal_gqa_attention(qs, k, v)[-1], rtol=1e-12, atol=1e-13)
+    # a single cached key returns its value; the order of the cache rows does not matter
+    assert np.allclose(oracle.decode_attention(q, k[:1], v[:1]), np.repeat(v[0], 2, axis=0), rtol=0, atol=1e-15)
+    perm = r.permutation(L)
+    assert np.allclose(oracle.decode_attention(q, k[perm], v[perm]), o, rtol=1e-12, atol=1e-13)
+
+
+def test_prefill_kv_entries_are_the_normed_rotated_keys():
+    cfg = _tiny_cfg()
+    w = _tiny_weights(cfg)
+    s = 5
+    x = _rng(94).standard_normal((s, cfg.hidden))
+    pos = oracle.mrope_positions(s, [(1, 2, 2)])
+    y, kc, vc = oracle.prefill_kv(x, w, cfg, pos)
+    assert np.allclose(y, oracle.layer_prefill(x, w, cfg, pos), rtol=0, atol=0)
+    xn = oracle.rms_norm(x, w["attn_norm"], cfg.eps)
+    v = brute.matvec_rows(xn.tolist(), w["wv"].tolist())
+    assert np.allclose(vc.reshape(s, -1), v, rtol=1e-12, atol=1e-13)
+    # the rotation keeps each (i, i + hd/2) pair's norm: the norm of the per-head RMSNorm
+    k = np.asarray(brute.matvec_rows(xn.tolist(), w["wk"].tolist())).reshape(s, cfg.n_kv_heads, cfg.head_dim)
+    kn = k / np.sqrt(np.mean(k * k, axis=-1, keepdims=True) + cfg.eps) * w["k_norm"]
+    half = cfg.head_dim // 2
+    assert np.allclose(kc[..., :half] ** 2 + kc[..., half:] ** 2, kn[..., :half] ** 2 + kn[..., half:] ** 2,
+                       rtol=1e-12, atol=1e-13)
+    # position 0 is not rotated
+    assert np.allclose(kc[0], kn[0], rtol=1e-12, atol=1e-13)
+
+
+def test_decode_steps_reproduce_the_prefill_rows():
+    cfg = _tiny_cfg()
+    w = _tiny_weights(cfg, seed=95)
+    n, s0 = 9, 4
+    x = _rng(96).standard_normal((n, cfg.hidden))
+    pos = oracle.mrope_positions(n, [(1, 2, 2)])
+    full = oracle.layer_prefill(x, w, cfg, pos)
+    _, kc, vc = oracle.prefill_kv(x[:s0], w, cfg, pos[:, :s0])
+    for t in range(s0, n):
+        y, kn, vn = oracle.layer_decode(x[t], w, cfg, pos[:, t], kc, vc)
+        assert np.allclose(y, full[t], rtol=1e-11, atol=1e-12)
+        kc = np.concatenate([kc, kn[None]], axis=0)
+        vc = np.concatenate([vc, vn[None]], axis=0)
+    # the appended entries equal the ones a prefill over the whole sequence forms
+    _, k_all, v_all = oracle.prefill_kv(x, w, cfg, pos)
+    assert np.allclose(kc, k_all, rtol=1e-12, atol=1e-13) and np.allclose(vc, v_all, rtol=1e-12, atol=1e-13)
+    # a decode step on an empty cache is the one-token prefill
+    y0, _, _ = oracle.layer_decode(x[0], w, cfg, pos[:, 0], kc[:0], vc[:0])
+    assert np.allclose(y0, full[0], rtol=1e-11, atol=1e-12)
+
+
 # ---------------------------------------------------------------- generator
 
 def test_generator_deterministic_and_distributions():
