@@ -270,6 +270,75 @@ int qwen3_model_prefill_logits_last(const qwen3_model_cfg* cfg, const qwen3_mode
                                     float* logits, void* workspace, size_t workspace_bytes,
                                     void* stream);
 
+/* ---- KV cache and one decode step -------------------------------------------------------------
+ *
+ * hf2q 0.1.1, qwen3vl_text/forward.rs: the module doc's note on why the prefill keeps no KV cache
+ * yet (a generation loop would prefill prompt + decoded tokens again per new token; keeping the
+ * keys and values for incremental decode is the later step) and point 4 of the notes on
+ * `forward_text_prefill_logits_last`. Reading taken here: per layer the cache keeps, for every
+ * position and KV head, k' (k after the per-head RMSNorm and the rotation) and v, exactly as the
+ * causal layer forms them; a decode step runs the layer on one new token whose query attends to
+ * every cached key and to its own, so its output equals the last row of a prefill over the longer
+ * sequence.
+ *
+ * Cache layout: K and V are separate device buffers, each [n_kv_heads][capacity][head_dim]
+ * (head-major: one KV head's rows are contiguous), of the layer's act_dtype (f16 by default).
+ * Row r of head g lives at cache + (g * capacity + r) * head_dim elements. The caller owns both
+ * buffers and the count of live rows.
+ */
+
+/* Copies n token rows of k and v into cache rows row0 .. row0+n-1, converting src_dtype to
+ * cache_dtype (round to nearest even; the same type copies bit for bit).
+ *   k, v        [n, n_kv_heads, head_dim] of src_dtype, token t of head g at k + t*k_stride +
+ *               g*head_dim (strides in elements, multiples of 8, >= n_kv_heads*head_dim).
+ *   head_dim    a multiple of 8. row0 >= 0, row0 + n <= capacity.
+ * The caches must not overlap k or v. */
+int kv_cache_write(const void *k, const void *v, int64_t k_stride, int64_t v_stride, int32_t n,
+                   int32_t n_kv_heads, int32_t head_dim, qwen3_dtype src_dtype, void *k_cache,
+                   void *v_cache, qwen3_dtype cache_dtype, int32_t capacity, int32_t row0, void *stream);
+
+/* qwen3_layer_prefill that also leaves the layer's cache: k' and v of positions 0 .. seq_len-1
+ * are written to rows 0 .. seq_len-1 of k_cache / v_cache (act_dtype, capacity >= seq_len rows
+ * per KV head). The output is the same as qwen3_layer_prefill's, bit for bit. The caches must
+ * not overlap the workspace, x_in or x_out. */
+int qwen3_layer_prefill_kv(const qwen3_layer_cfg *cfg, const qwen3_layer_weights *w,
+                           const void *x_in, void *x_out, int32_t seq_len,
+                           const int32_t *positions, const int32_t *ds_rows, int32_t n_ds,
+                           const void *ds, void *k_cache, void *v_cache, int32_t capacity,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/* Attention of one query row per head over the first `len` rows of the caches:
+ *   out[h] = sum_{j<len} softmax_j(scale * q[h] . K[g][j]) V[g][j],  g = h / (nh / nkv).
+ *   q, out      [n_heads, head_dim] fp32 (the query is rounded to cache_dtype before the
+ *               products, which accumulate in fp32; softmax and output in fp32).
+ *   k_cache, v_cache  [n_kv_heads][capacity][head_dim] of cache_dtype; 1 <= len <= capacity.
+ *   head_dim 64 or 128; n_heads / n_kv_heads <= 16; scale finite and > 0.
+ *   workspace   gqa_decode_attention_workspace_bytes(n_heads, n_kv_heads, head_dim, len) bytes,
+ *               256-byte aligned (per-split partial results; contents on entry do not matter). */
+int gqa_decode_attention(const float *q, const void *k_cache, const void *v_cache, int32_t capacity,
+                         int32_t len, int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, float scale,
+                         qwen3_dtype cache_dtype, float *out, void *workspace, size_t workspace_bytes,
+                         void *stream);
+/* Workspace for gqa_decode_attention; also enough for every smaller len. 0 for invalid input. */
+size_t gqa_decode_attention_workspace_bytes(int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, int32_t len);
+
+/* One new token through the layer, reading positions 0 .. len-1 from the caches and appending
+ * its own k' and v at row len:
+ *   xn = RMSNorm(x); q, k, v = xn W^T; per-head RMSNorm + interleaved MRoPE at `position`;
+ *   K[g][len] = k', V[g][len] = v; o = attention of q over rows 0 .. len; y1 = x + o Wo^T;
+ *   x_out = y1 + SwiGLU FFN(RMSNorm(y1)).
+ *   x_in, x_out [hidden] f32 (x_out may equal x_in); position device int32 [3] (t, h, w);
+ *   0 <= len < capacity. The new token's vectors stay in fp32 (matrix-vector products with
+ *   fp32 accumulation); the cache rows are stored in act_dtype. The same shape limits as
+ *   qwen3_layer_prefill, plus head_dim 64 or 128 and n_heads / n_kv_heads <= 16.
+ *   workspace   qwen3_layer_decode_workspace_bytes(cfg, capacity) bytes, 256-byte aligned.
+ * No DeepStack: decoded tokens are text. */
+int qwen3_layer_decode(const qwen3_layer_cfg *cfg, const qwen3_layer_weights *w, const float *x_in,
+                       float *x_out, const int32_t *position, void *k_cache, void *v_cache,
+                       int32_t capacity, int32_t len, void *workspace, size_t workspace_bytes,
+                       void *stream);
+size_t qwen3_layer_decode_workspace_bytes(const qwen3_layer_cfg *cfg, int32_t capacity);
+
 #ifdef __cplusplus
 }
 #endif

@@ -220,3 +220,70 @@ def test_model_argument_checks(lib):
 def test_timing_collect_empty(lib):
     n = ctypes.c_int32(-1)
     assert lib.qwen3_timing_collect(None, 0, ctypes.byref(n)) == 0 and n.value == 0
+
+
+# ---- KV cache and decode step: every call below fails a host check before any launch
+
+def test_kv_cache_write_argument_checks(lib):
+    # rows [50, 90) do not fit a capacity of 80
+    assert lib.kv_cache_write(FAKE, FAKE, 512, 512, 40, 4, 128, 2, FAKE, FAKE, 2, 80, 50, None) == 1
+    assert "capacity" in lib.qwen3_last_error().decode()
+    assert lib.kv_cache_write(FAKE, FAKE, 512, 512, 4, 4, 100, 2, FAKE, FAKE, 2, 80, 0, None) == 2   # hd % 8
+    assert lib.kv_cache_write(FAKE, FAKE, 256, 512, 4, 4, 128, 2, FAKE, FAKE, 2, 80, 0, None) == 1   # stride
+    assert lib.kv_cache_write(FAKE, FAKE, 512, 512, 4, 4, 128, 2, FAKE, FAKE, 5, 80, 0, None) == 1   # dtype
+    assert lib.kv_cache_write(FAKE, FAKE, 512, 512, 0, 4, 128, 2, FAKE, FAKE, 2, 80, 0, None) == 1   # n
+    assert lib.kv_cache_write(FAKE, None, 512, 512, 4, 4, 128, 2, FAKE, FAKE, 2, 80, 0, None) == 1
+    odd = ctypes.c_void_p(0x1002)
+    assert lib.kv_cache_write(FAKE, FAKE, 512, 512, 4, 4, 128, 2, odd, FAKE, 2, 80, 0, None) == 1
+
+
+def test_decode_attention_argument_checks(lib):
+    ws = ctypes.c_void_p(0x100000)
+    big = 1 << 30
+    assert lib.gqa_decode_attention(FAKE, FAKE, FAKE, 16, 17, 8, 2, 128, 0.1, 2, FAKE, ws, big, None) == 1   # len > cap
+    assert lib.gqa_decode_attention(FAKE, FAKE, FAKE, 16, 0, 8, 2, 128, 0.1, 2, FAKE, ws, big, None) == 1    # len 0
+    assert lib.gqa_decode_attention(FAKE, FAKE, FAKE, 16, 8, 34, 2, 128, 0.1, 2, FAKE, ws, big, None) == 2   # group 17
+    assert lib.gqa_decode_attention(FAKE, FAKE, FAKE, 16, 8, 8, 2, 96, 0.1, 2, FAKE, ws, big, None) == 2     # hd 96
+    assert lib.gqa_decode_attention(FAKE, FAKE, FAKE, 16, 8, 8, 3, 128, 0.1, 2, FAKE, ws, big, None) == 1    # 8 % 3
+    assert lib.gqa_decode_attention(FAKE, FAKE, FAKE, 16, 8, 8, 2, 128, 0.0, 2, FAKE, ws, big, None) == 1    # scale
+    assert lib.gqa_decode_attention(FAKE, FAKE, FAKE, 16, 8, 8, 2, 128, 0.1, 2, FAKE, ws, 16, None) == 3     # workspace
+    assert lib.gqa_decode_attention(FAKE, FAKE, FAKE, 16, 8, 8, 2, 128, 0.1, 2, FAKE, ctypes.c_void_p(0x100010),
+                                    big, None) == 3                                                           # alignment
+
+
+def test_decode_workspace_formula(lib):
+    def a256(b):
+        return (b + 255) // 256 * 256
+    # 8 KV heads: about 512 workgroups, so at most 64 key splits; 4096 keys = 64 tiles of 64
+    assert lib.gqa_decode_attention_workspace_bytes(32, 8, 128, 4096) == a256(32 * 64 * 128 * 4) + a256(32 * 64 * 8)
+    assert lib.gqa_decode_attention_workspace_bytes(32, 8, 128, 100) == a256(32 * 2 * 128 * 4) + a256(32 * 2 * 8)
+    assert lib.gqa_decode_attention_workspace_bytes(32, 8, 128, 10 ** 6) == lib.gqa_decode_attention_workspace_bytes(
+        32, 8, 128, 4096)
+    assert lib.gqa_decode_attention_workspace_bytes(32, 8, 128, 0) == 0
+    c = _cfg(hidden=4096, n_heads=32, n_kv_heads=8, ffn=12288)
+    attn = lib.gqa_decode_attention_workspace_bytes(32, 8, 128, 8192)
+    want = a256(4096 * 4) + a256((4096 + 2048) * 4) + a256(4096 * 4) + a256(12288 * 4) + attn
+    assert lib.qwen3_layer_decode_workspace_bytes(ctypes.byref(c), 8192) == want
+    assert lib.qwen3_layer_decode_workspace_bytes(ctypes.byref(c), 0) == 0
+
+
+def test_layer_decode_and_prefill_kv_argument_checks(lib):
+    c = _cfg()
+    w = _weights()
+    ws = ctypes.c_void_p(0x100000)
+    need = lib.qwen3_layer_decode_workspace_bytes(ctypes.byref(c), 64)
+    # len must leave the new token's row inside the cache
+    assert lib.qwen3_layer_decode(ctypes.byref(c), ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, ctypes.c_void_p(0x2000),
+                                  64, 64, ws, need, None) == 1
+    assert "capacity" in lib.qwen3_last_error().decode()
+    assert lib.qwen3_layer_decode(ctypes.byref(c), ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, 64, 3, ws, need,
+                                  None) == 1                                                 # same k and v cache
+    assert lib.qwen3_layer_decode(ctypes.byref(c), ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, ctypes.c_void_p(0x2000),
+                                  64, 3, ws, need - 256, None) == 3
+    assert lib.qwen3_layer_decode(ctypes.byref(_cfg(n_heads=32, n_kv_heads=1)), ctypes.byref(w), FAKE, FAKE, FAKE,
+                                  FAKE, ctypes.c_void_p(0x2000), 64, 3, ws, 1 << 30, None) == 2
+    ws_p = lib.qwen3_layer_workspace_bytes(ctypes.byref(c), 16)
+    assert lib.qwen3_layer_prefill_kv(ctypes.byref(c), ctypes.byref(w), FAKE, FAKE, 16, FAKE, None, 0, None, FAKE,
+                                      ctypes.c_void_p(0x2000), 15, ws, ws_p, None) == 1     # capacity < S
+    assert lib.qwen3_layer_prefill_kv(ctypes.byref(c), ctypes.byref(w), FAKE, FAKE, 16, FAKE, None, 0, None, None,
+                                      ctypes.c_void_p(0x2000), 16, ws, ws_p, None) == 1

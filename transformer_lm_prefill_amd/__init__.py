@@ -1,5 +1,5 @@
 """MI355X (gfx950) prefill of Qwen3/Qwen3-VL text decoder layers (and of the whole text model
-to its last position's logits).
+to its last position's logits), the KV cache a prefill leaves and one decode step over it.
 
 The computation runs in libqwen3_prefill.so (hand-written HIP kernels behind a C ABI, see
 include/qwen3_prefill.h). This package is the thin Python binding: it passes torch device
@@ -10,9 +10,16 @@ from .ops import (  # noqa: F401
     LayerSpec,
     Qwen3Error,
     apply_rope_tables,
+    decode_attention_workspace_bytes,
     gqa_bidirectional_attention,
     gqa_causal_attention,
+    gqa_decode_attention,
+    kv_cache_alloc,
+    kv_cache_write,
+    layer_decode,
+    layer_decode_workspace_bytes,
     layer_prefill,
+    layer_prefill_kv,
     layer_workspace_bytes,
     model_prefill_logits_last,
     model_workspace_bytes,

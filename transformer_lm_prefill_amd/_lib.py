@@ -16,6 +16,9 @@ EXPORTS = ("qwen3_layer_workspace_bytes", "qwen3_layer_prefill", "qk_norm_mrope"
            "gqa_causal_attention", "gqa_bidirectional_attention", "vision_rope_tables",
            "apply_rope_tables", "swiglu_ffn", "swiglu_ffn_workspace_bytes", "rms_norm_rows",
            "qwen3_model_workspace_bytes", "qwen3_model_prefill_logits_last",
+           "kv_cache_write", "qwen3_layer_prefill_kv", "gqa_decode_attention",
+           "gqa_decode_attention_workspace_bytes", "qwen3_layer_decode",
+           "qwen3_layer_decode_workspace_bytes",
            "qwen3_last_error", "qwen3_timing_enable", "qwen3_timing_collect")
 
 
@@ -96,6 +99,21 @@ def load():
                                                     ctypes.POINTER(i32), i32, vp, vp, i32,
                                                     ctypes.POINTER(vp), vp, vp, sz, vp]
     lib.qwen3_model_prefill_logits_last.restype = ctypes.c_int
+    i64 = ctypes.c_int64
+    lib.kv_cache_write.argtypes = [vp, vp, i64, i64, i32, i32, i32, ctypes.c_int, vp, vp, ctypes.c_int, i32, i32, vp]
+    lib.kv_cache_write.restype = ctypes.c_int
+    lib.qwen3_layer_prefill_kv.argtypes = [ctypes.POINTER(LayerCfg), ctypes.POINTER(LayerWeights),
+                                           vp, vp, i32, vp, vp, i32, vp, vp, vp, i32, vp, sz, vp]
+    lib.qwen3_layer_prefill_kv.restype = ctypes.c_int
+    lib.gqa_decode_attention.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, f32, ctypes.c_int, vp, vp, sz, vp]
+    lib.gqa_decode_attention.restype = ctypes.c_int
+    lib.gqa_decode_attention_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.gqa_decode_attention_workspace_bytes.restype = sz
+    lib.qwen3_layer_decode.argtypes = [ctypes.POINTER(LayerCfg), ctypes.POINTER(LayerWeights),
+                                       vp, vp, vp, vp, vp, i32, i32, vp, sz, vp]
+    lib.qwen3_layer_decode.restype = ctypes.c_int
+    lib.qwen3_layer_decode_workspace_bytes.argtypes = [ctypes.POINTER(LayerCfg), i32]
+    lib.qwen3_layer_decode_workspace_bytes.restype = sz
     lib.qwen3_last_error.argtypes = []
     lib.qwen3_last_error.restype = ctypes.c_char_p
     lib.qwen3_timing_enable.argtypes = [ctypes.c_int]

@@ -261,10 +261,13 @@ size_t swiglu_ffn_workspace_bytes(int32_t seq_len, int32_t ffn, qwen3_dtype x_dt
   return align256(static_cast<size_t>(seq_len) * ffn * dsize(x_dtype));
 }
 
-int qwen3_layer_prefill(const qwen3_layer_cfg* cfg, const qwen3_layer_weights* w, const void* x_in,
-                        void* x_out, int32_t seq_len, const int32_t* positions,
-                        const int32_t* ds_rows, int32_t n_ds, const void* ds, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+// The layer prefill; with k_cache set it also writes k' and v of every position into rows
+// 0..seq_len-1 of the caches (capacity rows per KV head).
+static int layer_prefill_impl(const qwen3_layer_cfg* cfg, const qwen3_layer_weights* w, const void* x_in,
+                              void* x_out, int32_t seq_len, const int32_t* positions,
+                              const int32_t* ds_rows, int32_t n_ds, const void* ds, void* k_cache,
+                              void* v_cache, int32_t capacity, void* workspace, size_t workspace_bytes,
+                              void* stream) {
   int st = check_cfg(cfg);
   if (st) return st;
   if (seq_len < 1) return fail(QWEN3_ERR_INVALID_ARG, "seq_len must be >= 1 (got %d): empty prompt", seq_len);
@@ -329,6 +332,14 @@ int qwen3_layer_prefill(const qwen3_layer_cfg* cfg, const qwen3_layer_weights* w
                      cfg->mrope_section[2]};
     if ((st = run_qk_norm_mrope(p, hd, dt, s))) return st;
   }
+  // k' and v of every position into the caches
+  if (k_cache) {
+    KTimer t("kv_cache_write", s);
+    q3::KvWriteParams kp{qkv + static_cast<size_t>(q_dim) * e, qkv + static_cast<size_t>(q_dim + kv_dim) * e,
+                         qkv_dim, qkv_dim, S, nkv, hd, k_cache, v_cache, capacity, 0};
+    const hipError_t he = q3::launch_kv_cache_write(kp, dt, dt, s);
+    if (he != hipSuccess) return hip_fail(he, "kv_cache_write launch");
+  }
   // a5: causal GQA attention -> o [S, q_dim]
   if ((st = run_attention(qkv, qkv + static_cast<size_t>(q_dim) * e, qkv + static_cast<size_t>(q_dim + kv_dim) * e,
                           o, qkv_dim, qkv_dim, qkv_dim, q_dim, S, nh, nkv, hd,
@@ -350,6 +361,28 @@ int qwen3_layer_prefill(const qwen3_layer_cfg* cfg, const qwen3_layer_weights* w
     if (he != hipSuccess) return hip_fail(he, "deepstack_add launch");
   }
   return QWEN3_OK;
+}
+
+int qwen3_layer_prefill(const qwen3_layer_cfg* cfg, const qwen3_layer_weights* w, const void* x_in,
+                        void* x_out, int32_t seq_len, const int32_t* positions,
+                        const int32_t* ds_rows, int32_t n_ds, const void* ds, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  return layer_prefill_impl(cfg, w, x_in, x_out, seq_len, positions, ds_rows, n_ds, ds, nullptr, nullptr, 0,
+                            workspace, workspace_bytes, stream);
+}
+
+int qwen3_layer_prefill_kv(const qwen3_layer_cfg* cfg, const qwen3_layer_weights* w, const void* x_in,
+                           void* x_out, int32_t seq_len, const int32_t* positions,
+                           const int32_t* ds_rows, int32_t n_ds, const void* ds, void* k_cache,
+                           void* v_cache, int32_t capacity, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  if (!k_cache || !v_cache) return fail(QWEN3_ERR_INVALID_ARG, "k_cache / v_cache is NULL");
+  if (k_cache == v_cache) return fail(QWEN3_ERR_INVALID_ARG, "k_cache and v_cache must be different buffers");
+  if (misaligned16({k_cache, v_cache})) return fail(QWEN3_ERR_INVALID_ARG, "cache pointers must be 16-byte aligned");
+  if (capacity < seq_len)
+    return fail(QWEN3_ERR_INVALID_ARG, "capacity (%d) must be >= seq_len (%d)", capacity, seq_len);
+  return layer_prefill_impl(cfg, w, x_in, x_out, seq_len, positions, ds_rows, n_ds, ds, k_cache, v_cache, capacity,
+                            workspace, workspace_bytes, stream);
 }
 
 // ---- whole-model prefill to the last position's logits --------------------------------------
@@ -611,6 +644,201 @@ int qwen3_timing_collect(qwen3_kernel_time* out, int32_t max_entries, int32_t* n
     ++n;
   }
   if (n_out) *n_out = n;
+  return QWEN3_OK;
+}
+
+// ---- KV cache and one decode step ---------------------------------------------------------
+int kv_cache_write(const void* k, const void* v, int64_t k_stride, int64_t v_stride, int32_t n, int32_t n_kv_heads,
+                   int32_t head_dim, qwen3_dtype src_dtype, void* k_cache, void* v_cache, qwen3_dtype cache_dtype,
+                   int32_t capacity, int32_t row0, void* stream) {
+  if (!valid_dtype(src_dtype) || !valid_dtype(cache_dtype))
+    return fail(QWEN3_ERR_INVALID_ARG, "src_dtype / cache_dtype is not a qwen3_dtype");
+  if (n < 1 || n_kv_heads < 1) return fail(QWEN3_ERR_INVALID_ARG, "n (%d) and n_kv_heads (%d) must be >= 1", n, n_kv_heads);
+  if (head_dim < 8 || head_dim % 8 != 0)
+    return fail(QWEN3_ERR_UNSUPPORTED, "head_dim (%d) must be a positive multiple of 8", head_dim);
+  if (k_stride < static_cast<int64_t>(n_kv_heads) * head_dim || v_stride < static_cast<int64_t>(n_kv_heads) * head_dim ||
+      k_stride % 8 != 0 || v_stride % 8 != 0)
+    return fail(QWEN3_ERR_INVALID_ARG, "row strides must be multiples of 8 and >= n_kv_heads * head_dim");
+  if (row0 < 0 || capacity < 1 || static_cast<int64_t>(row0) + n > capacity)
+    return fail(QWEN3_ERR_INVALID_ARG, "rows [%d, %lld) do not fit a capacity of %d", row0,
+                static_cast<long long>(row0) + n, capacity);
+  if (!k || !v || !k_cache || !v_cache) return fail(QWEN3_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (misaligned16({k, v, k_cache, v_cache})) return fail(QWEN3_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  KTimer t("kv_cache_write", s);
+  q3::KvWriteParams p{k, v, k_stride, v_stride, n, n_kv_heads, head_dim, k_cache, v_cache, capacity, row0};
+  const hipError_t e = q3::launch_kv_cache_write(p, src_dtype, cache_dtype, s);
+  return e == hipSuccess ? QWEN3_OK : hip_fail(e, "kv_cache_write launch");
+}
+
+static size_t decode_attn_scratch(int32_t nh, int32_t nkv, int32_t hd, int32_t max_len, size_t* o_bytes) {
+  const size_t ns = static_cast<size_t>(q3::decode_max_splits(max_len, nkv));
+  *o_bytes = align256(static_cast<size_t>(nh) * ns * hd * 4);
+  return *o_bytes + align256(static_cast<size_t>(nh) * ns * 2 * 4);
+}
+
+static int check_decode_heads(int32_t nh, int32_t nkv, int32_t hd) {
+  if (nh < 1 || nkv < 1 || nh % nkv != 0)
+    return fail(QWEN3_ERR_INVALID_ARG, "n_heads (%d) must be a positive multiple of n_kv_heads (%d)", nh, nkv);
+  if (nh / nkv > 16) return fail(QWEN3_ERR_UNSUPPORTED, "n_heads / n_kv_heads must be <= 16 (got %d)", nh / nkv);
+  if (hd != 64 && hd != 128) return fail(QWEN3_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", hd);
+  return QWEN3_OK;
+}
+
+static int run_decode_attention(const float* q, const void* kc, const void* vc, int32_t capacity, int32_t len,
+                                int32_t nh, int32_t nkv, int32_t hd, float scale, qwen3_dtype cdt, float* out,
+                                char* scratch, hipStream_t s) {
+  size_t ob;
+  (void)decode_attn_scratch(nh, nkv, hd, len, &ob);
+  q3::DecodeAttnParams p{q, kc, vc, capacity, len, nh, nkv, scale * 1.4426950408889634f,
+                         q3::decode_tiles_per_split(len, nkv), q3::decode_num_splits(len, nkv),
+                         reinterpret_cast<float*>(scratch), reinterpret_cast<float*>(scratch + ob)};
+  KTimer t("decode_attention", s);
+  const hipError_t e = q3::launch_decode_attention(p, hd, cdt, out, s);
+  return e == hipSuccess ? QWEN3_OK : hip_fail(e, "decode_attention launch");
+}
+
+size_t gqa_decode_attention_workspace_bytes(int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, int32_t len) {
+  if (n_heads < 1 || n_kv_heads < 1 || n_heads % n_kv_heads != 0 || head_dim < 1 || len < 1) return 0;
+  size_t ob;
+  return decode_attn_scratch(n_heads, n_kv_heads, head_dim, len, &ob);
+}
+
+int gqa_decode_attention(const float* q, const void* k_cache, const void* v_cache, int32_t capacity, int32_t len,
+                         int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, float scale, qwen3_dtype cache_dtype,
+                         float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_dtype(cache_dtype)) return fail(QWEN3_ERR_INVALID_ARG, "cache_dtype %d is not a qwen3_dtype", cache_dtype);
+  int st = check_decode_heads(n_heads, n_kv_heads, head_dim);
+  if (st) return st;
+  if (len < 1 || len > capacity)
+    return fail(QWEN3_ERR_INVALID_ARG, "len (%d) must be in [1, capacity = %d]", len, capacity);
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(QWEN3_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (!q || !k_cache || !v_cache || !out) return fail(QWEN3_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (misaligned16({q, k_cache, v_cache, out})) return fail(QWEN3_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  const size_t need = gqa_decode_attention_workspace_bytes(n_heads, n_kv_heads, head_dim, len);
+  if (!workspace || workspace_bytes < need)
+    return fail(QWEN3_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need, workspace_bytes,
+                workspace ? "" : ", NULL pointer");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(QWEN3_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  return run_decode_attention(q, k_cache, v_cache, capacity, len, n_heads, n_kv_heads, head_dim, scale, cache_dtype,
+                              out, static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+}
+
+struct DecodeWorkspace {
+  size_t xn, qkv, o, act, attn, total;
+};
+
+static DecodeWorkspace decode_layout(const qwen3_layer_cfg* c, int32_t capacity) {
+  const size_t q_dim = static_cast<size_t>(c->n_heads) * c->head_dim;
+  const size_t kv_dim = static_cast<size_t>(c->n_kv_heads) * c->head_dim;
+  DecodeWorkspace d;
+  size_t ob;
+  d.xn = 0;
+  d.qkv = d.xn + align256(static_cast<size_t>(c->hidden) * 4);
+  d.o = d.qkv + align256((q_dim + 2 * kv_dim) * 4);
+  d.act = d.o + align256(q_dim * 4);
+  d.attn = d.act + align256(static_cast<size_t>(c->ffn) * 4);
+  d.total = d.attn + decode_attn_scratch(c->n_heads, c->n_kv_heads, c->head_dim, capacity, &ob);
+  return d;
+}
+
+size_t qwen3_layer_decode_workspace_bytes(const qwen3_layer_cfg* cfg, int32_t capacity) {
+  if (!cfg || capacity < 1 || cfg->n_heads < 1 || cfg->n_kv_heads < 1 || cfg->n_heads % cfg->n_kv_heads != 0)
+    return 0;
+  return decode_layout(cfg, capacity).total;
+}
+
+static int run_gemv(const char* name, const q3::GemvParams& p, int epi, qwen3_dtype wdt, hipStream_t s) {
+  KTimer t(name, s);
+  const hipError_t e = q3::launch_gemv(p, epi, wdt, s);
+  return e == hipSuccess ? QWEN3_OK : hip_fail(e, name);
+}
+
+int qwen3_layer_decode(const qwen3_layer_cfg* cfg, const qwen3_layer_weights* w, const float* x_in, float* x_out,
+                       const int32_t* position, void* k_cache, void* v_cache, int32_t capacity, int32_t len,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_cfg(cfg);
+  if (st) return st;
+  if ((st = check_decode_heads(cfg->n_heads, cfg->n_kv_heads, cfg->head_dim))) return st;
+  if (!w) return fail(QWEN3_ERR_INVALID_ARG, "weights is NULL");
+  const void* wp[] = {w->attn_norm, w->wq, w->wk, w->wv, w->q_norm, w->k_norm,
+                      w->wo, w->ffn_norm, w->w_gate, w->w_up, w->w_down};
+  for (const void* q : wp)
+    if (!q) return fail(QWEN3_ERR_INVALID_ARG, "a weight pointer is NULL");
+  if (!x_in || !x_out || !position || !k_cache || !v_cache)
+    return fail(QWEN3_ERR_INVALID_ARG, "x_in / x_out / position / k_cache / v_cache is NULL");
+  if (k_cache == v_cache) return fail(QWEN3_ERR_INVALID_ARG, "k_cache and v_cache must be different buffers");
+  if (misaligned16({x_in, x_out, k_cache, v_cache, w->attn_norm, w->wq, w->wk, w->wv, w->q_norm, w->k_norm, w->wo,
+                    w->ffn_norm, w->w_gate, w->w_up, w->w_down}))
+    return fail(QWEN3_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  if (len < 0 || len >= capacity)
+    return fail(QWEN3_ERR_INVALID_ARG, "len (%d) must be in [0, capacity = %d): the new token takes row len", len,
+                capacity);
+  {
+    const size_t xb = static_cast<size_t>(cfg->hidden) * 4;
+    const char* a = reinterpret_cast<const char*>(x_in);
+    const char* b = reinterpret_cast<const char*>(x_out);
+    if (a != b && a < b + xb && b < a + xb)
+      return fail(QWEN3_ERR_INVALID_ARG, "x_out partially overlaps x_in (only x_out == x_in is allowed)");
+  }
+  const DecodeWorkspace L = decode_layout(cfg, capacity);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(QWEN3_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", L.total, workspace_bytes,
+                workspace ? "" : ", NULL pointer");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(QWEN3_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const qwen3_dtype wdt = cfg->wdtype, cdt = cfg->act_dtype;
+  const int H = cfg->hidden, nh = cfg->n_heads, nkv = cfg->n_kv_heads, hd = cfg->head_dim, F = cfg->ffn;
+  const int q_dim = nh * hd, kv_dim = nkv * hd, qkv_dim = q_dim + 2 * kv_dim;
+  char* ws = static_cast<char*>(workspace);
+  float* xn = reinterpret_cast<float*>(ws + L.xn);
+  float* qkv = reinterpret_cast<float*>(ws + L.qkv);
+  float* o = reinterpret_cast<float*>(ws + L.o);
+  float* act = reinterpret_cast<float*>(ws + L.act);
+
+  // input RMSNorm of the new row (fp32)
+  if ((st = run_rmsnorm(x_in, w->attn_norm, wdt, xn, QWEN3_F32, 1, H, cfg->rms_eps, s))) return st;
+  // q | k | v of the new token
+  {
+    q3::GemvParams p{w->wq, w->wk, w->wv, q_dim, q_dim + kv_dim, xn, qkv, nullptr, qkv_dim, H};
+    if ((st = run_gemv("gemv_qkv", p, q3::GV_STORE, wdt, s))) return st;
+  }
+  // per-head RMSNorm + interleaved MRoPE at the token's position
+  {
+    q3::RopeParams p{qkv, qkv + q_dim, qkv_dim, qkv_dim, 1, nh, nkv, w->q_norm, w->k_norm, wdt, position,
+                     cfg->rms_eps, std::log2(static_cast<double>(cfg->rope_theta)), cfg->mrope_section[1],
+                     cfg->mrope_section[2]};
+    if ((st = run_qk_norm_mrope(p, hd, QWEN3_F32, s))) return st;
+  }
+  // append k' and v at row len
+  {
+    KTimer t("kv_cache_write", s);
+    q3::KvWriteParams kp{qkv + q_dim, qkv + q_dim + kv_dim, qkv_dim, qkv_dim, 1, nkv, hd, k_cache, v_cache,
+                         capacity, len};
+    const hipError_t he = q3::launch_kv_cache_write(kp, QWEN3_F32, cdt, s);
+    if (he != hipSuccess) return hip_fail(he, "kv_cache_write launch");
+  }
+  // the new query over the len + 1 cached keys
+  if ((st = run_decode_attention(qkv, k_cache, v_cache, capacity, len + 1, nh, nkv, hd,
+                                 1.0f / std::sqrt(static_cast<float>(hd)), cdt, o, ws + L.attn, s)))
+    return st;
+  // y1 = x + o Wo^T
+  {
+    q3::GemvParams p{w->wo, nullptr, nullptr, H, H, o, x_out, x_in, H, q_dim};
+    if ((st = run_gemv("gemv_o_resid", p, q3::GV_RESID, wdt, s))) return st;
+  }
+  if ((st = run_rmsnorm(x_out, w->ffn_norm, wdt, xn, QWEN3_F32, 1, H, cfg->rms_eps, s))) return st;
+  {
+    q3::GemvParams p{w->w_gate, w->w_up, nullptr, F, F, xn, act, nullptr, F, H};
+    if ((st = run_gemv("gemv_gate_up_swiglu", p, q3::GV_SWIGLU, wdt, s))) return st;
+  }
+  {
+    q3::GemvParams p{w->w_down, nullptr, nullptr, H, H, act, x_out, x_out, H, F};
+    if ((st = run_gemv("gemv_down_resid", p, q3::GV_RESID, wdt, s))) return st;
+  }
   return QWEN3_OK;
 }
 

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kernels.h"
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -109,6 +111,51 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
   const float lo = __uint_as_float(w << 16);
   const float hi = __uint_as_float(w & 0xFFFF0000u);
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// 8 consecutive elements starting at src + i (element index), as floats; one 16-byte load for
+// 16-bit types, two for fp32. DT is a DType.
+template <int DT>
+__device__ __forceinline__ void load8(const void* src, int64_t i, float (&v)[8]) {
+  if (DT == DT_F32) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(static_cast<const float*>(src) + i);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(static_cast<const float*>(src) + i + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] = a[e];
+      v[4 + e] = b[e];
+    }
+  } else {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(src) + i);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint16_t lo = static_cast<uint16_t>(w[e] & 0xFFFF), hi = static_cast<uint16_t>(w[e] >> 16);
+      v[2 * e] = DT == DT_BF16 ? bf2f(lo) : h2f(lo);
+      v[2 * e + 1] = DT == DT_BF16 ? bf2f(hi) : h2f(hi);
+    }
+  }
+}
+
+// The inverse of load8: 8 floats stored at dst + i, rounded to nearest even for 16-bit types.
+template <int DT>
+__device__ __forceinline__ void store8(void* dst, int64_t i, const float (&v)[8]) {
+  if (DT == DT_F32) {
+    float* d = static_cast<float*>(dst) + i;
+    *reinterpret_cast<f32x4*>(d) = f32x4{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4*>(d + 4) = f32x4{v[4], v[5], v[6], v[7]};
+  } else {
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = DT == DT_BF16 ? Fmt<OP_BF16>::pack2(v[2 * e], v[2 * e + 1]) : Fmt<OP_F16>::pack2(v[2 * e], v[2 * e + 1]);
+    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(dst) + i) = w;
+  }
 }
 
 }  // namespace q3

@@ -39,6 +39,48 @@ hipError_t launch_vision_rope_tables(int layout, int t, int h, int w, int merge,
 hipError_t launch_apply_rope_tables(void* x, int dt, int n, int heads, int hd, int64_t row_stride,
                                     const float* cosv, const float* sinv, int pairing, hipStream_t s);
 
+// ---- KV cache and one decode step (decode.hip) ------------------------------------------------
+// Caches: K and V each [nkv][capacity][hd] of the cache type.
+struct KvWriteParams {
+  const void* k; const void* v;   // token t, kv head g at k + t*k_stride + g*hd (same for v)
+  int64_t k_stride, v_stride;     // elements between consecutive tokens
+  int n, nkv, hd;                 // tokens to write, hd % 8 == 0
+  void* kc; void* vc;
+  int64_t capacity;               // rows per head in the caches
+  int row0;                       // token t goes to row row0 + t (row0 + n <= capacity)
+};
+hipError_t launch_kv_cache_write(const KvWriteParams& p, int src_dt, int cache_dt, hipStream_t s);
+
+struct DecodeAttnParams {
+  const float* q;                 // [nh, hd] fp32: one query row per head
+  const void* kc; const void* vc; // caches, rows 0..len-1 live
+  int64_t capacity;
+  int len, nh, nkv;               // nh / nkv <= 16
+  float scale_log2;               // softmax scale * log2(e)
+  int tiles_per_split, nsplit;    // decode_tiles_per_split / decode_num_splits(len, nkv)
+  float* part_o;                  // [nh, nsplit, hd] fp32 scratch
+  float* part_ml;                 // [nh, nsplit, 2] fp32 scratch
+};
+int decode_tiles_per_split(int len, int nkv);
+int decode_num_splits(int len, int nkv);
+int decode_max_splits(int len, int nkv);   // >= decode_num_splits(l, nkv) for every l <= len
+// out [nh, hd] fp32 = softmax(scale q k^T) v over the len cached keys of each head's group.
+hipError_t launch_decode_attention(const DecodeAttnParams& p, int hd, int cache_dt, float* out, hipStream_t s);
+
+// y[r] = epilogue(sum_k W_r[k] x[k]) for r < rows; x, y, R fp32; W of wdt [*, K], K % 8 == 0.
+enum GemvEpilogue { GV_STORE = 0, GV_RESID = 1, GV_SWIGLU = 2 };
+struct GemvParams {
+  // GV_STORE / GV_RESID: row r < nseg0 is W0 row r, r < nseg1 is W1 row r - nseg0, else W2 row
+  // r - nseg1. GV_SWIGLU: W0 = gate, W1 = up, both [rows, K]; y[r] = silu(g_r) * u_r.
+  const void* W0; const void* W1; const void* W2;
+  int nseg0, nseg1;
+  const float* x;
+  float* y;
+  const float* R;                 // GV_RESID: y[r] = R[r] + product (R may alias y)
+  int rows, K;
+};
+hipError_t launch_gemv(const GemvParams& p, int epi, int wdt, hipStream_t s);
+
 // ---- per-head RMSNorm + interleaved MRoPE, in place ---------------------------------------
 struct RopeParams {
   void* q;            // token t, head h at q + t*q_stride + h*hd

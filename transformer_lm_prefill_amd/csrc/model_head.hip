@@ -13,28 +13,6 @@
 
 namespace q3 {
 
-// 8 consecutive elements starting at src + i, as floats (16-byte load for 16-bit types).
-template <int DT>
-__device__ __forceinline__ void load8(const void* src, int64_t i, float (&v)[8]) {
-  if (DT == DT_F32) {
-    const f32x4 a = *reinterpret_cast<const f32x4*>(static_cast<const float*>(src) + i);
-    const f32x4 b = *reinterpret_cast<const f32x4*>(static_cast<const float*>(src) + i + 4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      v[e] = a[e];
-      v[4 + e] = b[e];
-    }
-  } else {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(src) + i);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint16_t lo = static_cast<uint16_t>(w[e] & 0xFFFF), hi = static_cast<uint16_t>(w[e] >> 16);
-      v[2 * e] = DT == DT_BF16 ? bf2f(lo) : h2f(lo);
-      v[2 * e + 1] = DT == DT_BF16 ? bf2f(hi) : h2f(hi);
-    }
-  }
-}
-
 // x[s, :] = table[tokens[s], :] as fp32; one workgroup per token (tokens already range-checked).
 template <int DT>
 __global__ __launch_bounds__(256) void embed_gather_kernel(const int32_t* tokens, const void* table,

@@ -112,6 +112,95 @@ def layer_prefill(spec, weights, x, positions, ds_rows=None, ds=None, out=None, 
     return out
 
 
+def kv_cache_alloc(spec, capacity, device="cuda"):
+    """(k_cache, v_cache): zeroed [n_kv_heads, capacity, head_dim] tensors of spec's act dtype."""
+    shape = (spec.n_kv_heads, int(capacity), spec.head_dim)
+    dt = TORCH_DTYPES[spec.act_dtype]
+    return torch.zeros(shape, dtype=dt, device=device), torch.zeros(shape, dtype=dt, device=device)
+
+
+def kv_cache_write(k, v, k_cache, v_cache, row0=0):
+    """kv_cache_write: rows of k, v [n, n_kv_heads, head_dim] (rows may be strided views of a
+    wider row, heads contiguous) into cache rows row0.. of k_cache / v_cache [nkv, cap, hd]."""
+    lib = _lib.load()
+    n, nkv, hd = k.shape
+    for t in (k, v):
+        if t.stride(2) != 1 or t.stride(1) != hd:
+            raise ValueError("heads of a row must be contiguous")
+    if v.dtype != k.dtype:
+        raise TypeError("k and v must have one dtype")
+    _lib.check(lib.kv_cache_write(ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()), int(k.stride(0)),
+                                  int(v.stride(0)), int(n), int(nkv), int(hd), _dt(k), _ptr(k_cache),
+                                  _ptr(v_cache), _dt(k_cache), int(k_cache.shape[1]), int(row0), _stream()))
+
+
+def layer_prefill_kv(spec, weights, x, positions, k_cache, v_cache, ds_rows=None, ds=None, out=None,
+                     workspace=None):
+    """qwen3_layer_prefill_kv: layer_prefill that also writes k', v of every position into rows
+    0..S-1 of the caches ([n_kv_heads, capacity, head_dim], spec's act dtype)."""
+    lib = _lib.load()
+    cfg = _cfg(spec)
+    s = x.shape[0]
+    if out is None:
+        out = torch.empty_like(x)
+    need = int(lib.qwen3_layer_workspace_bytes(ctypes.byref(cfg), int(s)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    w = _lib.LayerWeights(*[_ptr(weights[n]) for n in WEIGHT_NAMES])
+    n_ds = 0 if ds_rows is None else int(ds_rows.numel())
+    _lib.check(lib.qwen3_layer_prefill_kv(
+        ctypes.byref(cfg), ctypes.byref(w), _ptr(x), _ptr(out), int(s), _ptr(positions),
+        _ptr(ds_rows), n_ds, _ptr(ds), _ptr(k_cache), _ptr(v_cache), int(k_cache.shape[1]),
+        _ptr(workspace), int(workspace.numel()), _stream()))
+    return out
+
+
+def decode_attention_workspace_bytes(n_heads, n_kv_heads, head_dim, length):
+    return int(_lib.load().gqa_decode_attention_workspace_bytes(int(n_heads), int(n_kv_heads), int(head_dim),
+                                                                int(length)))
+
+
+def gqa_decode_attention(q, k_cache, v_cache, length, scale=None, out=None, workspace=None):
+    """gqa_decode_attention: q [n_heads, head_dim] float32 over cache rows 0..length-1;
+    returns out [n_heads, head_dim] float32."""
+    lib = _lib.load()
+    nh, hd = q.shape
+    nkv, cap = k_cache.shape[0], k_cache.shape[1]
+    if scale is None:
+        scale = hd ** -0.5
+    if out is None:
+        out = torch.empty_like(q)
+    need = decode_attention_workspace_bytes(nh, nkv, hd, length)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _lib.check(lib.gqa_decode_attention(_ptr(q), _ptr(k_cache), _ptr(v_cache), int(cap), int(length), int(nh),
+                                        int(nkv), int(hd), float(scale), _dt(k_cache), _ptr(out), _ptr(workspace),
+                                        int(workspace.numel()), _stream()))
+    return out
+
+
+def layer_decode_workspace_bytes(spec, capacity):
+    return int(_lib.load().qwen3_layer_decode_workspace_bytes(ctypes.byref(_cfg(spec)), int(capacity)))
+
+
+def layer_decode(spec, weights, x, position, k_cache, v_cache, length, out=None, workspace=None):
+    """qwen3_layer_decode: one new token x [H] float32 at `position` (int32 [3] on the GPU) over
+    cache rows 0..length-1; appends its k', v at row `length`; returns out [H] float32."""
+    lib = _lib.load()
+    cfg = _cfg(spec)
+    cap = k_cache.shape[1]
+    if out is None:
+        out = torch.empty_like(x)
+    need = int(lib.qwen3_layer_decode_workspace_bytes(ctypes.byref(cfg), int(cap)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    w = _lib.LayerWeights(*[_ptr(weights[n]) for n in WEIGHT_NAMES])
+    _lib.check(lib.qwen3_layer_decode(ctypes.byref(cfg), ctypes.byref(w), _ptr(x), _ptr(out), _ptr(position),
+                                      _ptr(k_cache), _ptr(v_cache), int(cap), int(length), _ptr(workspace),
+                                      int(workspace.numel()), _stream()))
+    return out
+
+
 def _model_cfg(spec, n_layers, vocab, n_deepstack_layers):
     m = _lib.ModelCfg()
     m.layer = _cfg(spec)
