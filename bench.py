@@ -34,6 +34,8 @@ def parse():
     ap.add_argument("--no-model", action="store_true",
                     help="skip the whole-model (embedding + stack + LM head) measurement")
     ap.add_argument("--vocab", type=int, default=151936)
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the KV-cache decode measurement")
     ap.add_argument("--no-bidirectional", action="store_true",
                     help="skip the bidirectional-attention (vision encoder shape) measurement")
     ap.add_argument("--copy-calib", action="store_true",
@@ -189,6 +191,92 @@ def bidirectional_extra():
     return res
 
 
+def decode_extra(cfg, layers, x0, pos, n_tokens=16):
+    """Decode after a full prompt: every layer's cache is filled by a prefill of the S-token
+    prompt through the stack, then n_tokens new tokens go through all layers one at a time
+    (positions S, S+1, ...). Also decode attention alone over 4096 and 32768 cached keys."""
+    import torch
+
+    import transformer_lm_prefill_amd as q3
+    dev = torch.device("cuda:0")
+    S, L = cfg.seq_len, len(layers)
+    spec = q3.LayerSpec.of(cfg)
+    cap = S + n_tokens
+    caches = [q3.kv_cache_alloc(spec, cap) for _ in range(L)]
+    h = torch.empty_like(x0)
+    ws = torch.empty(q3.layer_workspace_bytes(spec, S), dtype=torch.uint8, device=dev)
+    q3.layer_prefill_kv(spec, layers[0], x0, pos, *caches[0], out=h, workspace=ws)
+    for li in range(1, L):
+        q3.layer_prefill_kv(spec, layers[li], h, pos, *caches[li], out=h, workspace=ws)
+    del ws
+    dws = torch.empty(q3.layer_decode_workspace_bytes(spec, cap), dtype=torch.uint8, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(99)
+    xs = torch.randn(n_tokens, cfg.hidden, device=dev, generator=g)
+    tpos = torch.arange(S, S + n_tokens, dtype=torch.int32, device=dev).repeat(3, 1).t().contiguous()
+    y = torch.empty(cfg.hidden, device=dev)
+
+    def token(i):
+        y.copy_(xs[i])
+        for li in range(L):
+            q3.layer_decode(spec, layers[li], y, tpos[i], *caches[li], S + i, out=y, workspace=dws)
+
+    token(0)   # warm-up (rewrites row S of every cache with the same values later)
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for i in range(n_tokens):
+        token(i)
+    torch.cuda.synchronize()
+    ms_tok = (time.perf_counter() - t) * 1e3 / n_tokens
+    q3.timing_enable(True)
+    for i in range(n_tokens):
+        token(i)
+    torch.cuda.synchronize()
+    kt = q3.timing_collect()
+    q3.timing_enable(False)
+    H, F, qd, kvd = cfg.hidden, cfg.ffn, cfg.n_heads * cfg.head_dim, cfg.n_kv_heads * cfg.head_dim
+    wbytes = {"gemv_qkv": (qd + 2 * kvd) * H * 2, "gemv_o_resid": H * qd * 2,
+              "gemv_gate_up_swiglu": 2 * F * H * 2, "gemv_down_resid": H * F * 2}
+    kern = {}
+    for k, (n, tot) in kt.items():
+        avg = tot / n
+        e = {"avg_ms": round(avg, 4)}
+        if k in wbytes:
+            e["GB_per_s"] = round(wbytes[k] / (avg * 1e-3) / 1e9, 1)
+            e["frac_of_hbm_peak"] = round(wbytes[k] / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+        kern[k] = e
+    layer_bytes = sum(wbytes.values()) + 2 * (S + n_tokens // 2) * kvd * 2
+    res = {"workload": f"{cfg.name}: {L} layers, {n_tokens} tokens decoded after a {S}-token prompt, "
+                       f"fp16 cache", "ms_per_token": round(ms_tok, 4),
+           "tokens_per_s": round(1e3 / ms_tok, 1), "ms_per_token_layer": round(ms_tok / L, 4),
+           "weight_and_cache_GB_per_s": round(layer_bytes * L / (ms_tok * 1e-3) / 1e9, 1),
+           "kernels": kern}
+    # decode attention alone at the 8B head layout
+    attn = {}
+    for length in (4096, 32768):
+        kc = torch.randn(cfg.n_kv_heads, length, cfg.head_dim, device=dev, generator=g).to(torch.float16)
+        vc = torch.randn(cfg.n_kv_heads, length, cfg.head_dim, device=dev, generator=g).to(torch.float16)
+        q = torch.randn(cfg.n_heads, cfg.head_dim, device=dev, generator=g)
+        wsa = torch.empty(q3.decode_attention_workspace_bytes(cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, length),
+                          dtype=torch.uint8, device=dev)
+        out = torch.empty_like(q)
+        q3.gqa_decode_attention(q, kc, vc, length, out=out, workspace=wsa)
+        torch.cuda.synchronize()
+        q3.timing_enable(True)
+        for _ in range(20):
+            q3.gqa_decode_attention(q, kc, vc, length, out=out, workspace=wsa)
+        torch.cuda.synchronize()
+        kt = q3.timing_collect()
+        q3.timing_enable(False)
+        ms = kt["decode_attention"][1] / kt["decode_attention"][0]
+        b = 2 * length * cfg.n_kv_heads * cfg.head_dim * 2
+        attn[f"len_{length}"] = {"avg_ms": round(ms, 4), "GB_per_s": round(b / (ms * 1e-3) / 1e9, 1),
+                                 "frac_of_hbm_peak": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del kc, vc
+    res["decode_attention"] = attn
+    return res
+
+
 def main():
     args = parse()
     if args.copy_calib:
@@ -287,6 +375,7 @@ def main():
 
     model = None if args.no_model else model_prefill_extra(cfg, layers, pos, stream, args.vocab)
     bidir = None if args.no_bidirectional else bidirectional_extra()
+    decode = None if args.no_decode else decode_extra(cfg, layers, x0, pos)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -320,6 +409,7 @@ def main():
         "cpu_baseline": cpu,
         "model_prefill_logits_last": model,
         "bidirectional_attention": bidir,
+        "decode": decode,
     }
     print(json.dumps(out))
 

@@ -240,21 +240,40 @@ __global__ __launch_bounds__(256) void decode_attn_partial_kernel(DecodeAttnPara
 }
 
 // out[h, d] = sum_s 2^(m_s - M) o_s[d] / sum_s 2^(m_s - M) l_s, M = max_s m_s; one workgroup
-// per query head, one thread per element.
+// per query head: the split weights are formed once in LDS, then thread d sums its column.
+constexpr int kDecMaxSplits = 512;
+
+__device__ __forceinline__ float block128_reduce(float v, bool is_max, float* red) {
+  v = is_max ? wave_max(v) : wave_sum(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const float r = is_max ? fmaxf(red[0], red[1]) : red[0] + red[1];
+  __syncthreads();
+  return r;
+}
+
 __global__ __launch_bounds__(128) void decode_attn_combine_kernel(const float* part_o, const float* part_ml,
                                                                   int nsplit, int hd, float* out) {
-  const int h = blockIdx.x, d = threadIdx.x;
-  if (d >= hd) return;
+  __shared__ float wsh[kDecMaxSplits];
+  __shared__ float red[2];
+  const int h = blockIdx.x, tid = threadIdx.x;
   const float* ml = part_ml + static_cast<int64_t>(h) * nsplit * 2;
   float mx = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, ml[2 * s]);
-  float acc = 0.f, l = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
+  for (int s = tid; s < nsplit; s += 128) mx = fmaxf(mx, ml[2 * s]);
+  mx = block128_reduce(mx, true, red);
+  float l = 0.f;
+  for (int s = tid; s < nsplit; s += 128) {
     const float w = fast_exp2(ml[2 * s] - mx);
+    wsh[s] = w;
     l = fmaf(w, ml[2 * s + 1], l);
-    acc = fmaf(w, part_o[(static_cast<int64_t>(h) * nsplit + s) * hd + d], acc);
   }
-  out[static_cast<int64_t>(h) * hd + d] = acc / l;
+  l = block128_reduce(l, false, red);   // its barriers also publish wsh
+  if (tid >= hd) return;
+  const float* po = part_o + static_cast<int64_t>(h) * nsplit * hd + tid;
+  float acc = 0.f;
+#pragma unroll 8
+  for (int s = 0; s < nsplit; ++s) acc = fmaf(wsh[s], po[static_cast<int64_t>(s) * hd], acc);
+  out[static_cast<int64_t>(h) * hd + tid] = acc / l;
 }
 
 template <int CDT>
@@ -267,7 +286,8 @@ static hipError_t decode_partial_hd(const DecodeAttnParams& p, int hd, dim3 grid
 
 hipError_t launch_decode_attention(const DecodeAttnParams& p, int hd, int cache_dt, float* out, hipStream_t s) {
   if (p.len < 1 || p.nkv < 1 || p.nh % p.nkv != 0 || p.nh / p.nkv > kDecMaxGroup) return hipErrorInvalidValue;
-  if (p.nsplit != decode_num_splits(p.len, p.nkv) || p.tiles_per_split != decode_tiles_per_split(p.len, p.nkv))
+  if (p.nsplit != decode_num_splits(p.len, p.nkv) || p.tiles_per_split != decode_tiles_per_split(p.len, p.nkv) ||
+      p.nsplit > kDecMaxSplits || hd > 128)
     return hipErrorInvalidValue;
   const dim3 grid(p.nsplit, p.nkv);
   hipError_t e;
@@ -282,13 +302,52 @@ hipError_t launch_decode_attention(const DecodeAttnParams& p, int hd, int cache_
 
 // ---- decode projections ---------------------------------------------------------------------
 // Wave = 4 output rows (SwiGLU: 4 gate rows and the matching 4 up rows); lane l covers the
-// 8-element chunks l, l + 64, ... of each row; fp32 accumulation, then a wave reduction.
+// 8-element chunks l, l + 64, ... of each row; fp32 accumulation, then a wave reduction. The
+// weight loads of U chunks of every row are issued together before any arithmetic, so each
+// wave keeps 16 loads of 16 bytes in flight.
 constexpr int kGvRows = 4;
+
+// 8 consecutive weights as raw 16-byte words (two words for fp32).
+template <int DT>
+struct Raw8 {
+  u32x4 w[DT == DT_F32 ? 2 : 1];
+};
+
+template <int DT>
+__device__ __forceinline__ Raw8<DT> load_raw8(const char* row, int i) {
+  Raw8<DT> r;
+  constexpr int ES = DT == DT_F32 ? 4 : 2;
+#pragma unroll
+  for (int h = 0; h < (DT == DT_F32 ? 2 : 1); ++h)
+    r.w[h] = *reinterpret_cast<const u32x4*>(row + static_cast<int64_t>(i) * ES + 16 * h);
+  return r;
+}
+
+template <int DT>
+__device__ __forceinline__ float dot_raw8(const Raw8<DT>& r, const float (&x)[8], float acc) {
+  if (DT == DT_F32) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t word = r.w[e >> 2][e & 3];
+      acc = fmaf(__uint_as_float(word), x[e], acc);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t word = r.w[0][e];
+      const uint16_t lo = static_cast<uint16_t>(word & 0xFFFF), hi = static_cast<uint16_t>(word >> 16);
+      acc = fmaf(DT == DT_BF16 ? bf2f(lo) : h2f(lo), x[2 * e], acc);
+      acc = fmaf(DT == DT_BF16 ? bf2f(hi) : h2f(hi), x[2 * e + 1], acc);
+    }
+  }
+  return acc;
+}
 
 template <int DT, int EPI>
 __global__ __launch_bounds__(256) void gemv_epi_kernel(GemvParams p) {
   constexpr int ES = DT == DT_F32 ? 4 : 2;
   constexpr int NR = EPI == GV_SWIGLU ? 2 * kGvRows : kGvRows;
+  constexpr int U = (DT == DT_F32 ? 8 : 16) / NR;   // chunks per row loaded together
   const int lane = threadIdx.x & 63;
   const int r0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * kGvRows;
   if (r0 >= p.rows) return;
@@ -308,16 +367,24 @@ __global__ __launch_bounds__(256) void gemv_epi_kernel(GemvParams p) {
   float acc[NR];
 #pragma unroll
   for (int j = 0; j < NR; ++j) acc[j] = 0.f;
-  for (int i = lane * 8; i < p.K; i += 64 * 8) {
-    float xv[8];
-    load8<DT_F32>(p.x, i, xv);
+  for (int i0 = lane * 8; i0 < p.K; i0 += 64 * 8 * U) {
+    Raw8<DT> w[U][NR];
+    float xv[U][8];
 #pragma unroll
-    for (int j = 0; j < NR; ++j) {
-      float w[8];
-      load8<DT>(rowp[j], i, w);
+    for (int u = 0; u < U; ++u) {
+      const int i = min(i0 + u * 512, p.K - 8);   // chunks past the end repeat the last, weighted 0
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[j] = fmaf(w[e], xv[e], acc[j]);
+      for (int j = 0; j < NR; ++j) w[u][j] = load_raw8<DT>(rowp[j], i);
+      load8<DT_F32>(p.x, i, xv[u]);
+      if (i0 + u * 512 >= p.K) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xv[u][e] = 0.f;
+      }
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int j = 0; j < NR; ++j) acc[j] = dot_raw8<DT>(w[u][j], xv[u], acc[j]);
   }
 #pragma unroll
   for (int j = 0; j < NR; ++j) acc[j] = wave_sum(acc[j]);
