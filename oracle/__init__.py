@@ -24,7 +24,10 @@ Sources (web pages, cited by title and item):
   * cortiq-engine 0.8.51, ``onevision2.rs``: three-axis vision rope tables, the
     adjacent-lane rotation and bidirectional ``attend`` (vision.py).
   * hf2q 0.1.1, ``qwen3vl_text/forward.rs``: the module doc's note on the deferred KV
-    cache (decode.py: the cache a prefill leaves, one decode step).
+    cache (decode.py: the cache a prefill leaves, one decode step); the Q4_0 FFN weights
+    (quant.py).
+  * cortiq-engine 0.8.21, ``qwen3te.rs``: ``q8_exact_matmat`` (quant.py: int8 rows with a
+    row scale).
 
 Parity pins: every function here is pinned by the ``-m "not gpu"`` tests
 against closed forms, invariants, textbook formulations and brute force; no
@@ -46,6 +49,7 @@ from .qwen3_layer import (  # noqa: F401
     swiglu_ffn,
 )
 from .decode import decode_attention, layer_decode, prefill_kv  # noqa: F401,E402
+from .quant import dequant, dequant_q4_0, dequant_q8_row  # noqa: F401,E402
 from .model import embed_tokens, lm_head_last, model_prefill_logits_last  # noqa: F401,E402
 from .vision import (  # noqa: F401,E402
     bidirectional_attention,

@@ -9,12 +9,15 @@ a host numpy array.
 
 from .configs import CONFIGS, LayerConfig, get_config  # noqa: F401
 from .gen import (  # noqa: F401
+    NORM_NAMES,
+    PROJ_NAMES,
     WEIGHT_NAMES,
     make_deepstack,
     make_deepstack_layers,
     make_layer_weights,
     make_model_weights,
     make_positions,
+    make_quant_layer_weights,
     make_tokens,
     make_x,
     round_to_bf16,

@@ -60,8 +60,9 @@ def normal(seed, name, shape, mean=0.0, std=1.0, dtype="bf16", threads=8):
     return out.reshape(shape)
 
 
-def make_layer_weights(cfg, layer=0):
-    """The eleven weight tensors of decoder layer `layer`, torch nn.Linear layout [out, in].
+def make_layer_weights(cfg, layer=0, names=WEIGHT_NAMES):
+    """The weight tensors `names` (default all eleven) of decoder layer `layer`, torch
+    nn.Linear layout [out, in].
 
     Projection weights ~ N(0, 0.02), norm weights ~ 1 + N(0, 0.1); no biases.
     """
@@ -72,7 +73,7 @@ def make_layer_weights(cfg, layer=0):
         "w_gate": (f, h), "w_up": (f, h), "w_down": (h, f),
     }
     w = {}
-    for name in WEIGHT_NAMES:
+    for name in names:
         is_norm = name.endswith("norm")
         w[name] = normal(cfg.seed, f"L{layer}.{name}", shapes[name],
                          mean=1.0 if is_norm else 0.0, std=0.1 if is_norm else 0.02,
@@ -151,3 +152,59 @@ def make_deepstack_layers(cfg, n_layers):
     slabs = [normal(cfg.seed, f"deepstack.L{li}", (len(rows), cfg.hidden), std=cfg.deepstack_std,
                     dtype=cfg.dtype) for li in range(n_layers)]
     return rows, slabs
+
+
+PROJ_NAMES = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
+NORM_NAMES = ("attn_norm", "q_norm", "k_norm", "ffn_norm")
+
+
+def _uniform_block(seed, key, n):
+    return np.random.Generator(np.random.SFC64(np.random.SeedSequence([seed, key, 1 << 20])))
+
+
+def make_q4_0_weight(seed, name, rows, cols, std=0.02):
+    """Q4_0 blocks of a [rows, cols] matrix as uint8 [rows, cols / 32, 18]: per block a
+    binary16 scale drawn as std / 4.6 * U(0.75, 1.25) (4.6 is about the spread of a uniform
+    4-bit code around 8), stored little-endian, then 16 bytes of uniform random codes."""
+    g = _uniform_block(seed, _key(name), 0)
+    nb = cols // 32
+    blocks = g.integers(0, 256, size=(rows, nb, 18), dtype=np.uint8)
+    d = (std / 4.6 * g.uniform(0.75, 1.25, size=(rows, nb))).astype("<f2")
+    blocks[:, :, 0:2] = d[..., None].view(np.uint8)
+    return blocks
+
+
+def make_q8_row_weight(seed, name, rows, cols, std=0.02):
+    """(codes int8 [rows, cols] uniform in [-127, 127], row scales float32 [rows] drawn as
+    std / 73.6 * U(0.75, 1.25); 73.6 is about the spread of such a code)."""
+    g = _uniform_block(seed, _key(name), 0)
+    q = g.integers(-127, 128, size=(rows, cols), dtype=np.int16).astype(np.int8)
+    rs = (std / 73.6 * g.uniform(0.75, 1.25, size=rows)).astype(np.float32)
+    return q, rs
+
+
+def make_quant_layer_weights(cfg, layer=0, formats=None):
+    """(norms, projections) of decoder layer `layer` with quantized projections: norms as in
+    make_layer_weights; projections[name] = (format, data, row_scale) with format "q4_0"
+    (data = blocks), "q8_row" (data = codes, row_scale) or "dense" (data = the matrix of
+    make_layer_weights). `formats` maps projection names to formats (default all "q4_0")."""
+    formats = formats or {}
+    h, f = cfg.hidden, cfg.ffn
+    shapes = {"wq": (cfg.q_dim, h), "wk": (cfg.kv_dim, h), "wv": (cfg.kv_dim, h), "wo": (h, cfg.q_dim),
+              "w_gate": (f, h), "w_up": (f, h), "w_down": (h, f)}
+    norms = make_layer_weights(cfg, layer, NORM_NAMES)
+    proj = {}
+    for name in PROJ_NAMES:
+        fmt = formats.get(name, "q4_0")
+        rows, cols = shapes[name]
+        tag = f"L{layer}.{name}.{fmt}"
+        if fmt == "q4_0":
+            proj[name] = (fmt, make_q4_0_weight(cfg.seed, tag, rows, cols), None)
+        elif fmt == "q8_row":
+            q, rs = make_q8_row_weight(cfg.seed, tag, rows, cols)
+            proj[name] = (fmt, q, rs)
+        elif fmt == "dense":
+            proj[name] = (fmt, make_layer_weights(cfg, layer, (name,))[name], None)
+        else:
+            raise ValueError(f"unknown weight format {fmt}")
+    return norms, proj

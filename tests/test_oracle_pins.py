@@ -637,6 +637,92 @@ def test_decode_steps_reproduce_the_prefill_rows():
     assert np.allclose(y0, full[0], rtol=1e-11, atol=1e-12)
 
 
+# ---------------------------------------------------------------- quantized weights (f4)
+
+def _golden_q4_0(name):
+    blocks, weights = [], []
+    with open(os.path.join(os.path.dirname(__file__), "golden", name)) as f:
+        for line in f:
+            if line.startswith("bytes"):
+                blocks.append([int(t, 16) for t in line.split()[1:]])
+            elif line.startswith("weights"):
+                weights.append([float(t) for t in line.split()[1:]])
+    return np.array(blocks, dtype=np.uint8), np.array(weights)
+
+
+def test_q4_0_matches_hand_worked_blocks():
+    blocks, want = _golden_q4_0("q4_0_two_blocks.txt")
+    assert blocks.shape == (2, 18)
+    got = oracle.dequant_q4_0(blocks.reshape(-1), 1, 64)
+    assert np.array_equal(got.reshape(2, 32), want)
+
+
+def _q4_0_brute(blocks, rows, cols):
+    import struct
+    raw = bytes(np.asarray(blocks, dtype=np.uint8).reshape(-1))
+    out = [[0.0] * cols for _ in range(rows)]
+    for o in range(rows):
+        for b in range(cols // 32):
+            off = (o * (cols // 32) + b) * 18
+            d = struct.unpack("<e", raw[off:off + 2])[0]
+            for j in range(16):
+                byte = raw[off + 2 + j]
+                out[o][32 * b + j] = d * ((byte & 15) - 8)
+                out[o][32 * b + j + 16] = d * ((byte >> 4) - 8)
+    return np.array(out)
+
+
+def test_q4_0_against_byte_loops_and_invariants():
+    r = _rng(110)
+    rows, cols = 3, 96
+    blocks = r.integers(0, 256, size=(rows, cols // 32, 18), dtype=np.uint8)
+    blocks[:, :, 0:2] = np.array(r.uniform(-2, 2, (rows, cols // 32)), dtype="<f2")[..., None].view(np.uint8)
+    w = oracle.dequant_q4_0(blocks, rows, cols)
+    assert np.array_equal(w, _q4_0_brute(blocks, rows, cols))
+    # every code 8 is the zero matrix; the scale is linear
+    z = blocks.copy()
+    z[:, :, 2:] = 0x88
+    assert np.array_equal(oracle.dequant_q4_0(z, rows, cols), np.zeros((rows, cols)))
+    half = blocks.copy()
+    half[:, :, 0:2] = (blocks[:, :, 0:2].copy().view("<f2") / 2).astype("<f2").view(np.uint8)
+    assert np.array_equal(oracle.dequant_q4_0(half, rows, cols), w / 2)
+    with pytest.raises(ValueError):
+        oracle.dequant_q4_0(blocks, rows, 100)
+
+
+def test_q4_0_round_trip_of_a_simple_quantizer():
+    # quantize with d = max|w| / 7 and codes round(w / d) + 8 (clipped), then dequantize:
+    # every weight comes back within half a step (plus the scale's binary16 rounding)
+    r = _rng(111)
+    rows, cols = 4, 64
+    w = 0.02 * r.standard_normal((rows, cols))
+    blocks = np.zeros((rows, cols // 32, 18), dtype=np.uint8)
+    for o in range(rows):
+        for b in range(cols // 32):
+            seg = w[o, 32 * b:32 * b + 32]
+            d = np.float16(np.abs(seg).max() / 7)
+            codes = np.clip(np.rint(seg / np.float64(d)) + 8, 0, 15).astype(np.uint8)
+            blocks[o, b, 0:2] = np.array([d], dtype="<f2").view(np.uint8)
+            blocks[o, b, 2:] = codes[:16] | (codes[16:] << 4)
+    back = oracle.dequant_q4_0(blocks, rows, cols)
+    d_all = np.repeat(blocks[:, :, 0:2].copy().view("<f2")[:, :, 0].astype(np.float64), 32, axis=1)
+    assert np.all(np.abs(back - w) <= 0.5 * d_all + 1e-3 * np.abs(w) + 1e-12)
+
+
+def test_q8_row_against_loops_and_invariants():
+    r = _rng(112)
+    rows, cols = 5, 48
+    q = r.integers(-128, 128, size=(rows, cols)).astype(np.int8)
+    rs = r.uniform(0.001, 0.01, rows).astype(np.float32)
+    w = oracle.dequant_q8_row(q, rs)
+    want = [[float(rs[o]) * int(q[o, j]) for j in range(cols)] for o in range(rows)]
+    assert np.array_equal(w, np.array(want))
+    assert np.array_equal(oracle.dequant_q8_row(q, np.ones(rows)), q.astype(np.float64))
+    # the product with the dequantized rows equals the row scale times the integer dot product
+    x = r.standard_normal((3, cols))
+    assert np.allclose(oracle.linear(x, w), (x @ q.T.astype(np.float64)) * rs[None, :], rtol=1e-13, atol=1e-15)
+
+
 # ---------------------------------------------------------------- generator
 
 def test_generator_deterministic_and_distributions():
@@ -662,6 +748,22 @@ def test_model_generators_deterministic():
     e2, _, h2 = synth.make_model_weights(cfg, 50, tied=True)
     assert np.array_equal(e1, e2) and h2 is None and h1.shape == e1.shape == (50, cfg.hidden)
     assert not np.array_equal(e1, h1)
+
+
+def test_quant_generators_deterministic_and_scaled():
+    cfg = synth.get_config("tiny_f32")
+    n1, p1 = synth.make_quant_layer_weights(cfg, 0, {"wo": "q8_row", "wk": "dense"})
+    n2, p2 = synth.make_quant_layer_weights(cfg, 0, {"wo": "q8_row", "wk": "dense"})
+    assert set(p1) == set(synth.PROJ_NAMES) and set(n1) == set(synth.NORM_NAMES)
+    for k in p1:
+        assert p1[k][0] == p2[k][0] and np.array_equal(p1[k][1], p2[k][1])
+    fmt, blocks, _ = p1["w_gate"]
+    assert fmt == "q4_0" and blocks.shape == (cfg.ffn, cfg.hidden // 32, 18) and blocks.dtype == np.uint8
+    w = oracle.dequant_q4_0(blocks, cfg.ffn, cfg.hidden)
+    assert abs(w.std() - 0.02) < 0.002
+    q, rs = p1["wo"][1], p1["wo"][2]
+    assert q.dtype == np.int8 and q.min() >= -127 and rs.dtype == np.float32
+    assert np.array_equal(p1["wk"][1], synth.make_layer_weights(cfg, 0, ("wk",))["wk"])
 
 
 def test_bf16_rounding_ties_to_even():
