@@ -339,6 +339,71 @@ int qwen3_layer_decode(const qwen3_layer_cfg *cfg, const qwen3_layer_weights *w,
                        void *stream);
 size_t qwen3_layer_decode_workspace_bytes(const qwen3_layer_cfg *cfg, int32_t capacity);
 
+/* ---- Weight-only quantized projections ---------------------------------------------------------
+ *
+ * hf2q 0.1.1, qwen3vl_text/forward.rs, the dense FFN step: the converted Qwen3-VL checkpoints hold
+ * their projections as GGML Q4_0 tensors. The page names the type only; the layout read here is
+ * GGML's published Q4_0 block: 32 consecutive weights of a row per 18-byte block, a little-endian
+ * binary16 scale d then 16 bytes of codes, byte j holding weight j's code in its low nibble and
+ * weight j + 16's in its high nibble; weight = d * (code - 8). A row of K weights is K/32 blocks
+ * back to back, rows back to back.
+ * cortiq-engine 0.8.21, qwen3te.rs, `q8_exact_matmat`: int8 rows with a per-row scale, weight[o, j]
+ * = row_scale[o] * q[o, j], activations not quantized.
+ *
+ * Projections with quantized weights compute x W^T with the dequantized W. In a prefill each
+ * quantized matrix is expanded to the operand type (f16 or bf16, one rounding per weight: d *
+ * (code - 8) and row_scale * q are rounded to nearest even) in the workspace just before its
+ * product; a decode step reads the quantized bytes directly and keeps the activations in fp32.
+ * Norm weights stay in cfg.wdtype; dense projections use cfg.wdtype as in qwen3_layer_weights.
+ */
+typedef enum { QWEN3_W_DENSE = 0, QWEN3_W_Q4_0 = 1, QWEN3_W_Q8_ROW = 2 } qwen3_wformat;
+
+typedef struct {
+  qwen3_wformat format;
+  const void *data;       /* DENSE: [rows, cols] of cfg.wdtype (16-byte aligned); Q4_0: rows*cols/32
+                             blocks of 18 bytes (4-byte aligned); Q8_ROW: int8 [rows, cols] (16-byte aligned) */
+  const float *row_scale; /* Q8_ROW: fp32 [rows]; otherwise ignored                                        */
+} qwen3_qmatrix;
+
+typedef struct {
+  const void *attn_norm;   /* [H] of cfg.wdtype */
+  qwen3_qmatrix wq;        /* [nh*hd, H]        */
+  qwen3_qmatrix wk;        /* [nkv*hd, H]       */
+  qwen3_qmatrix wv;        /* [nkv*hd, H]       */
+  const void *q_norm;      /* [hd]              */
+  const void *k_norm;      /* [hd]              */
+  qwen3_qmatrix wo;        /* [H, nh*hd]        */
+  const void *ffn_norm;    /* [H]               */
+  qwen3_qmatrix w_gate;    /* [F, H]            */
+  qwen3_qmatrix w_up;      /* [F, H]            */
+  qwen3_qmatrix w_down;    /* [H, F]            */
+} qwen3_layer_qweights;
+
+/* out [rows, cols] of out_dtype (f16 or bf16) = the dequantized matrix m (Q4_0 or Q8_ROW);
+ * cols a multiple of 64. */
+int dequantize_matrix(const qwen3_qmatrix *m, int32_t rows, int32_t cols, qwen3_dtype out_dtype, void *out,
+                      void *stream);
+
+/* Workspace of qwen3_layer_prefill_quant: the layer workspace plus room for the largest product
+ * group expanded to 16 bits. */
+size_t qwen3_layer_quant_workspace_bytes(const qwen3_layer_cfg *cfg, int32_t seq_len);
+
+/* qwen3_layer_prefill (and, with non-NULL caches, qwen3_layer_prefill_kv) with per-projection
+ * formats. Rules: act_dtype f16 or bf16 when any projection is quantized; wq, wk, wv all dense or
+ * all quantized (Q4_0 and Q8_ROW may be mixed); w_gate and w_up share one format. k_cache and
+ * v_cache are both NULL or both given (then capacity >= seq_len). */
+int qwen3_layer_prefill_quant(const qwen3_layer_cfg *cfg, const qwen3_layer_qweights *w, const void *x_in,
+                              void *x_out, int32_t seq_len, const int32_t *positions, const int32_t *ds_rows,
+                              int32_t n_ds, const void *ds, void *k_cache, void *v_cache, int32_t capacity,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/* qwen3_layer_decode with per-projection formats (same rules); the workspace is
+ * qwen3_layer_decode_workspace_bytes(cfg, capacity). */
+int qwen3_layer_decode_quant(const qwen3_layer_cfg *cfg, const qwen3_layer_qweights *w, const float *x_in,
+                             float *x_out, const int32_t *position, void *k_cache, void *v_cache,
+                             int32_t capacity, int32_t len, void *workspace, size_t workspace_bytes,
+                             void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -287,3 +287,48 @@ def test_layer_decode_and_prefill_kv_argument_checks(lib):
                                       ctypes.c_void_p(0x2000), 15, ws, ws_p, None) == 1     # capacity < S
     assert lib.qwen3_layer_prefill_kv(ctypes.byref(c), ctypes.byref(w), FAKE, FAKE, 16, FAKE, None, 0, None, None,
                                       ctypes.c_void_p(0x2000), 16, ws, ws_p, None) == 1
+
+
+# ---- quantized weights: every call below fails a host check before any launch
+
+def _qweights(fmt=1, data=FAKE, rs=None, **over):
+    m = {n: L.QMatrix(fmt, data, rs) for n in ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")}
+    for k, v in over.items():
+        m[k] = v
+    return L.LayerQWeights(attn_norm=FAKE, q_norm=FAKE, k_norm=FAKE, ffn_norm=FAKE, **m)
+
+
+def test_quant_weight_rules(lib):
+    c = _cfg(act_dtype=2)
+    ws = ctypes.c_void_p(0x100000)
+    need = lib.qwen3_layer_quant_workspace_bytes(ctypes.byref(c), 16)
+    assert need > lib.qwen3_layer_workspace_bytes(ctypes.byref(c), 16)
+
+    def call(w, ws_bytes=need, cfg=c):
+        return lib.qwen3_layer_prefill_quant(ctypes.byref(cfg), ctypes.byref(w), FAKE, FAKE, 16, FAKE, None, 0, None,
+                                             None, None, 0, ws, ws_bytes, None)
+    assert call(_qweights(fmt=7)) == 1 and "qwen3_wformat" in lib.qwen3_last_error().decode()
+    assert call(_qweights(wk=L.QMatrix(0, FAKE, None))) == 2                  # dense wk with quantized wq
+    assert "all dense or all quantized" in lib.qwen3_last_error().decode()
+    assert call(_qweights(w_up=L.QMatrix(2, FAKE, FAKE))) == 2                # gate Q4_0, up q8
+    assert call(_qweights(fmt=2, rs=None)) == 1 and "row_scale" in lib.qwen3_last_error().decode()
+    assert call(_qweights(data=ctypes.c_void_p(0x1002))) == 1                 # Q4_0 needs 4-byte alignment
+    assert call(_qweights(fmt=2, data=ctypes.c_void_p(0x1004), rs=FAKE)) == 1  # int8 rows need 16 bytes
+    assert call(_qweights(), need - 256) == 3
+    assert call(_qweights(), cfg=_cfg(wdtype=0, act_dtype=0, head_dim=64, sections=(12, 10, 10))) == 2
+    assert "16-bit operands" in lib.qwen3_last_error().decode()
+    # caches must come in pairs
+    assert lib.qwen3_layer_prefill_quant(ctypes.byref(c), ctypes.byref(_qweights()), FAKE, FAKE, 16, FAKE, None, 0,
+                                         None, FAKE, None, 16, ws, need, None) == 1
+    dws = lib.qwen3_layer_decode_workspace_bytes(ctypes.byref(c), 64)
+    assert lib.qwen3_layer_decode_quant(ctypes.byref(c), ctypes.byref(_qweights(fmt=9)), FAKE, FAKE, FAKE, FAKE,
+                                        ctypes.c_void_p(0x2000), 64, 3, ws, dws, None) == 1
+
+
+def test_dequantize_matrix_checks(lib):
+    m = L.QMatrix(1, FAKE, None)
+    assert lib.dequantize_matrix(ctypes.byref(m), 4, 96, 2, FAKE, None) == 2      # cols % 64
+    assert lib.dequantize_matrix(ctypes.byref(m), 4, 128, 0, FAKE, None) == 2     # f32 output
+    assert lib.dequantize_matrix(ctypes.byref(L.QMatrix(0, FAKE, None)), 4, 128, 2, FAKE, None) == 1
+    assert lib.dequantize_matrix(ctypes.byref(m), 0, 128, 2, FAKE, None) == 1
+    assert lib.dequantize_matrix(ctypes.byref(L.QMatrix(2, FAKE, None)), 4, 128, 2, FAKE, None) == 1

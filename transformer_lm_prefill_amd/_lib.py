@@ -18,7 +18,8 @@ EXPORTS = ("qwen3_layer_workspace_bytes", "qwen3_layer_prefill", "qk_norm_mrope"
            "qwen3_model_workspace_bytes", "qwen3_model_prefill_logits_last",
            "kv_cache_write", "qwen3_layer_prefill_kv", "gqa_decode_attention",
            "gqa_decode_attention_workspace_bytes", "qwen3_layer_decode",
-           "qwen3_layer_decode_workspace_bytes",
+           "qwen3_layer_decode_workspace_bytes", "dequantize_matrix",
+           "qwen3_layer_quant_workspace_bytes", "qwen3_layer_prefill_quant", "qwen3_layer_decode_quant",
            "qwen3_last_error", "qwen3_timing_enable", "qwen3_timing_collect")
 
 
@@ -34,6 +35,19 @@ class LayerCfg(ctypes.Structure):
 class LayerWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("attn_norm", "wq", "wk", "wv", "q_norm", "k_norm",
                                                "wo", "ffn_norm", "w_gate", "w_up", "w_down")]
+
+
+class QMatrix(ctypes.Structure):
+    _fields_ = [("format", ctypes.c_int), ("data", ctypes.c_void_p), ("row_scale", ctypes.c_void_p)]
+
+
+class LayerQWeights(ctypes.Structure):
+    _fields_ = [("attn_norm", ctypes.c_void_p), ("wq", QMatrix), ("wk", QMatrix), ("wv", QMatrix),
+                ("q_norm", ctypes.c_void_p), ("k_norm", ctypes.c_void_p), ("wo", QMatrix),
+                ("ffn_norm", ctypes.c_void_p), ("w_gate", QMatrix), ("w_up", QMatrix), ("w_down", QMatrix)]
+
+
+W_DENSE, W_Q4_0, W_Q8_ROW = 0, 1, 2
 
 
 class ModelCfg(ctypes.Structure):
@@ -114,6 +128,16 @@ def load():
     lib.qwen3_layer_decode.restype = ctypes.c_int
     lib.qwen3_layer_decode_workspace_bytes.argtypes = [ctypes.POINTER(LayerCfg), i32]
     lib.qwen3_layer_decode_workspace_bytes.restype = sz
+    lib.dequantize_matrix.argtypes = [ctypes.POINTER(QMatrix), i32, i32, ctypes.c_int, vp, vp]
+    lib.dequantize_matrix.restype = ctypes.c_int
+    lib.qwen3_layer_quant_workspace_bytes.argtypes = [ctypes.POINTER(LayerCfg), i32]
+    lib.qwen3_layer_quant_workspace_bytes.restype = sz
+    lib.qwen3_layer_prefill_quant.argtypes = [ctypes.POINTER(LayerCfg), ctypes.POINTER(LayerQWeights),
+                                              vp, vp, i32, vp, vp, i32, vp, vp, vp, i32, vp, sz, vp]
+    lib.qwen3_layer_prefill_quant.restype = ctypes.c_int
+    lib.qwen3_layer_decode_quant.argtypes = [ctypes.POINTER(LayerCfg), ctypes.POINTER(LayerQWeights),
+                                             vp, vp, vp, vp, vp, i32, i32, vp, sz, vp]
+    lib.qwen3_layer_decode_quant.restype = ctypes.c_int
     lib.qwen3_last_error.argtypes = []
     lib.qwen3_last_error.restype = ctypes.c_char_p
     lib.qwen3_timing_enable.argtypes = [ctypes.c_int]

@@ -17,7 +17,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqwen3_prefill.so")
 SOURCES = ["capi.hip", "norm_rope.hip", "gemm_mfma.hip", "attention_mfma.hip", "fp32_path.hip",
-           "model_head.hip", "vision_rope.hip", "decode.hip"]
+           "model_head.hip", "vision_rope.hip", "decode.hip",
+           "quant.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -7,6 +7,7 @@
 // shape the kernels do not run: there is no fallback path.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -245,6 +246,103 @@ int run_ffn(const void* x, const void* wg, const void* wu, const void* wd, const
   return run_gemm(R ? "gemm_down_resid" : "gemm_down", dn, epi, wdt, adt, s);
 }
 
+// ---- weights of one layer, dense or quantized ------------------------------------------------
+struct MatW {
+  int fmt;            // qwen3_wformat
+  const void* data;   // dense: cfg.wdtype matrix; Q4_0 blocks; int8 codes
+  const float* rs;    // q8 rows: row scales
+};
+struct LayerW {
+  const void *attn_norm, *q_norm, *k_norm, *ffn_norm;
+  MatW wq, wk, wv, wo, wg, wu, wd;
+};
+
+LayerW dense_layer(const qwen3_layer_weights* w) {
+  auto m = [](const void* d) { return MatW{QWEN3_W_DENSE, d, nullptr}; };
+  return LayerW{w->attn_norm, w->q_norm, w->k_norm, w->ffn_norm, m(w->wq), m(w->wk), m(w->wv), m(w->wo),
+                m(w->w_gate), m(w->w_up), m(w->w_down)};
+}
+
+LayerW quant_layer(const qwen3_layer_qweights* w) {
+  auto m = [](const qwen3_qmatrix& q) { return MatW{q.format, q.data, q.row_scale}; };
+  return LayerW{w->attn_norm, w->q_norm, w->k_norm, w->ffn_norm, m(w->wq), m(w->wk), m(w->wv), m(w->wo),
+                m(w->w_gate), m(w->w_up), m(w->w_down)};
+}
+
+int check_matrix(const MatW& m, const char* name) {
+  if (m.fmt != QWEN3_W_DENSE && m.fmt != QWEN3_W_Q4_0 && m.fmt != QWEN3_W_Q8_ROW)
+    return fail(QWEN3_ERR_INVALID_ARG, "weight %s: format %d is not a qwen3_wformat", name, m.fmt);
+  if (!m.data) return fail(QWEN3_ERR_INVALID_ARG, "weight %s is NULL", name);
+  const uintptr_t a = reinterpret_cast<uintptr_t>(m.data);
+  if (m.fmt == QWEN3_W_Q4_0) {
+    if (a % 4 != 0) return fail(QWEN3_ERR_INVALID_ARG, "weight %s: Q4_0 blocks must be 4-byte aligned", name);
+  } else if (a % 16 != 0) {
+    return fail(QWEN3_ERR_INVALID_ARG, "weight %s: tensor pointers must be 16-byte aligned", name);
+  }
+  if (m.fmt == QWEN3_W_Q8_ROW && (!m.rs || reinterpret_cast<uintptr_t>(m.rs) % 4 != 0))
+    return fail(QWEN3_ERR_INVALID_ARG, "weight %s: q8 rows need a 4-byte aligned row_scale", name);
+  return QWEN3_OK;
+}
+
+// Null and alignment checks of every weight; `quant` tells whether quantized formats are
+// allowed (they need 16-bit operands).
+int check_layer_w(const LayerW& w, const qwen3_layer_cfg* cfg, bool* any_quant) {
+  const void* norms[] = {w.attn_norm, w.q_norm, w.k_norm, w.ffn_norm};
+  const char* nn[] = {"attn_norm", "q_norm", "k_norm", "ffn_norm"};
+  for (int i = 0; i < 4; ++i) {
+    if (!norms[i]) return fail(QWEN3_ERR_INVALID_ARG, "weight %s is NULL", nn[i]);
+    if (misaligned16({norms[i]})) return fail(QWEN3_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  }
+  const MatW* ms[] = {&w.wq, &w.wk, &w.wv, &w.wo, &w.wg, &w.wu, &w.wd};
+  const char* mn[] = {"wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down"};
+  *any_quant = false;
+  for (int i = 0; i < 7; ++i) {
+    int st = check_matrix(*ms[i], mn[i]);
+    if (st) return st;
+    *any_quant = *any_quant || ms[i]->fmt != QWEN3_W_DENSE;
+  }
+  if (*any_quant && cfg->act_dtype == QWEN3_F32)
+    return fail(QWEN3_ERR_UNSUPPORTED, "quantized weights need 16-bit operands (act_dtype f16 or bf16)");
+  auto same_class = [](const MatW& a, const MatW& b) { return (a.fmt == QWEN3_W_DENSE) == (b.fmt == QWEN3_W_DENSE); };
+  if (!same_class(w.wq, w.wk) || !same_class(w.wq, w.wv))
+    return fail(QWEN3_ERR_UNSUPPORTED, "wq, wk and wv must be all dense or all quantized");
+  if (w.wg.fmt != w.wu.fmt) return fail(QWEN3_ERR_UNSUPPORTED, "w_gate and w_up must share one format");
+  return QWEN3_OK;
+}
+
+// Bytes of the buffer the prefill expands quantized matrices into: the largest product group.
+size_t dequant_bytes(const qwen3_layer_cfg* c) {
+  const size_t e = 2, H = c->hidden, F = c->ffn;
+  const size_t q_dim = static_cast<size_t>(c->n_heads) * c->head_dim;
+  const size_t kv_dim = static_cast<size_t>(c->n_kv_heads) * c->head_dim;
+  size_t m = (q_dim + 2 * kv_dim) * H;
+  m = std::max(m, H * q_dim);
+  m = std::max(m, 2 * F * H);
+  m = std::max(m, H * F);
+  return align256(m * e);
+}
+
+// The matrices of one product group in one storage type: all dense -> as given (wdt); all
+// quantized -> expanded back to back into dq in the operand type.
+int group_weights(const MatW* const* m, int n, const int* rows, int cols, qwen3_dtype wdt, qwen3_dtype act,
+                  char* dq, const void** out, qwen3_dtype* bdt, hipStream_t s) {
+  if (m[0]->fmt == QWEN3_W_DENSE) {
+    for (int i = 0; i < n; ++i) out[i] = m[i]->data;
+    *bdt = wdt;
+    return QWEN3_OK;
+  }
+  KTimer t("dequant", s);
+  size_t off = 0;
+  for (int i = 0; i < n; ++i) {
+    const hipError_t e = q3::launch_dequant(m[i]->fmt, m[i]->data, m[i]->rs, rows[i], cols, act, dq + off, s);
+    if (e != hipSuccess) return hip_fail(e, "dequant launch");
+    out[i] = dq + off;
+    off += static_cast<size_t>(rows[i]) * cols * 2;
+  }
+  *bdt = act;
+  return QWEN3_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -262,8 +360,9 @@ size_t swiglu_ffn_workspace_bytes(int32_t seq_len, int32_t ffn, qwen3_dtype x_dt
 }
 
 // The layer prefill; with k_cache set it also writes k' and v of every position into rows
-// 0..seq_len-1 of the caches (capacity rows per KV head).
-static int layer_prefill_impl(const qwen3_layer_cfg* cfg, const qwen3_layer_weights* w, const void* x_in,
+// 0..seq_len-1 of the caches (capacity rows per KV head). Quantized matrices are expanded into
+// a buffer after the layer workspace just before their product.
+static int layer_prefill_impl(const qwen3_layer_cfg* cfg, const LayerW& w, const void* x_in,
                               void* x_out, int32_t seq_len, const int32_t* positions,
                               const int32_t* ds_rows, int32_t n_ds, const void* ds, void* k_cache,
                               void* v_cache, int32_t capacity, void* workspace, size_t workspace_bytes,
@@ -271,17 +370,11 @@ static int layer_prefill_impl(const qwen3_layer_cfg* cfg, const qwen3_layer_weig
   int st = check_cfg(cfg);
   if (st) return st;
   if (seq_len < 1) return fail(QWEN3_ERR_INVALID_ARG, "seq_len must be >= 1 (got %d): empty prompt", seq_len);
-  if (!w) return fail(QWEN3_ERR_INVALID_ARG, "weights is NULL");
-  const void* wp[] = {w->attn_norm, w->wq, w->wk, w->wv, w->q_norm, w->k_norm,
-                      w->wo, w->ffn_norm, w->w_gate, w->w_up, w->w_down};
-  const char* wn[] = {"attn_norm", "wq", "wk", "wv", "q_norm", "k_norm",
-                      "wo", "ffn_norm", "w_gate", "w_up", "w_down"};
-  for (int i = 0; i < 11; ++i)
-    if (!wp[i]) return fail(QWEN3_ERR_INVALID_ARG, "weight %s is NULL", wn[i]);
+  bool quant = false;
+  if ((st = check_layer_w(w, cfg, &quant))) return st;
   if (!x_in || !x_out) return fail(QWEN3_ERR_INVALID_ARG, "x_in / x_out is NULL");
   if (!positions) return fail(QWEN3_ERR_INVALID_ARG, "positions is NULL");
-  if (misaligned16({x_in, x_out, ds, w->attn_norm, w->wq, w->wk, w->wv, w->q_norm, w->k_norm, w->wo,
-                    w->ffn_norm, w->w_gate, w->w_up, w->w_down}))
+  if (misaligned16({x_in, x_out, ds}))
     return fail(QWEN3_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
   if (n_ds < 0 || n_ds > seq_len)
     return fail(QWEN3_ERR_INVALID_ARG, "n_ds (%d) must be in [0, seq_len = %d]", n_ds, seq_len);
@@ -289,8 +382,9 @@ static int layer_prefill_impl(const qwen3_layer_cfg* cfg, const qwen3_layer_weig
   if (n_ds > 0 && (!ds || !ds_rows))
     return fail(QWEN3_ERR_INVALID_ARG, "n_ds = %d needs both ds_rows and ds", n_ds);
   const Workspace L = layout(cfg, seq_len);
-  if (!workspace || workspace_bytes < L.total)
-    return fail(QWEN3_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", L.total, workspace_bytes,
+  const size_t need = L.total + (quant ? dequant_bytes(cfg) : 0);
+  if (!workspace || workspace_bytes < need)
+    return fail(QWEN3_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need, workspace_bytes,
                 workspace ? "" : ", NULL pointer");
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
     return fail(QWEN3_ERR_WORKSPACE, "workspace must be 256-byte aligned");
@@ -313,21 +407,27 @@ static int layer_prefill_impl(const qwen3_layer_cfg* cfg, const qwen3_layer_weig
   char* qkv = ws + L.qkv;
   void* o = ws + L.o;
   void* act = ws + L.act;
+  char* dq = ws + L.total;   // expanded quantized matrices (quantized layers only)
   const float* x = static_cast<const float*>(x_in);
   float* y = static_cast<float*>(x_out);
+  const void* B[3];
+  qwen3_dtype bdt;
 
   // a1: input RMSNorm
-  if ((st = run_rmsnorm(x, w->attn_norm, wdt, xn, dt, S, H, cfg->rms_eps, s))) return st;
+  if ((st = run_rmsnorm(x, w.attn_norm, wdt, xn, dt, S, H, cfg->rms_eps, s))) return st;
   // a2: q | k | v = xn [Wq; Wk; Wv]^T in one product, token-major [S, q_dim + 2 kv_dim]
   {
-    Proj p{xn, H, w->wq, w->wk, w->wv, q_dim, q_dim + kv_dim, H, qkv, qkv_dim, nullptr, 0, S, qkv_dim, H};
-    if ((st = run_gemm("gemm_qkv", p, dt == QWEN3_F32 ? q3::EPI_STORE_F32 : q3::EPI_STORE_16, wdt, dt, s)))
+    const MatW* g[3] = {&w.wq, &w.wk, &w.wv};
+    const int rows[3] = {q_dim, kv_dim, kv_dim};
+    if ((st = group_weights(g, 3, rows, H, wdt, dt, dq, B, &bdt, s))) return st;
+    Proj p{xn, H, B[0], B[1], B[2], q_dim, q_dim + kv_dim, H, qkv, qkv_dim, nullptr, 0, S, qkv_dim, H};
+    if ((st = run_gemm("gemm_qkv", p, dt == QWEN3_F32 ? q3::EPI_STORE_F32 : q3::EPI_STORE_16, bdt, dt, s)))
       return st;
   }
   // a3+a4: per-head RMSNorm and interleaved MRoPE on q and k, in place
   {
     q3::RopeParams p{qkv, qkv + static_cast<size_t>(q_dim) * e, qkv_dim, qkv_dim, S, nh, nkv,
-                     w->q_norm, w->k_norm, wdt, positions, cfg->rms_eps,
+                     w.q_norm, w.k_norm, wdt, positions, cfg->rms_eps,
                      std::log2(static_cast<double>(cfg->rope_theta)), cfg->mrope_section[1],
                      cfg->mrope_section[2]};
     if ((st = run_qk_norm_mrope(p, hd, dt, s))) return st;
@@ -347,13 +447,30 @@ static int layer_prefill_impl(const qwen3_layer_cfg* cfg, const qwen3_layer_weig
     return st;
   // a6: y1 = x + o Wo^T (fp32, into x_out)
   {
-    Proj p{o, q_dim, w->wo, nullptr, nullptr, H, H, q_dim, y, H, x, H, S, H, q_dim};
-    if ((st = run_gemm("gemm_o_resid", p, q3::EPI_STORE_F32, wdt, dt, s))) return st;
+    const MatW* g[1] = {&w.wo};
+    const int rows[1] = {H};
+    if ((st = group_weights(g, 1, rows, q_dim, wdt, dt, dq, B, &bdt, s))) return st;
+    Proj p{o, q_dim, B[0], nullptr, nullptr, H, H, q_dim, y, H, x, H, S, H, q_dim};
+    if ((st = run_gemm("gemm_o_resid", p, q3::EPI_STORE_F32, bdt, dt, s))) return st;
   }
   // a7: yn = RMSNorm(y1, ffn_norm) (reuses the xn buffer)
-  if ((st = run_rmsnorm(y, w->ffn_norm, wdt, xn, dt, S, H, cfg->rms_eps, s))) return st;
-  // a8 + a9: y2 = y1 + (silu(yn Wg^T) * (yn Wu^T)) Wd^T
-  if ((st = run_ffn(xn, w->w_gate, w->w_up, w->w_down, y, y, QWEN3_F32, act, S, H, F, wdt, dt, s))) return st;
+  if ((st = run_rmsnorm(y, w.ffn_norm, wdt, xn, dt, S, H, cfg->rms_eps, s))) return st;
+  // a8: a = silu(yn Wg^T) * (yn Wu^T)
+  {
+    const MatW* g[2] = {&w.wg, &w.wu};
+    const int rows[2] = {F, F};
+    if ((st = group_weights(g, 2, rows, H, wdt, dt, dq, B, &bdt, s))) return st;
+    Proj gu{xn, H, B[0], B[1], nullptr, 0, 0, H, act, F, nullptr, 0, S, 2 * F, H};
+    if ((st = run_gemm("gemm_gate_up_swiglu", gu, q3::EPI_SWIGLU_16, bdt, dt, s))) return st;
+  }
+  // a9: y2 = y1 + a Wd^T
+  {
+    const MatW* g[1] = {&w.wd};
+    const int rows[1] = {H};
+    if ((st = group_weights(g, 1, rows, F, wdt, dt, dq, B, &bdt, s))) return st;
+    Proj dn{act, F, B[0], nullptr, nullptr, H, H, F, y, H, y, H, S, H, F};
+    if ((st = run_gemm("gemm_down_resid", dn, q3::EPI_STORE_F32, bdt, dt, s))) return st;
+  }
   // a10: DeepStack rows
   if (n_ds > 0) {
     KTimer t("deepstack_add", s);
@@ -367,8 +484,9 @@ int qwen3_layer_prefill(const qwen3_layer_cfg* cfg, const qwen3_layer_weights* w
                         void* x_out, int32_t seq_len, const int32_t* positions,
                         const int32_t* ds_rows, int32_t n_ds, const void* ds, void* workspace,
                         size_t workspace_bytes, void* stream) {
-  return layer_prefill_impl(cfg, w, x_in, x_out, seq_len, positions, ds_rows, n_ds, ds, nullptr, nullptr, 0,
-                            workspace, workspace_bytes, stream);
+  if (!w) return fail(QWEN3_ERR_INVALID_ARG, "weights is NULL");
+  return layer_prefill_impl(cfg, dense_layer(w), x_in, x_out, seq_len, positions, ds_rows, n_ds, ds, nullptr,
+                            nullptr, 0, workspace, workspace_bytes, stream);
 }
 
 int qwen3_layer_prefill_kv(const qwen3_layer_cfg* cfg, const qwen3_layer_weights* w, const void* x_in,
@@ -381,8 +499,51 @@ int qwen3_layer_prefill_kv(const qwen3_layer_cfg* cfg, const qwen3_layer_weights
   if (misaligned16({k_cache, v_cache})) return fail(QWEN3_ERR_INVALID_ARG, "cache pointers must be 16-byte aligned");
   if (capacity < seq_len)
     return fail(QWEN3_ERR_INVALID_ARG, "capacity (%d) must be >= seq_len (%d)", capacity, seq_len);
-  return layer_prefill_impl(cfg, w, x_in, x_out, seq_len, positions, ds_rows, n_ds, ds, k_cache, v_cache, capacity,
-                            workspace, workspace_bytes, stream);
+  if (!w) return fail(QWEN3_ERR_INVALID_ARG, "weights is NULL");
+  return layer_prefill_impl(cfg, dense_layer(w), x_in, x_out, seq_len, positions, ds_rows, n_ds, ds, k_cache,
+                            v_cache, capacity, workspace, workspace_bytes, stream);
+}
+
+size_t qwen3_layer_quant_workspace_bytes(const qwen3_layer_cfg* cfg, int32_t seq_len) {
+  if (!cfg || seq_len < 1 || !valid_dtype(cfg->act_dtype) || cfg->hidden < 1 || cfg->ffn < 1) return 0;
+  return layout(cfg, seq_len).total + dequant_bytes(cfg);
+}
+
+int qwen3_layer_prefill_quant(const qwen3_layer_cfg* cfg, const qwen3_layer_qweights* w, const void* x_in,
+                              void* x_out, int32_t seq_len, const int32_t* positions, const int32_t* ds_rows,
+                              int32_t n_ds, const void* ds, void* k_cache, void* v_cache, int32_t capacity,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (!w) return fail(QWEN3_ERR_INVALID_ARG, "weights is NULL");
+  if ((k_cache == nullptr) != (v_cache == nullptr))
+    return fail(QWEN3_ERR_INVALID_ARG, "k_cache and v_cache must be given together");
+  if (k_cache) {
+    if (k_cache == v_cache) return fail(QWEN3_ERR_INVALID_ARG, "k_cache and v_cache must be different buffers");
+    if (misaligned16({k_cache, v_cache}))
+      return fail(QWEN3_ERR_INVALID_ARG, "cache pointers must be 16-byte aligned");
+    if (capacity < seq_len)
+      return fail(QWEN3_ERR_INVALID_ARG, "capacity (%d) must be >= seq_len (%d)", capacity, seq_len);
+  }
+  return layer_prefill_impl(cfg, quant_layer(w), x_in, x_out, seq_len, positions, ds_rows, n_ds, ds, k_cache,
+                            v_cache, capacity, workspace, workspace_bytes, stream);
+}
+
+int dequantize_matrix(const qwen3_qmatrix* m, int32_t rows, int32_t cols, qwen3_dtype out_dtype, void* out,
+                      void* stream) {
+  if (!m) return fail(QWEN3_ERR_INVALID_ARG, "matrix is NULL");
+  const MatW mw{m->format, m->data, m->row_scale};
+  int st = check_matrix(mw, "matrix");
+  if (st) return st;
+  if (mw.fmt == QWEN3_W_DENSE) return fail(QWEN3_ERR_INVALID_ARG, "a dense matrix has nothing to dequantize");
+  if (out_dtype != QWEN3_F16 && out_dtype != QWEN3_BF16)
+    return fail(QWEN3_ERR_UNSUPPORTED, "out_dtype must be f16 or bf16");
+  if (rows < 1 || cols < 1) return fail(QWEN3_ERR_INVALID_ARG, "rows (%d) and cols (%d) must be >= 1", rows, cols);
+  if (cols % 64 != 0) return fail(QWEN3_ERR_UNSUPPORTED, "cols (%d) must be a multiple of 64", cols);
+  if (!out) return fail(QWEN3_ERR_INVALID_ARG, "out is NULL");
+  if (misaligned16({out})) return fail(QWEN3_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  KTimer t("dequant", s);
+  const hipError_t e = q3::launch_dequant(mw.fmt, mw.data, mw.rs, rows, cols, out_dtype, out, s);
+  return e == hipSuccess ? QWEN3_OK : hip_fail(e, "dequant launch");
 }
 
 // ---- whole-model prefill to the last position's logits --------------------------------------
@@ -749,28 +910,50 @@ size_t qwen3_layer_decode_workspace_bytes(const qwen3_layer_cfg* cfg, int32_t ca
   return decode_layout(cfg, capacity).total;
 }
 
-static int run_gemv(const char* name, const q3::GemvParams& p, int epi, qwen3_dtype wdt, hipStream_t s) {
+// One matrix-vector product group: p's W0..W2 come from m (n matrices). Dense matrices use the
+// dense kernel; quantized ones of one format the quantized kernel; a store group whose matrices
+// differ in format runs one launch per matrix.
+static int run_gemv(const char* name, const MatW* const* m, int n, q3::GemvParams p, int epi, qwen3_dtype wdt,
+                    hipStream_t s) {
   KTimer t(name, s);
-  const hipError_t e = q3::launch_gemv(p, epi, wdt, s);
+  bool same = true;
+  for (int i = 1; i < n; ++i) same = same && m[i]->fmt == m[0]->fmt;
+  hipError_t e = hipSuccess;
+  if (same) {
+    p.W0 = m[0]->data;
+    p.W1 = n > 1 ? m[1]->data : nullptr;
+    p.W2 = n > 2 ? m[2]->data : nullptr;
+    if (m[0]->fmt == QWEN3_W_DENSE) e = q3::launch_gemv(p, epi, wdt, s);
+    else e = q3::launch_gemv_quant(p, epi, m[0]->fmt, m[0]->rs, n > 1 ? m[1]->rs : nullptr, n > 2 ? m[2]->rs : nullptr, s);
+  } else {
+    if (epi != q3::GV_STORE) return fail(QWEN3_ERR_UNSUPPORTED, "%s: mixed weight formats", name);
+    const int lo[3] = {0, p.nseg0, p.nseg1}, hi[3] = {p.nseg0, p.nseg1, p.rows};
+    for (int i = 0; i < n && e == hipSuccess; ++i) {
+      q3::GemvParams q = p;
+      q.W0 = m[i]->data;
+      q.W1 = q.W2 = nullptr;
+      q.rows = hi[i] - lo[i];
+      q.nseg0 = q.nseg1 = q.rows;
+      q.y = p.y + lo[i];
+      if (m[i]->fmt == QWEN3_W_DENSE) e = q3::launch_gemv(q, epi, wdt, s);
+      else e = q3::launch_gemv_quant(q, epi, m[i]->fmt, m[i]->rs, nullptr, nullptr, s);
+    }
+  }
   return e == hipSuccess ? QWEN3_OK : hip_fail(e, name);
 }
 
-int qwen3_layer_decode(const qwen3_layer_cfg* cfg, const qwen3_layer_weights* w, const float* x_in, float* x_out,
-                       const int32_t* position, void* k_cache, void* v_cache, int32_t capacity, int32_t len,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+static int layer_decode_impl(const qwen3_layer_cfg* cfg, const LayerW& w, const float* x_in, float* x_out,
+                             const int32_t* position, void* k_cache, void* v_cache, int32_t capacity, int32_t len,
+                             void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_cfg(cfg);
   if (st) return st;
   if ((st = check_decode_heads(cfg->n_heads, cfg->n_kv_heads, cfg->head_dim))) return st;
-  if (!w) return fail(QWEN3_ERR_INVALID_ARG, "weights is NULL");
-  const void* wp[] = {w->attn_norm, w->wq, w->wk, w->wv, w->q_norm, w->k_norm,
-                      w->wo, w->ffn_norm, w->w_gate, w->w_up, w->w_down};
-  for (const void* q : wp)
-    if (!q) return fail(QWEN3_ERR_INVALID_ARG, "a weight pointer is NULL");
+  bool quant = false;
+  if ((st = check_layer_w(w, cfg, &quant))) return st;
   if (!x_in || !x_out || !position || !k_cache || !v_cache)
     return fail(QWEN3_ERR_INVALID_ARG, "x_in / x_out / position / k_cache / v_cache is NULL");
   if (k_cache == v_cache) return fail(QWEN3_ERR_INVALID_ARG, "k_cache and v_cache must be different buffers");
-  if (misaligned16({x_in, x_out, k_cache, v_cache, w->attn_norm, w->wq, w->wk, w->wv, w->q_norm, w->k_norm, w->wo,
-                    w->ffn_norm, w->w_gate, w->w_up, w->w_down}))
+  if (misaligned16({x_in, x_out, k_cache, v_cache}))
     return fail(QWEN3_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
   if (len < 0 || len >= capacity)
     return fail(QWEN3_ERR_INVALID_ARG, "len (%d) must be in [0, capacity = %d): the new token takes row len", len,
@@ -800,15 +983,16 @@ int qwen3_layer_decode(const qwen3_layer_cfg* cfg, const qwen3_layer_weights* w,
   float* act = reinterpret_cast<float*>(ws + L.act);
 
   // input RMSNorm of the new row (fp32)
-  if ((st = run_rmsnorm(x_in, w->attn_norm, wdt, xn, QWEN3_F32, 1, H, cfg->rms_eps, s))) return st;
+  if ((st = run_rmsnorm(x_in, w.attn_norm, wdt, xn, QWEN3_F32, 1, H, cfg->rms_eps, s))) return st;
   // q | k | v of the new token
   {
-    q3::GemvParams p{w->wq, w->wk, w->wv, q_dim, q_dim + kv_dim, xn, qkv, nullptr, qkv_dim, H};
-    if ((st = run_gemv("gemv_qkv", p, q3::GV_STORE, wdt, s))) return st;
+    const MatW* g[3] = {&w.wq, &w.wk, &w.wv};
+    q3::GemvParams p{nullptr, nullptr, nullptr, q_dim, q_dim + kv_dim, xn, qkv, nullptr, qkv_dim, H};
+    if ((st = run_gemv("gemv_qkv", g, 3, p, q3::GV_STORE, wdt, s))) return st;
   }
   // per-head RMSNorm + interleaved MRoPE at the token's position
   {
-    q3::RopeParams p{qkv, qkv + q_dim, qkv_dim, qkv_dim, 1, nh, nkv, w->q_norm, w->k_norm, wdt, position,
+    q3::RopeParams p{qkv, qkv + q_dim, qkv_dim, qkv_dim, 1, nh, nkv, w.q_norm, w.k_norm, wdt, position,
                      cfg->rms_eps, std::log2(static_cast<double>(cfg->rope_theta)), cfg->mrope_section[1],
                      cfg->mrope_section[2]};
     if ((st = run_qk_norm_mrope(p, hd, QWEN3_F32, s))) return st;
@@ -827,19 +1011,38 @@ int qwen3_layer_decode(const qwen3_layer_cfg* cfg, const qwen3_layer_weights* w,
     return st;
   // y1 = x + o Wo^T
   {
-    q3::GemvParams p{w->wo, nullptr, nullptr, H, H, o, x_out, x_in, H, q_dim};
-    if ((st = run_gemv("gemv_o_resid", p, q3::GV_RESID, wdt, s))) return st;
+    const MatW* g[1] = {&w.wo};
+    q3::GemvParams p{nullptr, nullptr, nullptr, H, H, o, x_out, x_in, H, q_dim};
+    if ((st = run_gemv("gemv_o_resid", g, 1, p, q3::GV_RESID, wdt, s))) return st;
   }
-  if ((st = run_rmsnorm(x_out, w->ffn_norm, wdt, xn, QWEN3_F32, 1, H, cfg->rms_eps, s))) return st;
+  if ((st = run_rmsnorm(x_out, w.ffn_norm, wdt, xn, QWEN3_F32, 1, H, cfg->rms_eps, s))) return st;
   {
-    q3::GemvParams p{w->w_gate, w->w_up, nullptr, F, F, xn, act, nullptr, F, H};
-    if ((st = run_gemv("gemv_gate_up_swiglu", p, q3::GV_SWIGLU, wdt, s))) return st;
+    const MatW* g[2] = {&w.wg, &w.wu};
+    q3::GemvParams p{nullptr, nullptr, nullptr, F, F, xn, act, nullptr, F, H};
+    if ((st = run_gemv("gemv_gate_up_swiglu", g, 2, p, q3::GV_SWIGLU, wdt, s))) return st;
   }
   {
-    q3::GemvParams p{w->w_down, nullptr, nullptr, H, H, act, x_out, x_out, H, F};
-    if ((st = run_gemv("gemv_down_resid", p, q3::GV_RESID, wdt, s))) return st;
+    const MatW* g[1] = {&w.wd};
+    q3::GemvParams p{nullptr, nullptr, nullptr, H, H, act, x_out, x_out, H, F};
+    if ((st = run_gemv("gemv_down_resid", g, 1, p, q3::GV_RESID, wdt, s))) return st;
   }
   return QWEN3_OK;
+}
+
+int qwen3_layer_decode(const qwen3_layer_cfg* cfg, const qwen3_layer_weights* w, const float* x_in, float* x_out,
+                       const int32_t* position, void* k_cache, void* v_cache, int32_t capacity, int32_t len,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (!w) return fail(QWEN3_ERR_INVALID_ARG, "weights is NULL");
+  return layer_decode_impl(cfg, dense_layer(w), x_in, x_out, position, k_cache, v_cache, capacity, len, workspace,
+                           workspace_bytes, stream);
+}
+
+int qwen3_layer_decode_quant(const qwen3_layer_cfg* cfg, const qwen3_layer_qweights* w, const float* x_in,
+                             float* x_out, const int32_t* position, void* k_cache, void* v_cache, int32_t capacity,
+                             int32_t len, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!w) return fail(QWEN3_ERR_INVALID_ARG, "weights is NULL");
+  return layer_decode_impl(cfg, quant_layer(w), x_in, x_out, position, k_cache, v_cache, capacity, len, workspace,
+                           workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -81,6 +81,20 @@ struct GemvParams {
 };
 hipError_t launch_gemv(const GemvParams& p, int epi, int wdt, hipStream_t s);
 
+// ---- weight-only quantized projections (quant.hip) -------------------------------------------
+// Formats; the values match qwen3_wformat in the public header.
+enum WFormat : int { WF_DENSE = 0, WF_Q4_0 = 1, WF_Q8_ROW = 2 };
+// out [rows, cols] of out_dt (f16 or bf16) = the dequantized weights (one rounding each).
+// Q4_0: data = rows * cols / 32 blocks of 18 bytes (2-byte aligned), cols % 32 == 0.
+// Q8 rows: data int8 [rows, cols] (16-byte aligned), row_scale fp32 [rows], cols % 16 == 0.
+hipError_t launch_dequant(int fmt, const void* data, const float* row_scale, int64_t rows, int cols, int out_dt,
+                          void* out, hipStream_t s);
+// launch_gemv on quantized W0..W2 (one format for all); rs0..rs2: the row scales of W0..W2
+// (q8 rows only). Q4_0 needs K % 64 == 0 and 4-byte aligned matrices; q8 rows K % 16 == 0
+// and 16-byte aligned matrices.
+hipError_t launch_gemv_quant(const GemvParams& p, int epi, int fmt, const float* rs0, const float* rs1,
+                             const float* rs2, hipStream_t s);
+
 // ---- per-head RMSNorm + interleaved MRoPE, in place ---------------------------------------
 struct RopeParams {
   void* q;            // token t, head h at q + t*q_stride + h*hd

@@ -1,0 +1,303 @@
+// Weight-only quantized projections: GGML Q4_0 blocks (hf2q 0.1.1, qwen3vl_text/forward.rs,
+// the dense FFN step: the converted checkpoints' projections are Q4_0) and int8 rows with a
+// per-row scale (cortiq-engine 0.8.21, qwen3te.rs, `q8_exact_matmat`).
+//
+// Q4_0: 32 consecutive weights of a row per 18-byte block, a binary16 scale d then 16 bytes of
+// codes; byte j holds weight j's code in its low nibble and weight j + 16's in its high nibble;
+// weight = d * (code - 8). Rows are K/32 blocks back to back (18-byte blocks, so a block is only
+// 2-byte aligned; two blocks, 36 bytes, start 4-byte aligned when K % 64 == 0 and the matrix
+// is 4-byte aligned).
+// q8 rows: weight[o, j] = row_scale[o] * q[o, j], q int8 [rows, K].
+//
+// Prefill (M = S rows of activations) is MFMA-bound: the weights are expanded once per call
+// into the operand format (d * (code - 8) is exact in fp32 and rounded once to fp16/bf16;
+// row_scale * q likewise) and the dense GEMM runs on them.
+// Decode (one activation row) is HBM-bound: the matrix-vector kernels read the quantized bytes
+// directly (0.5625 B per weight for Q4_0, 1 B for q8 rows) and keep the activations in fp32:
+//   sum_j w_j x_j = d * (sum_j code_j x_j - 8 * sum_j x_j)     per Q4_0 block,
+//   sum_j w_j x_j = rs * (sum_j (q_j + 128) x_j - 128 * sum_j x_j)   per q8 row,
+// so each weight costs one byte-to-float conversion and one FMA, and the block sums of x are
+// shared by the four rows a wave computes.
+#include "common.h"
+#include "kernels.h"
+
+namespace q3 {
+
+typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
+
+// ---- expansion to the operand format -----------------------------------------------------------
+// Thread = one Q4_0 block (32 weights); the block's 18 bytes are read as 9 halfwords.
+template <int ODT>
+__global__ __launch_bounds__(256) void dequant_q4_0_kernel(const uint8_t* blocks, int64_t nblocks, void* out) {
+  const int64_t b = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (b >= nblocks) return;
+  const uint16_t* h = reinterpret_cast<const uint16_t*>(blocks + b * 18);
+  const float d = h2f(h[0]);
+  float lo[16], hi[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t two = h[1 + i];   // bytes 2i, 2i + 1 of the codes
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const uint32_t byte = (two >> (8 * k)) & 0xFF;
+      lo[2 * i + k] = d * static_cast<float>(static_cast<int>(byte & 0xF) - 8);
+      hi[2 * i + k] = d * static_cast<float>(static_cast<int>(byte >> 4) - 8);
+    }
+  }
+  const int64_t o = b * 32;
+  store8<ODT>(out, o, *reinterpret_cast<const float(*)[8]>(lo));
+  store8<ODT>(out, o + 8, *reinterpret_cast<const float(*)[8]>(lo + 8));
+  store8<ODT>(out, o + 16, *reinterpret_cast<const float(*)[8]>(hi));
+  store8<ODT>(out, o + 24, *reinterpret_cast<const float(*)[8]>(hi + 8));
+}
+
+// Thread = 16 consecutive weights of one row (cols % 16 == 0).
+template <int ODT>
+__global__ __launch_bounds__(256) void dequant_q8_row_kernel(const int8_t* q, const float* rs, int64_t rows,
+                                                             int cols, void* out) {
+  const int64_t c = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int per_row = cols / 16;
+  if (c >= rows * per_row) return;
+  const int64_t r = c / per_row;
+  const float s = rs[r];
+  const u32x4 w = *reinterpret_cast<const u32x4*>(q + c * 16);
+  float v[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int8_t code = static_cast<int8_t>((w[e >> 2] >> (8 * (e & 3))) & 0xFF);
+    v[e] = s * static_cast<float>(code);
+  }
+  store8<ODT>(out, c * 16, *reinterpret_cast<const float(*)[8]>(v));
+  store8<ODT>(out, c * 16 + 8, *reinterpret_cast<const float(*)[8]>(v + 8));
+}
+
+hipError_t launch_dequant(int fmt, const void* data, const float* row_scale, int64_t rows, int cols, int out_dt,
+                          void* out, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (out_dt != DT_F16 && out_dt != DT_BF16) return hipErrorInvalidValue;
+  if (fmt == WF_Q4_0) {
+    if (cols % 32 != 0) return hipErrorInvalidValue;
+    const int64_t nb = rows * (cols / 32);
+    const unsigned grid = static_cast<unsigned>((nb + 255) / 256);
+    const uint8_t* b = static_cast<const uint8_t*>(data);
+    if (out_dt == DT_F16) dequant_q4_0_kernel<DT_F16><<<grid, 256, 0, s>>>(b, nb, out);
+    else dequant_q4_0_kernel<DT_BF16><<<grid, 256, 0, s>>>(b, nb, out);
+  } else if (fmt == WF_Q8_ROW) {
+    if (cols % 16 != 0) return hipErrorInvalidValue;
+    const int64_t nc = rows * (cols / 16);
+    const unsigned grid = static_cast<unsigned>((nc + 255) / 256);
+    const int8_t* q = static_cast<const int8_t*>(data);
+    if (out_dt == DT_F16) dequant_q8_row_kernel<DT_F16><<<grid, 256, 0, s>>>(q, row_scale, rows, cols, out);
+    else dequant_q8_row_kernel<DT_BF16><<<grid, 256, 0, s>>>(q, row_scale, rows, cols, out);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// ---- matrix-vector products on the quantized bytes (decode) ----------------------------------
+constexpr int kQvRows = 4;   // output rows per wave
+
+// Sum over the 32 weights of a Q4_0 block of code_j * x_j; q holds the 16 code bytes as 4
+// words (byte j: code j low, code j + 16 high), x the block's 32 activations.
+__device__ __forceinline__ float q4_codes_dot(const uint32_t (&q)[4], const float* x) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = q[i] & 0x0F0F0F0Fu, hi = (q[i] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      s = fmaf(static_cast<float>((lo >> (8 * k)) & 0xFF), x[4 * i + k], s);
+      s = fmaf(static_cast<float>((hi >> (8 * k)) & 0xFF), x[16 + 4 * i + k], s);
+    }
+  }
+  return s;
+}
+
+// Lane = one pair of consecutive blocks (64 weights, 36 bytes, 4-byte aligned) of each row.
+template <int EPI>
+__global__ __launch_bounds__(256) void gemv_q4_0_kernel(GemvParams p) {
+  constexpr int NR = EPI == GV_SWIGLU ? 2 * kQvRows : kQvRows;
+  const int lane = threadIdx.x & 63;
+  const int r0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * kQvRows;
+  if (r0 >= p.rows) return;
+  const int64_t row_bytes = static_cast<int64_t>(p.K / 32) * 18;
+  const uint8_t* rowp[NR];
+#pragma unroll
+  for (int j = 0; j < kQvRows; ++j) {
+    const int r = min(r0 + j, p.rows - 1);  // rows past the end repeat the last (never stored)
+    if (EPI == GV_SWIGLU) {
+      rowp[j] = static_cast<const uint8_t*>(p.W0) + r * row_bytes;
+      rowp[kQvRows + j] = static_cast<const uint8_t*>(p.W1) + r * row_bytes;
+    } else {
+      const void* W = r < p.nseg0 ? p.W0 : r < p.nseg1 ? p.W1 : p.W2;
+      const int rr = r < p.nseg0 ? r : r < p.nseg1 ? r - p.nseg0 : r - p.nseg1;
+      rowp[j] = static_cast<const uint8_t*>(W) + rr * row_bytes;
+    }
+  }
+  float acc[NR];
+#pragma unroll
+  for (int j = 0; j < NR; ++j) acc[j] = 0.f;
+  const int npairs = p.K / 64;
+  for (int pp = lane; pp < npairs; pp += 64) {
+    uint32_t w[NR][9];
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+      const uint8_t* src = rowp[j] + pp * 36;
+      const u32x4a4 a = *reinterpret_cast<const u32x4a4*>(src);
+      const u32x4a4 b = *reinterpret_cast<const u32x4a4*>(src + 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        w[j][e] = a[e];
+        w[j][4 + e] = b[e];
+      }
+      w[j][8] = *reinterpret_cast<const uint32_t*>(src + 32);
+    }
+    float x[64];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) load8<DT_F32>(p.x, pp * 64 + 8 * i, *reinterpret_cast<float(*)[8]>(x + 8 * i));
+    float sxa = 0.f, sxb = 0.f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      sxa += x[e];
+      sxb += x[32 + e];
+    }
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+      const float da = h2f(static_cast<uint16_t>(w[j][0] & 0xFFFF));
+      const float db = h2f(static_cast<uint16_t>(w[j][4] >> 16));
+      uint32_t qa[4], qb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        qa[i] = __builtin_amdgcn_alignbyte(w[j][i + 1], w[j][i], 2);  // bytes 2 .. 17 of block a
+        qb[i] = w[j][5 + i];                                           // bytes 20 .. 35: codes of block b
+      }
+      acc[j] = fmaf(da, fmaf(-8.f, sxa, q4_codes_dot(qa, x)), acc[j]);
+      acc[j] = fmaf(db, fmaf(-8.f, sxb, q4_codes_dot(qb, x + 32)), acc[j]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NR; ++j) acc[j] = wave_sum(acc[j]);
+  if (lane < kQvRows && r0 + lane < p.rows) {
+    float v = acc[0];
+#pragma unroll
+    for (int j = 1; j < kQvRows; ++j) v = lane == j ? acc[j] : v;
+    const int r = r0 + lane;
+    if (EPI == GV_SWIGLU) {
+      float u = acc[kQvRows];
+#pragma unroll
+      for (int j = 1; j < kQvRows; ++j) u = lane == j ? acc[kQvRows + j] : u;
+      v = v / (1.f + __expf(-v)) * u;
+    } else if (EPI == GV_RESID) {
+      v += p.R[r];
+    }
+    p.y[r] = v;
+  }
+}
+
+// Lane = 16 consecutive int8 weights of each row per step; U steps loaded together. Codes are
+// offset by 128 (flipping the sign bit) so each byte converts as an unsigned value.
+template <int EPI>
+__global__ __launch_bounds__(256) void gemv_q8_row_kernel(GemvParams p, const float* rs0, const float* rs1,
+                                                          const float* rs2) {
+  constexpr int NR = EPI == GV_SWIGLU ? 2 * kQvRows : kQvRows;
+  constexpr int U = 16 / NR;
+  const int lane = threadIdx.x & 63;
+  const int r0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * kQvRows;
+  if (r0 >= p.rows) return;
+  const int8_t* rowp[NR];
+  float scale[NR];
+#pragma unroll
+  for (int j = 0; j < kQvRows; ++j) {
+    const int r = min(r0 + j, p.rows - 1);
+    if (EPI == GV_SWIGLU) {
+      rowp[j] = static_cast<const int8_t*>(p.W0) + static_cast<int64_t>(r) * p.K;
+      rowp[kQvRows + j] = static_cast<const int8_t*>(p.W1) + static_cast<int64_t>(r) * p.K;
+      scale[j] = rs0[r];
+      scale[kQvRows + j] = rs1[r];
+    } else {
+      const int seg = r < p.nseg0 ? 0 : r < p.nseg1 ? 1 : 2;
+      const void* W = seg == 0 ? p.W0 : seg == 1 ? p.W1 : p.W2;
+      const float* rs = seg == 0 ? rs0 : seg == 1 ? rs1 : rs2;
+      const int rr = seg == 0 ? r : seg == 1 ? r - p.nseg0 : r - p.nseg1;
+      rowp[j] = static_cast<const int8_t*>(W) + static_cast<int64_t>(rr) * p.K;
+      scale[j] = rs[rr];
+    }
+  }
+  float acc[NR];
+#pragma unroll
+  for (int j = 0; j < NR; ++j) acc[j] = 0.f;
+  for (int i0 = lane * 16; i0 < p.K; i0 += 64 * 16 * U) {
+    u32x4 w[U][NR];
+    float x[U][16];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = min(i0 + u * 1024, p.K - 16);   // steps past the end repeat the last, weighted 0
+#pragma unroll
+      for (int j = 0; j < NR; ++j) w[u][j] = *reinterpret_cast<const u32x4*>(rowp[j] + i);
+      load8<DT_F32>(p.x, i, *reinterpret_cast<float(*)[8]>(x[u]));
+      load8<DT_F32>(p.x, i + 8, *reinterpret_cast<float(*)[8]>(x[u] + 8));
+      if (i0 + u * 1024 >= p.K) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) x[u][e] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float sx = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sx += x[u][e];
+#pragma unroll
+      for (int j = 0; j < NR; ++j) {
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const uint32_t word = w[u][j][e >> 2] ^ 0x80808080u;
+          s = fmaf(static_cast<float>((word >> (8 * (e & 3))) & 0xFF), x[u][e], s);
+        }
+        acc[j] += fmaf(-128.f, sx, s);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NR; ++j) acc[j] = wave_sum(acc[j]) * scale[j];
+  if (lane < kQvRows && r0 + lane < p.rows) {
+    float v = acc[0];
+#pragma unroll
+    for (int j = 1; j < kQvRows; ++j) v = lane == j ? acc[j] : v;
+    const int r = r0 + lane;
+    if (EPI == GV_SWIGLU) {
+      float u = acc[kQvRows];
+#pragma unroll
+      for (int j = 1; j < kQvRows; ++j) u = lane == j ? acc[kQvRows + j] : u;
+      v = v / (1.f + __expf(-v)) * u;
+    } else if (EPI == GV_RESID) {
+      v += p.R[r];
+    }
+    p.y[r] = v;
+  }
+}
+
+hipError_t launch_gemv_quant(const GemvParams& p, int epi, int fmt, const float* rs0, const float* rs1,
+                             const float* rs2, hipStream_t s) {
+  if (p.rows <= 0) return hipSuccess;
+  const unsigned blocks = static_cast<unsigned>((p.rows + 4 * kQvRows - 1) / (4 * kQvRows));
+  if (fmt == WF_Q4_0) {
+    if (p.K % 64 != 0) return hipErrorInvalidValue;
+    if (epi == GV_STORE) gemv_q4_0_kernel<GV_STORE><<<blocks, 256, 0, s>>>(p);
+    else if (epi == GV_RESID) gemv_q4_0_kernel<GV_RESID><<<blocks, 256, 0, s>>>(p);
+    else if (epi == GV_SWIGLU) gemv_q4_0_kernel<GV_SWIGLU><<<blocks, 256, 0, s>>>(p);
+    else return hipErrorInvalidValue;
+  } else if (fmt == WF_Q8_ROW) {
+    if (p.K % 16 != 0) return hipErrorInvalidValue;
+    if (epi == GV_STORE) gemv_q8_row_kernel<GV_STORE><<<blocks, 256, 0, s>>>(p, rs0, rs1, rs2);
+    else if (epi == GV_RESID) gemv_q8_row_kernel<GV_RESID><<<blocks, 256, 0, s>>>(p, rs0, rs1, rs2);
+    else if (epi == GV_SWIGLU) gemv_q8_row_kernel<GV_SWIGLU><<<blocks, 256, 0, s>>>(p, rs0, rs1, rs2);
+    else return hipErrorInvalidValue;
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace q3

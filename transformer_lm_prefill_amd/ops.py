@@ -201,6 +201,78 @@ def layer_decode(spec, weights, x, position, k_cache, v_cache, length, out=None,
     return out
 
 
+_WFORMATS = {"dense": _lib.W_DENSE, "q4_0": _lib.W_Q4_0, "q8_row": _lib.W_Q8_ROW}
+PROJ_NAMES = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
+NORM_NAMES = ("attn_norm", "q_norm", "k_norm", "ffn_norm")
+
+
+def _qmatrix(entry):
+    """(format name, data tensor, row_scale tensor or None) -> QMatrix."""
+    fmt, data, rs = entry
+    if not data.is_cuda or not data.is_contiguous():
+        raise ValueError("quantized weights must be contiguous GPU tensors")
+    return _lib.QMatrix(_WFORMATS[fmt], ctypes.c_void_p(data.data_ptr()), _ptr(rs))
+
+
+def _qweights(norms, proj):
+    args = {n: _ptr(norms[n]) for n in NORM_NAMES}
+    args.update({n: _qmatrix(proj[n]) for n in PROJ_NAMES})
+    return _lib.LayerQWeights(**args)
+
+
+def dequantize_matrix(fmt, data, rows, cols, row_scale=None, out_dtype=torch.float16, out=None):
+    """dequantize_matrix: [rows, cols] of out_dtype from Q4_0 blocks (uint8) or int8 rows + scales."""
+    lib = _lib.load()
+    if out is None:
+        out = torch.empty(rows, cols, dtype=out_dtype, device=data.device)
+    m = _qmatrix((fmt, data, row_scale))
+    _lib.check(lib.dequantize_matrix(ctypes.byref(m), int(rows), int(cols), _dt(out), _ptr(out), _stream()))
+    return out
+
+
+def layer_quant_workspace_bytes(spec, seq_len):
+    return int(_lib.load().qwen3_layer_quant_workspace_bytes(ctypes.byref(_cfg(spec)), int(seq_len)))
+
+
+def layer_prefill_quant(spec, norms, proj, x, positions, ds_rows=None, ds=None, k_cache=None, v_cache=None,
+                        out=None, workspace=None):
+    """qwen3_layer_prefill_quant: norms maps the four norm names to tensors of spec's dtype; proj
+    maps the seven projection names to (format, data, row_scale) with format "dense", "q4_0"
+    or "q8_row". Optional caches as for layer_prefill_kv."""
+    lib = _lib.load()
+    cfg = _cfg(spec)
+    s = x.shape[0]
+    if out is None:
+        out = torch.empty_like(x)
+    need = int(lib.qwen3_layer_quant_workspace_bytes(ctypes.byref(cfg), int(s)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    w = _qweights(norms, proj)
+    n_ds = 0 if ds_rows is None else int(ds_rows.numel())
+    cap = 0 if k_cache is None else int(k_cache.shape[1])
+    _lib.check(lib.qwen3_layer_prefill_quant(
+        ctypes.byref(cfg), ctypes.byref(w), _ptr(x), _ptr(out), int(s), _ptr(positions), _ptr(ds_rows), n_ds,
+        _ptr(ds), _ptr(k_cache), _ptr(v_cache), cap, _ptr(workspace), int(workspace.numel()), _stream()))
+    return out
+
+
+def layer_decode_quant(spec, norms, proj, x, position, k_cache, v_cache, length, out=None, workspace=None):
+    """qwen3_layer_decode_quant: layer_decode with the weights of layer_prefill_quant."""
+    lib = _lib.load()
+    cfg = _cfg(spec)
+    cap = k_cache.shape[1]
+    if out is None:
+        out = torch.empty_like(x)
+    need = int(lib.qwen3_layer_decode_workspace_bytes(ctypes.byref(cfg), int(cap)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    w = _qweights(norms, proj)
+    _lib.check(lib.qwen3_layer_decode_quant(ctypes.byref(cfg), ctypes.byref(w), _ptr(x), _ptr(out), _ptr(position),
+                                            _ptr(k_cache), _ptr(v_cache), int(cap), int(length), _ptr(workspace),
+                                            int(workspace.numel()), _stream()))
+    return out
+
+
 def _model_cfg(spec, n_layers, vocab, n_deepstack_layers):
     m = _lib.ModelCfg()
     m.layer = _cfg(spec)
