@@ -34,6 +34,8 @@ def parse():
     ap.add_argument("--no-model", action="store_true",
                     help="skip the whole-model (embedding + stack + LM head) measurement")
     ap.add_argument("--vocab", type=int, default=151936)
+    ap.add_argument("--no-quant", action="store_true",
+                    help="skip the Q4_0-weight layer measurement")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the KV-cache decode measurement")
     ap.add_argument("--no-bidirectional", action="store_true",
@@ -277,6 +279,85 @@ def decode_extra(cfg, layers, x0, pos, n_tokens=16):
     return res
 
 
+def quant_extra(cfg, x0, pos, n_tokens=16):
+    """One 8B-shaped layer with every projection in Q4_0 blocks (seeded random codes and scales):
+    the prefill of the S-token prompt (expansion + MFMA products) and decode steps after it
+    (matrix-vector products on the quantized bytes)."""
+    import numpy as np
+    import torch
+
+    import synth
+    import transformer_lm_prefill_amd as q3
+    dev = torch.device("cuda:0")
+    S = cfg.seq_len
+    norms, proj = synth.make_quant_layer_weights(cfg, 0)
+    wdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    dn = {n: torch.from_numpy(a).to(dev).to(wdt) for n, a in norms.items()}
+    dp = {n: (f, torch.from_numpy(np.ascontiguousarray(d)).to(dev), None) for n, (f, d, _) in proj.items()}
+    qbytes = {n: d.numel() for n, (_, d, _) in dp.items()}
+    spec = q3.LayerSpec.of(cfg)
+    cap = S + n_tokens
+    kc, vc = q3.kv_cache_alloc(spec, cap)
+    ws = torch.empty(q3.layer_quant_workspace_bytes(spec, S), dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x0)
+
+    def prefill():
+        q3.layer_prefill_quant(spec, dn, dp, x0, pos, k_cache=kc, v_cache=vc, out=y, workspace=ws)
+
+    prefill()
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(3):
+        prefill()
+    torch.cuda.synchronize()
+    ms_pre = (time.perf_counter() - t) * 1e3 / 3
+    q3.timing_enable(True)
+    prefill()
+    torch.cuda.synchronize()
+    kt = q3.timing_collect()
+    q3.timing_enable(False)
+    res = {"workload": f"{cfg.name} layer 1 with Q4_0 projections (18 bytes per 32 weights), seq {S}",
+           "prefill": {"ms": round(ms_pre, 4), "tokens_per_s": round(S / (ms_pre * 1e-3), 1),
+                       "dequant_ms": round(kt["dequant"][1], 4),
+                       "kernels_ms": {k: round(v[1], 4) for k, v in kt.items()}}}
+    del ws
+    dws = torch.empty(q3.layer_decode_workspace_bytes(spec, cap), dtype=torch.uint8, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    xs = torch.randn(n_tokens, cfg.hidden, device=dev, generator=g)
+    tpos = torch.arange(S, S + n_tokens, dtype=torch.int32, device=dev).repeat(3, 1).t().contiguous()
+    out = torch.empty(cfg.hidden, device=dev)
+
+    def decode_all():
+        for i in range(n_tokens):
+            q3.layer_decode_quant(spec, dn, dp, xs[i], tpos[i], kc, vc, S + i, out=out, workspace=dws)
+
+    decode_all()
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    decode_all()
+    torch.cuda.synchronize()
+    ms_tok = (time.perf_counter() - t) * 1e3 / n_tokens
+    q3.timing_enable(True)
+    decode_all()
+    torch.cuda.synchronize()
+    kt = q3.timing_collect()
+    q3.timing_enable(False)
+    gbytes = {"gemv_qkv": qbytes["wq"] + qbytes["wk"] + qbytes["wv"], "gemv_o_resid": qbytes["wo"],
+              "gemv_gate_up_swiglu": qbytes["w_gate"] + qbytes["w_up"], "gemv_down_resid": qbytes["w_down"]}
+    kern = {}
+    for k, (n, tot) in kt.items():
+        avg = tot / n
+        e = {"avg_ms": round(avg, 4)}
+        if k in gbytes:
+            e["GB_per_s"] = round(gbytes[k] / (avg * 1e-3) / 1e9, 1)
+            e["frac_of_hbm_peak"] = round(gbytes[k] / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+        kern[k] = e
+    res["decode"] = {"ms_per_token_layer": round(ms_tok, 4), "tokens_per_s_layer": round(1e3 / ms_tok, 1),
+                     "quantized_weight_MB": round(sum(gbytes.values()) / 1e6, 1), "kernels": kern}
+    return res
+
+
 def main():
     args = parse()
     if args.copy_calib:
@@ -376,6 +457,7 @@ def main():
     model = None if args.no_model else model_prefill_extra(cfg, layers, pos, stream, args.vocab)
     bidir = None if args.no_bidirectional else bidirectional_extra()
     decode = None if args.no_decode else decode_extra(cfg, layers, x0, pos)
+    quant = None if args.no_quant else quant_extra(cfg, x0, pos)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -410,6 +492,7 @@ def main():
         "model_prefill_logits_last": model,
         "bidirectional_attention": bidir,
         "decode": decode,
+        "quantized_q4_0": quant,
     }
     print(json.dumps(out))
 

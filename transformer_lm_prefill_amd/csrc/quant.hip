@@ -26,29 +26,50 @@ namespace q3 {
 typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
 
 // ---- expansion to the operand format -----------------------------------------------------------
-// Thread = one Q4_0 block (32 weights); the block's 18 bytes are read as 9 halfwords.
+// Workgroup = 256 consecutive blocks: their 4608 bytes come in with coalesced dword loads into
+// LDS, thread t expands block t into an LDS tile of 16-bit weights, and the 16 KB tile leaves
+// with coalesced 16-byte stores. (Blocks are 18 bytes, so a thread reading its own block from
+// global memory would issue nine 2-byte loads at an 18-byte lane stride.)
+constexpr int kDqBlocks = 256;
+
 template <int ODT>
 __global__ __launch_bounds__(256) void dequant_q4_0_kernel(const uint8_t* blocks, int64_t nblocks, void* out) {
-  const int64_t b = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (b >= nblocks) return;
-  const uint16_t* h = reinterpret_cast<const uint16_t*>(blocks + b * 18);
-  const float d = h2f(h[0]);
-  float lo[16], hi[16];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t two = h[1 + i];   // bytes 2i, 2i + 1 of the codes
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const uint32_t byte = (two >> (8 * k)) & 0xFF;
-      lo[2 * i + k] = d * static_cast<float>(static_cast<int>(byte & 0xF) - 8);
-      hi[2 * i + k] = d * static_cast<float>(static_cast<int>(byte >> 4) - 8);
-    }
+  __shared__ __align__(16) uint32_t raw[kDqBlocks * 18 / 4];
+  __shared__ __align__(16) uint16_t tile[kDqBlocks * 32];
+  const int tid = threadIdx.x;
+  const int64_t b0 = static_cast<int64_t>(blockIdx.x) * kDqBlocks;
+  const int nb = static_cast<int>(min<int64_t>(kDqBlocks, nblocks - b0));
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(blocks + b0 * 18);   // 4-byte aligned: b0 % 2 == 0
+  for (int i = tid; i < nb * 18 / 4; i += 256) raw[i] = src[i];
+  if (nb % 2 != 0 && tid == 0) {   // an odd last block ends on a halfword
+    const uint16_t* h = reinterpret_cast<const uint16_t*>(blocks + b0 * 18);
+    reinterpret_cast<uint16_t*>(raw)[nb * 9 - 1] = h[nb * 9 - 1];
   }
-  const int64_t o = b * 32;
-  store8<ODT>(out, o, *reinterpret_cast<const float(*)[8]>(lo));
-  store8<ODT>(out, o + 8, *reinterpret_cast<const float(*)[8]>(lo + 8));
-  store8<ODT>(out, o + 16, *reinterpret_cast<const float(*)[8]>(hi));
-  store8<ODT>(out, o + 24, *reinterpret_cast<const float(*)[8]>(hi + 8));
+  __syncthreads();
+  if (tid < nb) {
+    const uint16_t* h = reinterpret_cast<const uint16_t*>(raw) + tid * 9;
+    const float d = h2f(h[0]);
+    float lo[16], hi[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t two = h[1 + i];   // code bytes 2i, 2i + 1
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const uint32_t byte = (two >> (8 * k)) & 0xFF;
+        lo[2 * i + k] = d * static_cast<float>(static_cast<int>(byte & 0xF) - 8);
+        hi[2 * i + k] = d * static_cast<float>(static_cast<int>(byte >> 4) - 8);
+      }
+    }
+    uint16_t* t = tile + tid * 32;
+    store8<ODT>(t, 0, *reinterpret_cast<const float(*)[8]>(lo));
+    store8<ODT>(t, 8, *reinterpret_cast<const float(*)[8]>(lo + 8));
+    store8<ODT>(t, 16, *reinterpret_cast<const float(*)[8]>(hi));
+    store8<ODT>(t, 24, *reinterpret_cast<const float(*)[8]>(hi + 8));
+  }
+  __syncthreads();
+  u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + b0 * 32);
+  const u32x4* from = reinterpret_cast<const u32x4*>(tile);
+  for (int i = tid; i < nb * 4; i += 256) dst[i] = from[i];
 }
 
 // Thread = 16 consecutive weights of one row (cols % 16 == 0).
@@ -78,7 +99,7 @@ hipError_t launch_dequant(int fmt, const void* data, const float* row_scale, int
   if (fmt == WF_Q4_0) {
     if (cols % 32 != 0) return hipErrorInvalidValue;
     const int64_t nb = rows * (cols / 32);
-    const unsigned grid = static_cast<unsigned>((nb + 255) / 256);
+    const unsigned grid = static_cast<unsigned>((nb + kDqBlocks - 1) / kDqBlocks);
     const uint8_t* b = static_cast<const uint8_t*>(data);
     if (out_dt == DT_F16) dequant_q4_0_kernel<DT_F16><<<grid, 256, 0, s>>>(b, nb, out);
     else dequant_q4_0_kernel<DT_BF16><<<grid, 256, 0, s>>>(b, nb, out);
