@@ -353,7 +353,8 @@ size_t qwen3_layer_decode_workspace_bytes(const qwen3_layer_cfg *cfg, int32_t ca
  * Projections with quantized weights compute x W^T with the dequantized W. In a prefill each
  * quantized matrix is expanded to the operand type (f16 or bf16, one rounding per weight: d *
  * (code - 8) and row_scale * q are rounded to nearest even) in the workspace just before its
- * product; a decode step reads the quantized bytes directly and keeps the activations in fp32.
+ * product; a decode step reads the quantized bytes directly (Q4_0: the activations are rounded to
+ * binary16 for v_dot2 products with fp32 sums; int8 rows: fp32 activations).
  * Norm weights stay in cfg.wdtype; dense projections use cfg.wdtype as in qwen3_layer_weights.
  */
 typedef enum { QWEN3_W_DENSE = 0, QWEN3_W_Q4_0 = 1, QWEN3_W_Q8_ROW = 2 } qwen3_wformat;

@@ -13,11 +13,13 @@
 // into the operand format (d * (code - 8) is exact in fp32 and rounded once to fp16/bf16;
 // row_scale * q likewise) and the dense GEMM runs on them.
 // Decode (one activation row) is HBM-bound: the matrix-vector kernels read the quantized bytes
-// directly (0.5625 B per weight for Q4_0, 1 B for q8 rows) and keep the activations in fp32:
-//   sum_j w_j x_j = d * (sum_j code_j x_j - 8 * sum_j x_j)     per Q4_0 block,
-//   sum_j w_j x_j = rs * (sum_j (q_j + 128) x_j - 128 * sum_j x_j)   per q8 row,
-// so each weight costs one byte-to-float conversion and one FMA, and the block sums of x are
-// shared by the four rows a wave computes.
+// directly (0.5625 B per weight for Q4_0, 1 B for q8 rows):
+//   sum_j w_j x_j = d * (sum_j code_j x_j - 8 * sum_j x_j)   per Q4_0 block, x rounded to
+//     binary16, each code pair masked in place into exact binary16 subnormals and multiplied by
+//     v_dot2 with fp32 sums (about 1.1 instructions per weight);
+//   sum_j w_j x_j = rs * (sum_j (q_j + 128) x_j - 128 * sum_j x_j)   per q8 row, x in fp32,
+//     one byte-to-float conversion and one FMA per weight;
+// the block sums of x are shared by the four rows a wave computes.
 #include "common.h"
 #include "kernels.h"
 
@@ -119,20 +121,42 @@ hipError_t launch_dequant(int fmt, const void* data, const float* row_scale, int
 // ---- matrix-vector products on the quantized bytes (decode) ----------------------------------
 constexpr int kQvRows = 4;   // output rows per wave
 
-// Sum over the 32 weights of a Q4_0 block of code_j * x_j; q holds the 16 code bytes as 4
-// words (byte j: code j low, code j + 16 high), x the block's 32 activations.
-__device__ __forceinline__ float q4_codes_dot(const uint32_t (&q)[4], const float* x) {
-  float s = 0.f;
+typedef _Float16 h2x __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2h(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2x, a), __builtin_bit_cast(h2x, b), acc, false);
+}
+
+// The activations of one Q4_0 block as 16 binary16 pairs in the order the code pairs below
+// take them: for code word i (codes of weights 4i .. 4i+3 in its low nibbles, 16+4i .. 16+4i+3
+// in its high nibbles), pairs (x[4i], x[4i+2]), (x[16+4i], x[16+4i+2]), (x[4i+1], x[4i+3]),
+// (x[16+4i+1], x[16+4i+3]).
+__device__ __forceinline__ void q4_pack_x(const float* x, uint32_t (&xp)[16]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t lo = q[i] & 0x0F0F0F0Fu, hi = (q[i] >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      s = fmaf(static_cast<float>((lo >> (8 * k)) & 0xFF), x[4 * i + k], s);
-      s = fmaf(static_cast<float>((hi >> (8 * k)) & 0xFF), x[16 + 4 * i + k], s);
-    }
+    const int a = 4 * i;
+    xp[4 * i + 0] = Fmt<OP_F16>::pack2(x[a], x[a + 2]);
+    xp[4 * i + 1] = Fmt<OP_F16>::pack2(x[16 + a], x[16 + a + 2]);
+    xp[4 * i + 2] = Fmt<OP_F16>::pack2(x[a + 1], x[a + 3]);
+    xp[4 * i + 3] = Fmt<OP_F16>::pack2(x[16 + a + 1], x[16 + a + 3]);
   }
-  return s;
+}
+
+// sum_j code_j * x_j over one block, two codes at a time: a 4-bit code masked in place inside a
+// 16-bit half is the binary16 subnormal code * 2^-24 (bits 0-3) or code * 2^-20 (bits 4-7), so
+// one AND makes a pair of exact operands for v_dot2 (fp32 sums; binary16 subnormals are kept,
+// not flushed); the two scales are undone at the end. q holds the 16 code bytes as 4 words.
+__device__ __forceinline__ float q4_codes_dot(const uint32_t (&q)[4], const uint32_t (&xp)[16]) {
+  float lo = 0.f, hi = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t q8 = q[i] >> 8;
+    lo = dot2h(q[i] & 0x000F000Fu, xp[4 * i + 0], lo);   // codes 4i, 4i+2 (low nibbles of bytes 0, 2)
+    hi = dot2h(q[i] & 0x00F000F0u, xp[4 * i + 1], hi);   // codes 16+4i, 16+4i+2 (high nibbles)
+    lo = dot2h(q8 & 0x000F000Fu, xp[4 * i + 2], lo);     // codes 4i+1, 4i+3 (bytes 1, 3)
+    hi = dot2h(q8 & 0x00F000F0u, xp[4 * i + 3], hi);     // codes 16+4i+1, 16+4i+3
+  }
+  return fmaf(lo, 16777216.f, hi * 1048576.f);
 }
 
 // Lane = one pair of consecutive blocks (64 weights, 36 bytes, 4-byte aligned) of each row.
@@ -177,11 +201,15 @@ __global__ __launch_bounds__(256) void gemv_q4_0_kernel(GemvParams p) {
     float x[64];
 #pragma unroll
     for (int i = 0; i < 8; ++i) load8<DT_F32>(p.x, pp * 64 + 8 * i, *reinterpret_cast<float(*)[8]>(x + 8 * i));
+    uint32_t xa[16], xb[16];
+    q4_pack_x(x, xa);
+    q4_pack_x(x + 32, xb);
+    // the code offset 8 goes out against the sums of the same binary16 activations
     float sxa = 0.f, sxb = 0.f;
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      sxa += x[e];
-      sxb += x[32 + e];
+    for (int e = 0; e < 16; ++e) {
+      sxa = Fmt<OP_F16>::sum2(xa[e], sxa);
+      sxb = Fmt<OP_F16>::sum2(xb[e], sxb);
     }
 #pragma unroll
     for (int j = 0; j < NR; ++j) {
@@ -193,8 +221,8 @@ __global__ __launch_bounds__(256) void gemv_q4_0_kernel(GemvParams p) {
         qa[i] = __builtin_amdgcn_alignbyte(w[j][i + 1], w[j][i], 2);  // bytes 2 .. 17 of block a
         qb[i] = w[j][5 + i];                                           // bytes 20 .. 35: codes of block b
       }
-      acc[j] = fmaf(da, fmaf(-8.f, sxa, q4_codes_dot(qa, x)), acc[j]);
-      acc[j] = fmaf(db, fmaf(-8.f, sxb, q4_codes_dot(qb, x + 32)), acc[j]);
+      acc[j] = fmaf(da, fmaf(-8.f, sxa, q4_codes_dot(qa, xa)), acc[j]);
+      acc[j] = fmaf(db, fmaf(-8.f, sxb, q4_codes_dot(qb, xb)), acc[j]);
     }
   }
 #pragma unroll
