@@ -8,6 +8,7 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <cmath>
 #include <type_traits>
 
 namespace q3 {
@@ -132,71 +133,121 @@ hipError_t launch_deepstack_add(float* y, const int32_t* rows, const void* ds, i
 }
 
 // ------------------------------------------------------------------------------------------
-// q/k RMSNorm + interleaved MRoPE. One 256-thread workgroup per token. A lane owns rotation
-// pair i = (x_i, x_{i+hd/2}) of one head row, so the rotation is lane-local; the hd/2 lanes of
-// a row reduce the sum of squares with cross-lane shuffles. The angle of pair i depends on
-// the token only (not the head), so each lane forms cos/sin once and applies them to every
-// q and k head of the token.
+// q/k RMSNorm + interleaved MRoPE. One 256-thread workgroup per token. A lane owns four
+// consecutive rotation pairs (x_i, x_{i+hd/2}), i = i0 .. i0+3, of one head row, read and written
+// with 8-byte (16-bit types) or 16-byte (fp32) accesses, so the rotation is lane-local and the
+// hd/8 lanes of a row reduce the sum of squares with cross-lane shuffles. The angle of pair i
+// depends on the token only (not the head), so each lane forms its four cos/sin once and applies
+// them to every q and k head of the token; the norm weights are read once per lane.
 //
-// Angle precision: phi = pos * theta^(-2i/hd) is formed in double and reduced to
-// [-pi, pi] in double before the single-precision sincos, so its error does not grow with
-// the position.
+// Angle precision: theta^(-2i/hd) is formed in double on the host, phi = pos * theta^(-2i/hd)
+// in double and reduced to [-pi, pi] in double before the single-precision sincos, so its
+// error does not grow with the position.
+struct RopeFreqs {
+  double inv[64];
+};
+
+template <int DT>
+__device__ __forceinline__ void load4(const void* row, int i, float (&v)[4]) {
+  if (DT == DT_F32) {
+    const f32x4 w = *reinterpret_cast<const f32x4*>(static_cast<const float*>(row) + i);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = w[e];
+  } else {
+    const u32x2 w = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(row) + i);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const uint16_t lo = static_cast<uint16_t>(w[e] & 0xFFFF), hi = static_cast<uint16_t>(w[e] >> 16);
+      v[2 * e] = DT == DT_BF16 ? bf2f(lo) : h2f(lo);
+      v[2 * e + 1] = DT == DT_BF16 ? bf2f(hi) : h2f(hi);
+    }
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void store4(void* row, int i, const float (&v)[4]) {
+  if (DT == DT_F32) {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(row) + i) = f32x4{v[0], v[1], v[2], v[3]};
+  } else {
+    u32x2 w;
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      w[e] = DT == DT_BF16 ? Fmt<OP_BF16>::pack2(v[2 * e], v[2 * e + 1]) : Fmt<OP_F16>::pack2(v[2 * e], v[2 * e + 1]);
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(row) + i) = w;
+  }
+}
+
 template <int DT, int HD>
-__global__ __launch_bounds__(256) void qk_norm_mrope_kernel(const RopeParams p) {
+__global__ __launch_bounds__(256) void qk_norm_mrope_kernel(const RopeParams p, const RopeFreqs f) {
+  const double* inv_freq = f.inv;
   constexpr int HALF = HD / 2;
-  constexpr int ROWS_PER_WAVE = 64 / HALF;          // 1 (hd 128) or 2 (hd 64)
+  constexpr int LPR = HALF / 4;                     // lanes per head row
+  constexpr int ROWS_PER_WAVE = 64 / LPR;           // 4 (hd 128) or 8 (hd 64)
   constexpr int ROWS_PER_PASS = 4 * ROWS_PER_WAVE;  // 4 waves
-  typedef typename std::conditional<DT == DT_F32, float, uint16_t>::type T;
   const int s = blockIdx.x;
   const int lane = threadIdx.x & 63;
-  const int i = lane % HALF;
-  const int sub = (threadIdx.x >> 6) * ROWS_PER_WAVE + lane / HALF;
+  const int i0 = 4 * (lane % LPR);
+  const int sub = (threadIdx.x >> 6) * ROWS_PER_WAVE + lane / LPR;
 
-  int axis = 0;
-  if (i % 3 == 1 && i < 3 * p.sec_h) axis = 1;
-  else if (i % 3 == 2 && i < 3 * p.sec_w) axis = 2;
-  const double pos = static_cast<double>(p.pos[static_cast<int64_t>(axis) * p.S + s]);
-  const double inv = exp2(-(2.0 * i / HD) * p.log2_theta);
-  const double phi = pos * inv;
-  const double two_pi = 6.283185307179586476925286766559;
-  const double red = phi - two_pi * rint(phi / two_pi);
-  float sn, cs;
-  sincosf(static_cast<float>(red), &sn, &cs);
+  float cs[4], sn[4], qa[4], qb[4], ka[4], kb[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int i = i0 + e;
+    int axis = 0;
+    if (i % 3 == 1 && i < 3 * p.sec_h) axis = 1;
+    else if (i % 3 == 2 && i < 3 * p.sec_w) axis = 2;
+    const double pos = static_cast<double>(p.pos[static_cast<int64_t>(axis) * p.S + s]);
+    const double phi = pos * inv_freq[i];
+    const double two_pi = 6.283185307179586476925286766559;
+    const double red = fma(-two_pi, rint(phi * (1.0 / two_pi)), phi);
+    sincosf(static_cast<float>(red), &sn[e], &cs[e]);
+    qa[e] = load_elem(p.q_norm, i, p.norm_dt);
+    qb[e] = load_elem(p.q_norm, i + HALF, p.norm_dt);
+    ka[e] = load_elem(p.k_norm, i, p.norm_dt);
+    kb[e] = load_elem(p.k_norm, i + HALF, p.norm_dt);
+  }
 
   const int nrows = p.nh + p.nkv;
   for (int h = sub; h < nrows; h += ROWS_PER_PASS) {
     const bool is_q = h < p.nh;
-    T* row = is_q ? static_cast<T*>(p.q) + static_cast<int64_t>(s) * p.q_stride + static_cast<int64_t>(h) * HD
-                  : static_cast<T*>(p.k) + static_cast<int64_t>(s) * p.k_stride + static_cast<int64_t>(h - p.nh) * HD;
-    const void* nw = is_q ? p.q_norm : p.k_norm;
-    float a = load_elem(row, i, DT);
-    float b = load_elem(row, i + HALF, DT);
-    const float ss = group_sum(a * a + b * b, HALF);
+    void* row = is_q ? static_cast<void*>(static_cast<char*>(p.q) +
+                                          (static_cast<int64_t>(s) * p.q_stride + static_cast<int64_t>(h) * HD) *
+                                              (DT == DT_F32 ? 4 : 2))
+                     : static_cast<void*>(static_cast<char*>(p.k) +
+                                          (static_cast<int64_t>(s) * p.k_stride +
+                                           static_cast<int64_t>(h - p.nh) * HD) *
+                                              (DT == DT_F32 ? 4 : 2));
+    float a[4], b[4];
+    load4<DT>(row, i0, a);
+    load4<DT>(row, i0 + HALF, b);
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ss = fmaf(a[e], a[e], fmaf(b[e], b[e], ss));
+    ss = group_sum(ss, LPR);
     const float r = 1.0f / sqrtf(ss / static_cast<float>(HD) + p.eps);
-    a = a * r * load_elem(nw, i, p.norm_dt);
-    b = b * r * load_elem(nw, i + HALF, p.norm_dt);
-    const float ra = a * cs - b * sn;
-    const float rb = a * sn + b * cs;
-    if (DT == DT_F32) {
-      row[i] = ra;
-      row[i + HALF] = rb;
-    } else if (DT == DT_BF16) {
-      row[i] = f2bf(ra);
-      row[i + HALF] = f2bf(rb);
-    } else {
-      row[i] = f2h(ra);
-      row[i + HALF] = f2h(rb);
+    float ra[4], rb[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float x = a[e] * r * (is_q ? qa[e] : ka[e]);
+      const float y = b[e] * r * (is_q ? qb[e] : kb[e]);
+      ra[e] = x * cs[e] - y * sn[e];
+      rb[e] = x * sn[e] + y * cs[e];
     }
+    store4<DT>(row, i0, ra);
+    store4<DT>(row, i0 + HALF, rb);
   }
 }
 
 template <int HD>
 static hipError_t rope_launch(const RopeParams& p, int dt, hipStream_t s) {
   dim3 grid(p.S), block(256);
+  // theta^(-2i/hd) for i < hd/2, in double on the host, passed with the launch
+  RopeFreqs f;
+  for (int i = 0; i < HD / 2; ++i) f.inv[i] = std::exp2(-(2.0 * i / HD) * p.log2_theta);
   switch (dt) {
-    case DT_F32: qk_norm_mrope_kernel<DT_F32, HD><<<grid, block, 0, s>>>(p); break;
-    case DT_BF16: qk_norm_mrope_kernel<DT_BF16, HD><<<grid, block, 0, s>>>(p); break;
-    case DT_F16: qk_norm_mrope_kernel<DT_F16, HD><<<grid, block, 0, s>>>(p); break;
+    case DT_F32: qk_norm_mrope_kernel<DT_F32, HD><<<grid, block, 0, s>>>(p, f); break;
+    case DT_BF16: qk_norm_mrope_kernel<DT_BF16, HD><<<grid, block, 0, s>>>(p, f); break;
+    case DT_F16: qk_norm_mrope_kernel<DT_F16, HD><<<grid, block, 0, s>>>(p, f); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
