@@ -138,12 +138,35 @@ def model_prefill_extra(cfg, layers, pos, stream, vocab):
     head_ms = kt["lm_head"][1] / kt["lm_head"][0]
     head_bytes = vocab * cfg.hidden * (2 if wdt == torch.bfloat16 else 4)
     emb_ms = kt["embed_gather"][1] / kt["embed_gather"][0]
+
+    # generation after the prompt: the prefill leaves every layer's cache, then single tokens
+    n_dec = 16
+    caches = [q3.kv_cache_alloc(spec, cfg.seq_len + n_dec) for _ in layers]
+    q3.model_prefill_logits_last(spec, layers, emb, norm, head, tokens, pos, out=out, workspace=ws, caches=caches)
+    dws = torch.empty(q3.model_decode_workspace_bytes(spec, len(layers), vocab, cfg.seq_len + n_dec),
+                      dtype=torch.uint8, device=dev)
+    dpos = torch.arange(cfg.seq_len, cfg.seq_len + n_dec, dtype=torch.int32, device=dev).repeat(3, 1).t().contiguous()
+    new_tok = torch.randint(0, vocab, (n_dec,), generator=torch.Generator().manual_seed(6)).tolist()
+
+    def gen():
+        for i in range(n_dec):
+            q3.model_decode_logits(spec, layers, emb, norm, head, new_tok[i], dpos[i], caches, cfg.seq_len + i,
+                                   out=out, workspace=dws)
+
+    gen()
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    gen()
+    torch.cuda.synchronize()
+    dec_ms = (time.perf_counter() - t) * 1e3 / n_dec
     return {"workload": f"{cfg.name}: {len(layers)} layers, seq {cfg.seq_len}, vocab {vocab} untied head",
             "ms": round(ms, 4), "tokens_per_s": round(cfg.seq_len / (ms * 1e-3), 1),
             "lm_head": {"avg_ms": round(head_ms, 4), "bound": "hbm",
                         "GB_per_s": round(head_bytes / (head_ms * 1e-3) / 1e9, 1),
                         "frac_of_hbm_peak": round(head_bytes / (head_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
             "embed_gather_ms": round(emb_ms, 4),
+            "decode_after_prompt": {"tokens": n_dec, "ms_per_token": round(dec_ms, 4),
+                                    "tokens_per_s": round(1e3 / dec_ms, 1)},
             "finite_logits": bool(torch.isfinite(out).all().item())}
 
 

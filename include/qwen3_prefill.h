@@ -339,6 +339,25 @@ int qwen3_layer_decode(const qwen3_layer_cfg *cfg, const qwen3_layer_weights *w,
                        void *stream);
 size_t qwen3_layer_decode_workspace_bytes(const qwen3_layer_cfg *cfg, int32_t capacity);
 
+/* Whole-model forms of the cache and the decode step.
+ * qwen3_model_prefill_logits_last_kv: qwen3_model_prefill_logits_last that also leaves every
+ *   layer's cache; k_caches, v_caches are HOST arrays of n_layers device pointers (layer l's
+ *   caches as for qwen3_layer_prefill_kv), capacity >= seq_len. Same workspace.
+ * qwen3_model_decode_logits: logits [vocab] fp32 of one new token (host id in [0, vocab)) at
+ *   `position` (device int32 [3]) after len tokens: the embedding row, every layer's decode step
+ *   (each appends its cache row len), final RMSNorm and the LM head. Equals the last position's
+ *   logits of a prefill over the len + 1 tokens. workspace: qwen3_model_decode_workspace_bytes. */
+int qwen3_model_prefill_logits_last_kv(const qwen3_model_cfg* cfg, const qwen3_model_weights* w,
+                                       const int32_t* tokens, int32_t seq_len, const int32_t* positions,
+                                       const int32_t* ds_rows, int32_t n_ds, const void* const* ds,
+                                       void* const* k_caches, void* const* v_caches, int32_t capacity,
+                                       float* logits, void* workspace, size_t workspace_bytes, void* stream);
+size_t qwen3_model_decode_workspace_bytes(const qwen3_model_cfg* cfg, int32_t capacity);
+int qwen3_model_decode_logits(const qwen3_model_cfg* cfg, const qwen3_model_weights* w, int32_t token,
+                              const int32_t* position, void* const* k_caches, void* const* v_caches,
+                              int32_t capacity, int32_t len, float* logits, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
 /* ---- Weight-only quantized projections ---------------------------------------------------------
  *
  * hf2q 0.1.1, qwen3vl_text/forward.rs, the dense FFN step: the converted Qwen3-VL checkpoints hold

@@ -332,3 +332,31 @@ def test_dequantize_matrix_checks(lib):
     assert lib.dequantize_matrix(ctypes.byref(L.QMatrix(0, FAKE, None)), 4, 128, 2, FAKE, None) == 1
     assert lib.dequantize_matrix(ctypes.byref(m), 0, 128, 2, FAKE, None) == 1
     assert lib.dequantize_matrix(ctypes.byref(L.QMatrix(2, FAKE, None)), 4, 128, 2, FAKE, None) == 1
+
+
+def test_model_decode_argument_checks(lib):
+    m = _model_cfg(n_layers=2, vocab=100)
+    lw = (L.LayerWeights * 2)(_weights(), _weights())
+    mw = L.ModelWeights(FAKE, lw, FAKE, None)
+    ws = ctypes.c_void_p(0x100000)
+    need = lib.qwen3_model_decode_workspace_bytes(ctypes.byref(m), 64)
+    assert need > lib.qwen3_layer_decode_workspace_bytes(ctypes.byref(m.layer), 64)
+    kc = (ctypes.c_void_p * 2)(0x2000, 0x3000)
+    vc = (ctypes.c_void_p * 2)(0x4000, 0x5000)
+
+    def call(token=5, length=3, caches=(kc, vc), ws_bytes=need, cap=64):
+        return lib.qwen3_model_decode_logits(ctypes.byref(m), ctypes.byref(mw), token, FAKE, caches[0], caches[1],
+                                             cap, length, FAKE, ws, ws_bytes, None)
+    assert call(token=100) == 1 and "vocab" in lib.qwen3_last_error().decode()
+    assert call(token=-1) == 1
+    assert call(length=64) == 1 and "capacity" in lib.qwen3_last_error().decode()
+    assert call(caches=(kc, None)) == 1
+    assert call(caches=(kc, (ctypes.c_void_p * 2)(0x2000, 0x5000))) == 1      # layer 0: same k and v
+    assert call(ws_bytes=need - 256) == 3
+    # the model prefill that leaves the caches checks them the same way
+    tok = (ctypes.c_int32 * 16)(*range(16))
+    mws = lib.qwen3_model_workspace_bytes(ctypes.byref(m), 16)
+    assert lib.qwen3_model_prefill_logits_last_kv(ctypes.byref(m), ctypes.byref(mw), tok, 16, FAKE, None, 0, None,
+                                                  kc, vc, 15, FAKE, ws, mws, None) == 1
+    assert lib.qwen3_model_prefill_logits_last_kv(ctypes.byref(m), ctypes.byref(mw), tok, 16, FAKE, None, 0, None,
+                                                  None, None, 16, FAKE, ws, mws, None) == 1

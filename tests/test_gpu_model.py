@@ -65,3 +65,30 @@ def test_model_tied_head_equals_passing_the_table_and_no_layers():
     got = host(_run(cfg.with_seq(1), [], emb, norm, None, one, pos[:, :1], None, None))
     ref = oracle.model_prefill_logits_last(one, emb, [], norm, None, cfg, pos[:, :1])
     assert rel_err(got, ref) <= 1e-5
+
+
+@pytest.mark.parametrize("name,n_layers,vocab,s0,steps,tied", [
+    ("tiny_f32", 2, 300, 20, 5, False),
+    ("qwen3vl_2b_text", 2, 4096, 64, 2, True),
+    ("qwen3vl_2b_image", 2, 2048, 1200, 2, False),   # the prompt holds the image span
+])
+def test_model_decode_continues_the_prefill(name, n_layers, vocab, s0, steps, tied):
+    """Whole-model prefill with every layer's cache, then decode steps: the logits of each new
+    token equal the oracle's last-position logits of the prefill over the longer sequence."""
+    cfg, layers, emb, norm, head, tokens, pos, _, _ = _model(synth.get_config(name), n_layers, vocab, tied=tied)
+    d = cfg.dtype
+    spec = q3.LayerSpec.of(cfg)
+    dl = [dev_weights(w, d) for w in layers]
+    de, dn, dh = dev(emb, d), dev(norm, d), None if head is None else dev(head, d)
+    caches = [q3.kv_cache_alloc(spec, s0 + steps) for _ in range(n_layers)]
+    first = q3.model_prefill_logits_last(spec, dl, de, dn, dh, tokens[:s0].tolist(), dev_i32(pos[:, :s0]),
+                                         caches=caches)
+    plain = q3.model_prefill_logits_last(spec, dl, de, dn, dh, tokens[:s0].tolist(), dev_i32(pos[:, :s0]))
+    torch.cuda.synchronize()
+    assert torch.equal(first, plain)
+    for t in range(s0, s0 + steps):
+        got = host(q3.model_decode_logits(spec, dl, de, dn, dh, int(tokens[t]), dev_i32(pos[:, t]), caches, t))
+        ref = oracle.model_prefill_logits_last(tokens[:t + 1], emb, layers, norm, head, cfg, pos[:, :t + 1])
+        err = rel_err(got, ref)
+        log_err(f"model_decode[{name},L{n_layers},V{vocab},t={t}]", err)
+        assert err <= TOL[cfg.dtype], (t, err)

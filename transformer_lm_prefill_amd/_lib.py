@@ -20,6 +20,7 @@ EXPORTS = ("qwen3_layer_workspace_bytes", "qwen3_layer_prefill", "qk_norm_mrope"
            "gqa_decode_attention_workspace_bytes", "qwen3_layer_decode",
            "qwen3_layer_decode_workspace_bytes", "dequantize_matrix",
            "qwen3_layer_quant_workspace_bytes", "qwen3_layer_prefill_quant", "qwen3_layer_decode_quant",
+           "qwen3_model_prefill_logits_last_kv", "qwen3_model_decode_workspace_bytes", "qwen3_model_decode_logits",
            "qwen3_last_error", "qwen3_timing_enable", "qwen3_timing_collect")
 
 
@@ -138,6 +139,14 @@ def load():
     lib.qwen3_layer_decode_quant.argtypes = [ctypes.POINTER(LayerCfg), ctypes.POINTER(LayerQWeights),
                                              vp, vp, vp, vp, vp, i32, i32, vp, sz, vp]
     lib.qwen3_layer_decode_quant.restype = ctypes.c_int
+    lib.qwen3_model_prefill_logits_last_kv.argtypes = [ctypes.POINTER(ModelCfg), ctypes.POINTER(ModelWeights),
+                                                       vp, i32, vp, vp, i32, vp, vp, vp, i32, vp, vp, sz, vp]
+    lib.qwen3_model_prefill_logits_last_kv.restype = ctypes.c_int
+    lib.qwen3_model_decode_workspace_bytes.argtypes = [ctypes.POINTER(ModelCfg), i32]
+    lib.qwen3_model_decode_workspace_bytes.restype = sz
+    lib.qwen3_model_decode_logits.argtypes = [ctypes.POINTER(ModelCfg), ctypes.POINTER(ModelWeights), i32, vp, vp,
+                                              vp, i32, i32, vp, vp, sz, vp]
+    lib.qwen3_model_decode_logits.restype = ctypes.c_int
     lib.qwen3_last_error.argtypes = []
     lib.qwen3_last_error.restype = ctypes.c_char_p
     lib.qwen3_timing_enable.argtypes = [ctypes.c_int]

@@ -567,10 +567,42 @@ size_t qwen3_model_workspace_bytes(const qwen3_model_cfg* cfg, int32_t seq_len) 
   return model_layout(cfg, seq_len).total;
 }
 
-int qwen3_model_prefill_logits_last(const qwen3_model_cfg* cfg, const qwen3_model_weights* w,
-                                    const int32_t* tokens, int32_t seq_len, const int32_t* positions,
-                                    const int32_t* ds_rows, int32_t n_ds, const void* const* ds, float* logits,
-                                    void* workspace, size_t workspace_bytes, void* stream) {
+static int check_model(const qwen3_model_cfg* cfg, const qwen3_model_weights* w, const float* logits) {
+  if (!cfg) return fail(QWEN3_ERR_INVALID_ARG, "cfg is NULL");
+  int st = check_cfg(&cfg->layer);
+  if (st) return st;
+  if (cfg->n_layers < 0) return fail(QWEN3_ERR_INVALID_ARG, "n_layers (%d) must be >= 0", cfg->n_layers);
+  if (cfg->vocab < 1) return fail(QWEN3_ERR_INVALID_ARG, "vocab (%d) must be >= 1", cfg->vocab);
+  if (!w || !w->token_embd || !w->output_norm || (cfg->n_layers > 0 && !w->layers))
+    return fail(QWEN3_ERR_INVALID_ARG, "model weights (token_embd, output_norm, layers) must not be NULL");
+  if (!logits) return fail(QWEN3_ERR_INVALID_ARG, "logits is NULL");
+  if (misaligned16({w->token_embd, w->output_norm, w->lm_head, logits}))
+    return fail(QWEN3_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  return QWEN3_OK;
+}
+
+// Per-layer caches of a model call: host arrays of n_layers device pointers, both given or both
+// NULL; each layer's two caches distinct and 16-byte aligned.
+static int check_model_caches(const qwen3_model_cfg* cfg, void* const* kc, void* const* vc, int32_t capacity,
+                              int32_t need_rows, bool required) {
+  if (cfg->n_layers == 0) return QWEN3_OK;  // no layer, no cache
+  if ((kc == nullptr) != (vc == nullptr)) return fail(QWEN3_ERR_INVALID_ARG, "k_caches and v_caches go together");
+  if (!kc) return required ? fail(QWEN3_ERR_INVALID_ARG, "k_caches / v_caches is NULL") : QWEN3_OK;
+  if (capacity < need_rows)
+    return fail(QWEN3_ERR_INVALID_ARG, "capacity (%d) must be >= %d", capacity, need_rows);
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    if (!kc[l] || !vc[l] || kc[l] == vc[l])
+      return fail(QWEN3_ERR_INVALID_ARG, "layer %d: caches must be two distinct non-NULL buffers", l);
+    if (misaligned16({kc[l], vc[l]})) return fail(QWEN3_ERR_INVALID_ARG, "cache pointers must be 16-byte aligned");
+  }
+  return QWEN3_OK;
+}
+
+static int model_prefill_impl(const qwen3_model_cfg* cfg, const qwen3_model_weights* w, const int32_t* tokens,
+                              int32_t seq_len, const int32_t* positions, const int32_t* ds_rows, int32_t n_ds,
+                              const void* const* ds, void* const* k_caches, void* const* v_caches,
+                              int32_t capacity, float* logits, void* workspace, size_t workspace_bytes,
+                              void* stream) {
   if (!cfg) return fail(QWEN3_ERR_INVALID_ARG, "cfg is NULL");
   int st = check_cfg(&cfg->layer);
   if (st) return st;
@@ -622,13 +654,105 @@ int qwen3_model_prefill_logits_last(const qwen3_model_cfg* cfg, const qwen3_mode
   const size_t lbytes = L.total - L.layer;
   for (int l = 0; l < cfg->n_layers; ++l) {
     const bool with_ds = l < nds && n_ds > 0;
-    st = qwen3_layer_prefill(&cfg->layer, &w->layers[l], x, x, S, positions, with_ds ? ds_rows : nullptr,
-                             with_ds ? n_ds : 0, with_ds ? ds[l] : nullptr, ws + L.layer, lbytes, stream);
+    st = k_caches ? qwen3_layer_prefill_kv(&cfg->layer, &w->layers[l], x, x, S, positions,
+                                           with_ds ? ds_rows : nullptr, with_ds ? n_ds : 0,
+                                           with_ds ? ds[l] : nullptr, k_caches[l], v_caches[l], capacity,
+                                           ws + L.layer, lbytes, stream)
+                  : qwen3_layer_prefill(&cfg->layer, &w->layers[l], x, x, S, positions, with_ds ? ds_rows : nullptr,
+                                        with_ds ? n_ds : 0, with_ds ? ds[l] : nullptr, ws + L.layer, lbytes, stream);
     if (st) return st;
   }
   if ((st = run_rmsnorm(x + static_cast<size_t>(S - 1) * H, w->output_norm, wdt, xlast, QWEN3_F32, 1, H,
                         cfg->layer.rms_eps, s)))
     return st;
+  {
+    KTimer t("lm_head", s);
+    e = q3::launch_gemv_rows(w->lm_head ? w->lm_head : w->token_embd, wdt, xlast, logits, cfg->vocab, H, s);
+    if (e != hipSuccess) return hip_fail(e, "lm_head launch");
+  }
+  return QWEN3_OK;
+}
+
+int qwen3_model_prefill_logits_last(const qwen3_model_cfg* cfg, const qwen3_model_weights* w,
+                                    const int32_t* tokens, int32_t seq_len, const int32_t* positions,
+                                    const int32_t* ds_rows, int32_t n_ds, const void* const* ds, float* logits,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  return model_prefill_impl(cfg, w, tokens, seq_len, positions, ds_rows, n_ds, ds, nullptr, nullptr, 0, logits,
+                            workspace, workspace_bytes, stream);
+}
+
+int qwen3_model_prefill_logits_last_kv(const qwen3_model_cfg* cfg, const qwen3_model_weights* w,
+                                       const int32_t* tokens, int32_t seq_len, const int32_t* positions,
+                                       const int32_t* ds_rows, int32_t n_ds, const void* const* ds,
+                                       void* const* k_caches, void* const* v_caches, int32_t capacity,
+                                       float* logits, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!cfg) return fail(QWEN3_ERR_INVALID_ARG, "cfg is NULL");
+  int st = check_model_caches(cfg, k_caches, v_caches, capacity, seq_len, true);
+  if (st) return st;
+  return model_prefill_impl(cfg, w, tokens, seq_len, positions, ds_rows, n_ds, ds, k_caches, v_caches, capacity,
+                            logits, workspace, workspace_bytes, stream);
+}
+
+struct ModelDecodeWorkspace {
+  size_t x, xlast, layer, total;
+};
+
+static ModelDecodeWorkspace model_decode_layout(const qwen3_model_cfg* c, int32_t capacity) {
+  ModelDecodeWorkspace m{};
+  const size_t H = c->layer.hidden;
+  m.x = 0;
+  m.xlast = m.x + align256(H * 4);
+  m.layer = m.xlast + align256(H * 4);
+  m.total = m.layer + qwen3_layer_decode_workspace_bytes(&c->layer, capacity);
+  return m;
+}
+
+size_t qwen3_model_decode_workspace_bytes(const qwen3_model_cfg* cfg, int32_t capacity) {
+  if (!cfg || capacity < 1 || cfg->n_layers < 0) return 0;
+  const size_t layer = qwen3_layer_decode_workspace_bytes(&cfg->layer, capacity);
+  if (layer == 0) return 0;
+  return model_decode_layout(cfg, capacity).total;
+}
+
+int qwen3_model_decode_logits(const qwen3_model_cfg* cfg, const qwen3_model_weights* w, int32_t token,
+                              const int32_t* position, void* const* k_caches, void* const* v_caches,
+                              int32_t capacity, int32_t len, float* logits, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  int st = check_model(cfg, w, logits);
+  if (st) return st;
+  if (token < 0 || token >= cfg->vocab)
+    return fail(QWEN3_ERR_INVALID_ARG, "token id %d is outside [0, vocab = %d)", token, cfg->vocab);
+  if (!position) return fail(QWEN3_ERR_INVALID_ARG, "position is NULL");
+  if (len < 0 || len >= capacity)
+    return fail(QWEN3_ERR_INVALID_ARG, "len (%d) must be in [0, capacity = %d): the new token takes row len", len,
+                capacity);
+  if (cfg->n_layers > 0 && (st = check_model_caches(cfg, k_caches, v_caches, capacity, len + 1, true))) return st;
+  const ModelDecodeWorkspace L = model_decode_layout(cfg, capacity);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(QWEN3_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", L.total, workspace_bytes,
+                workspace ? "" : ", NULL pointer");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(QWEN3_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int H = cfg->layer.hidden;
+  const qwen3_dtype wdt = cfg->layer.wdtype;
+  char* ws = static_cast<char*>(workspace);
+  float* x = reinterpret_cast<float*>(ws + L.x);
+  float* xlast = reinterpret_cast<float*>(ws + L.xlast);
+  hipError_t e;
+  {
+    KTimer t("embed_gather", s);
+    e = q3::launch_embed_row(w->token_embd, wdt, token, x, H, s);
+    if (e != hipSuccess) return hip_fail(e, "embed_row launch");
+  }
+  const size_t lbytes = L.total - L.layer;
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    st = qwen3_layer_decode(&cfg->layer, &w->layers[l], x, x, position, k_caches[l], v_caches[l], capacity, len,
+                            ws + L.layer, lbytes, stream);
+    if (st) return st;
+  }
+  if ((st = run_rmsnorm(x, w->output_norm, wdt, xlast, QWEN3_F32, 1, H, cfg->layer.rms_eps, s))) return st;
   {
     KTimer t("lm_head", s);
     e = q3::launch_gemv_rows(w->lm_head ? w->lm_head : w->token_embd, wdt, xlast, logits, cfg->vocab, H, s);

@@ -26,6 +26,8 @@ hipError_t launch_deepstack_add(float* y, const int32_t* rows, const void* ds, i
 // x[s, :] = table[tokens[s], :] as fp32 (tokens are device int32, already in range).
 hipError_t launch_embed_gather(const int32_t* tokens, const void* table, int dt, float* x, int S, int hidden,
                                hipStream_t s);
+// x[:] = table[token, :] as fp32, token already range-checked on the host.
+hipError_t launch_embed_row(const void* table, int dt, int64_t token, float* x, int hidden, hipStream_t s);
 // y[r] = sum_k W[r, k] x[k], W [rows, hidden] of dt, x and y fp32 (hidden % 8 == 0).
 hipError_t launch_gemv_rows(const void* W, int dt, const float* x, float* y, int rows, int hidden, hipStream_t s);
 

@@ -69,6 +69,27 @@ hipError_t launch_embed_gather(const int32_t* tokens, const void* table, int dt,
   return hipGetLastError();
 }
 
+// x[:] = one table row as fp32 (the row chosen on the host).
+template <int DT>
+__global__ __launch_bounds__(256) void embed_row_kernel(const void* row, float* x, int hidden) {
+  for (int i = threadIdx.x * 8; i < hidden; i += 256 * 8) {
+    float v[8];
+    load8<DT>(row, i, v);
+    *reinterpret_cast<f32x4*>(x + i) = f32x4{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4*>(x + i + 4) = f32x4{v[4], v[5], v[6], v[7]};
+  }
+}
+
+hipError_t launch_embed_row(const void* table, int dt, int64_t token, float* x, int hidden, hipStream_t s) {
+  if (hidden % 8 != 0) return hipErrorInvalidValue;
+  const int64_t off = token * hidden;
+  if (dt == DT_BF16) embed_row_kernel<DT_BF16><<<1, 256, 0, s>>>(static_cast<const uint16_t*>(table) + off, x, hidden);
+  else if (dt == DT_F16) embed_row_kernel<DT_F16><<<1, 256, 0, s>>>(static_cast<const uint16_t*>(table) + off, x, hidden);
+  else if (dt == DT_F32) embed_row_kernel<DT_F32><<<1, 256, 0, s>>>(static_cast<const float*>(table) + off, x, hidden);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 hipError_t launch_gemv_rows(const void* W, int dt, const float* x, float* y, int rows, int hidden, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   if (hidden % 8 != 0) return hipErrorInvalidValue;

@@ -285,14 +285,61 @@ def model_workspace_bytes(spec, n_layers, vocab, seq_len, n_deepstack_layers=0):
     return int(_lib.load().qwen3_model_workspace_bytes(ctypes.byref(m), int(seq_len)))
 
 
+def _model_weights(layers, token_embd, output_norm, lm_head):
+    lw = (_lib.LayerWeights * max(len(layers), 1))()
+    for i, w in enumerate(layers):
+        lw[i] = _lib.LayerWeights(*[_ptr(w[n]) for n in WEIGHT_NAMES])
+    return _lib.ModelWeights(_ptr(token_embd), lw if layers else None, _ptr(output_norm), _ptr(lm_head)), lw
+
+
+def _cache_arrays(caches):
+    """[(k, v) per layer] -> two host arrays of device pointers (or None, None)."""
+    if caches is None:
+        return None, None
+    for k, v in caches:
+        _ptr(k), _ptr(v)
+    kc = (ctypes.c_void_p * max(len(caches), 1))(*[k.data_ptr() for k, _ in caches])
+    vc = (ctypes.c_void_p * max(len(caches), 1))(*[v.data_ptr() for _, v in caches])
+    return kc, vc
+
+
+def model_decode_workspace_bytes(spec, n_layers, vocab, capacity):
+    m = _model_cfg(spec, n_layers, vocab, 0)
+    return int(_lib.load().qwen3_model_decode_workspace_bytes(ctypes.byref(m), int(capacity)))
+
+
+def model_decode_logits(spec, layers, token_embd, output_norm, lm_head, token, position, caches, length,
+                        out=None, workspace=None):
+    """qwen3_model_decode_logits: logits [vocab] float32 of one new token (host int id) at
+    `position` (int32 [3] on the GPU) after `length` cached tokens; caches: [(k, v)] per layer
+    as from kv_cache_alloc, filled by model_prefill_logits_last(..., caches=...)."""
+    lib = _lib.load()
+    vocab = int(token_embd.shape[0])
+    m = _model_cfg(spec, len(layers), vocab, 0)
+    cap = int(caches[0][0].shape[1]) if caches else 1
+    if out is None:
+        out = torch.empty(vocab, dtype=torch.float32, device=token_embd.device)
+    need = int(lib.qwen3_model_decode_workspace_bytes(ctypes.byref(m), cap))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=token_embd.device)
+    mw, _keep = _model_weights(layers, token_embd, output_norm, lm_head)
+    kc, vc = _cache_arrays(caches)
+    _lib.check(lib.qwen3_model_decode_logits(ctypes.byref(m), ctypes.byref(mw), int(token), _ptr(position), kc, vc,
+                                             cap, int(length), _ptr(out), _ptr(workspace), int(workspace.numel()),
+                                             _stream()))
+    return out
+
+
 def model_prefill_logits_last(spec, layers, token_embd, output_norm, lm_head, tokens, positions,
-                              ds_rows=None, ds=None, out=None, workspace=None):
+                              ds_rows=None, ds=None, out=None, workspace=None, caches=None):
     """qwen3_model_prefill_logits_last: logits [vocab] float32 of the last prompt position.
 
     layers: list of weight mappings (one per decoder layer); token_embd [vocab, H],
     output_norm [H], lm_head [vocab, H] or None (tied) on the GPU in spec's dtype; tokens: a
     host sequence of int token ids; positions [3, S] int32 on the GPU; ds_rows [n] int32 and ds
     a list of [n, H] slabs (one per DeepStack layer, the first len(ds) layers) or None.
+    caches: None, or [(k, v)] per layer (kv_cache_alloc) to be filled with every layer's k', v
+    (qwen3_model_prefill_logits_last_kv).
     """
     lib = _lib.load()
     vocab = int(token_embd.shape[0])
@@ -315,9 +362,16 @@ def model_prefill_logits_last(spec, layers, token_embd, output_norm, lm_head, to
         for t in ds:
             _ptr(t)  # device and contiguity checks
     n_ds = 0 if ds_rows is None else int(ds_rows.numel())
-    _lib.check(lib.qwen3_model_prefill_logits_last(
-        ctypes.byref(m), ctypes.byref(mw), tok, int(s), _ptr(positions), _ptr(ds_rows), n_ds, slabs,
-        _ptr(out), _ptr(workspace), int(workspace.numel()), _stream()))
+    if caches is None:
+        _lib.check(lib.qwen3_model_prefill_logits_last(
+            ctypes.byref(m), ctypes.byref(mw), tok, int(s), _ptr(positions), _ptr(ds_rows), n_ds, slabs,
+            _ptr(out), _ptr(workspace), int(workspace.numel()), _stream()))
+    else:
+        kc, vc = _cache_arrays(caches)
+        _lib.check(lib.qwen3_model_prefill_logits_last_kv(
+            ctypes.byref(m), ctypes.byref(mw), tok, int(s), _ptr(positions), _ptr(ds_rows), n_ds, slabs, kc, vc,
+            int(caches[0][0].shape[1]) if caches else 0, _ptr(out), _ptr(workspace), int(workspace.numel()),
+            _stream()))
     return out
 
 
