@@ -477,10 +477,22 @@ def main():
 
     kernels = {k: {"launches": v[0], "avg_ms": round(v[1] / v[0], 4)} for k, v in kt.items()}
 
-    model = None if args.no_model else model_prefill_extra(cfg, layers, pos, stream, args.vocab)
-    bidir = None if args.no_bidirectional else bidirectional_extra()
-    decode = None if args.no_decode else decode_extra(cfg, layers, x0, pos)
-    quant = None if args.no_quant else quant_extra(cfg, x0, pos)
+    def extra(skip, fn, *a):
+        """A secondary measurement; a failure is reported in its field, not by losing the line."""
+        if skip:
+            return None
+        try:
+            return fn(*a)
+        except Exception as e:  # noqa: BLE001
+            print(f"bench.py: {fn.__name__} failed: {e!r}", file=sys.stderr)
+            return {"error": repr(e)}
+        finally:
+            torch.cuda.synchronize()
+
+    model = extra(args.no_model, model_prefill_extra, cfg, layers, pos, stream, args.vocab)
+    bidir = extra(args.no_bidirectional, bidirectional_extra)
+    decode = extra(args.no_decode, decode_extra, cfg, layers, x0, pos)
+    quant = extra(args.no_quant, quant_extra, cfg, x0, pos)
 
     cpu = None
     if not args.no_cpu_baseline:
