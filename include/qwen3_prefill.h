@@ -2,7 +2,7 @@
  * qwen3_prefill.h — C ABI of the MI355X (gfx950) Qwen3/Qwen3-VL text decoder-layer prefill.
  *
  * The library computes the full-sequence causal prefill of one Qwen3/Qwen3-VL text
- * decoder layer (no KV cache, every token at once):
+ * decoder layer (every token at once):
  *
  *   xn = RMSNorm(x, attn_norm)                                 plain weight, eps inside the sqrt
  *   q, k, v = xn Wq^T, xn Wk^T, xn Wv^T                        no biases
@@ -11,6 +11,10 @@
  *   y1 = x + o Wo^T
  *   y2 = y1 + (silu(RMSNorm(y1, ffn_norm) Wg^T) * (RMSNorm(y1, ffn_norm) Wu^T)) Wd^T
  *   y2[rows[i]] += deepstack[i]                                 optional, image-token rows only
+ *
+ * Around it: the whole-model text prefill to the last position's logits, the KV cache a prefill
+ * can leave and one-token decode steps over it, bidirectional attention and rotary tables for
+ * vision-tower blocks, and weight-only quantized (Q4_0, int8-row) projections (sections below).
  *
  * Sources (web pages, cited by title and item):
  *   hf2q 0.1.1, qwen3vl_text/forward.rs — module doc (the per-layer graph of the peer

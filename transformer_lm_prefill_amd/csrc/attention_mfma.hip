@@ -1,8 +1,10 @@
-// Causal grouped-query flash attention, 16-bit (fp16 or bf16) operands, head_dim 128, for gfx950.
+// Grouped-query flash attention, 16-bit (fp16 or bf16) operands, head_dim 64 or 128, for gfx950.
 //
-// Computes o[s, h] = sum_{j<=s} softmax_j(scale * q[s,h] . k[j,g]) v[j,g] with
+// Causal: o[s, h] = sum_{j<=s} softmax_j(scale * q[s,h] . k[j,g]) v[j,g] with
 // g = h / (nh / nkv) (cortiq-engine 0.8.21, qwen3te.rs: the per-pair causal loop and
 // `attention_gemm`; hf2q 0.1.1, qwen3vl_text/forward.rs: SDPA causal, scale 1/sqrt(head_dim)).
+// Bidirectional (a runtime flag): every key j < S (inferencelayer 0.2.3, vision.rs, the vision
+// block's `attention`; cortiq-engine 0.8.51, onevision2.rs, `attend`).
 // Unlike those pages, no score matrix is formed: keys stream through LDS in tiles of 64 and
 // each query row keeps an online softmax (running maximum and sum, fp32, base 2).
 //

@@ -139,7 +139,7 @@ struct GemmParams {
 hipError_t launch_gemm_mfma(const GemmParams& p, int epi, int op, bool b_bf16, int nb, hipStream_t s);
 int gemm_pick_nb(int M, int N, int epi);
 
-// ---- 16-bit causal GQA flash attention, head_dim 128 --------------------------------------
+// ---- 16-bit GQA flash attention (causal or bidirectional), head_dim 64 or 128 ---------------
 struct AttnParams {
   const uint16_t* q; const uint16_t* k; const uint16_t* v; uint16_t* o;
   int64_t q_stride, k_stride, v_stride, o_stride;  // elements between consecutive tokens
