@@ -362,3 +362,35 @@ def test_32b_encoder_sampled_rows():
     print(f"32B encoder sampled rows err {err:.3e}")
     log_err("32b_encoder[sampled rows]", err)
     assert err <= TOL["bf16"]
+
+
+# ------------------------------------------------------------------ other head layouts
+
+_SHAPES = {
+    # name: hidden, n_heads, n_kv_heads, head_dim, ffn, seq_len, sections
+    "hd64_mha": (1024, 16, 16, 64, 2048, 300, (12, 10, 10)),
+    "hd64_gqa4": (1024, 16, 4, 64, 2048, 333, (12, 10, 10)),
+    "hd128_gqa8": (2048, 16, 2, 128, 2048, 200, (24, 20, 20)),
+}
+
+
+@pytest.mark.parametrize("shape", sorted(_SHAPES))
+def test_layer_and_decode_other_head_layouts(shape):
+    """The layer (16-bit path) and a decode step after it on head layouts the named workloads do
+    not use: head_dim 64 with and without grouping, 8 query heads per KV head."""
+    h, nh, nkv, hd, f, s, sec = _SHAPES[shape]
+    cfg = synth.LayerConfig(name=shape, hidden=h, n_heads=nh, n_kv_heads=nkv, head_dim=hd, ffn=f,
+                            seq_len=s + 1, sections=sec, theta=1e6)
+    w = synth.make_layer_weights(cfg)
+    x, pos = synth.make_x(cfg), synth.make_positions(cfg)
+    ref = oracle.layer_prefill(x, w, cfg, pos)
+    spec = q3.LayerSpec.of(cfg)
+    dw = dev_weights(w, cfg.dtype)
+    kc, vc = q3.kv_cache_alloc(spec, s + 1)
+    y = host(q3.layer_prefill_kv(spec, dw, dev(x[:s]), dev_i32(pos[:, :s]), kc, vc))
+    err = rel_err(y, ref[:s])
+    yd = host(q3.layer_decode(spec, dw, dev(x[s]), dev_i32(pos[:, s]), kc, vc, s))
+    err_d = rel_err(yd, ref[s])
+    log_err(f"layer[{shape}]", err)
+    log_err(f"layer_decode[{shape}]", err_d)
+    assert err <= TOL[cfg.dtype] and err_d <= TOL[cfg.dtype], (err, err_d)
