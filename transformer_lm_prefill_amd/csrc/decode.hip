@@ -301,10 +301,11 @@ hipError_t launch_decode_attention(const DecodeAttnParams& p, int hd, int cache_
 }
 
 // ---- decode projections ---------------------------------------------------------------------
-// Wave = 4 output rows (SwiGLU: 4 gate rows and the matching 4 up rows); lane l covers the
-// 8-element chunks l, l + 64, ... of each row; fp32 accumulation, then a wave reduction. The
-// weight loads of U chunks of every row are issued together before any arithmetic, so each
-// wave keeps 16 loads of 16 bytes in flight.
+// Workgroup = 4 output rows (SwiGLU: 4 gate rows and the matching 4 up rows), its four waves
+// splitting K; fp32 accumulation, wave reductions, then the four partial sums meet in LDS. The
+// weight loads of U chunks of every row are issued together before any arithmetic (8 loads of
+// 16 bytes in flight per wave), and even the smaller matrices spread over enough workgroups to
+// hide the load latency.
 constexpr int kGvRows = 4;
 
 // 8 consecutive weights as raw 16-byte words (two words for fp32).
@@ -347,10 +348,13 @@ template <int DT, int EPI>
 __global__ __launch_bounds__(256) void gemv_epi_kernel(GemvParams p) {
   constexpr int ES = DT == DT_F32 ? 4 : 2;
   constexpr int NR = EPI == GV_SWIGLU ? 2 * kGvRows : kGvRows;
-  constexpr int U = (DT == DT_F32 ? 8 : 16) / NR;   // chunks per row loaded together
+  constexpr int U = (DT == DT_F32 ? 8 : 8) / NR > 0 ? (DT == DT_F32 ? 8 : 8) / NR : 1;  // chunks per row per pass
+  __shared__ float red[4][NR];
   const int lane = threadIdx.x & 63;
-  const int r0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * kGvRows;
-  if (r0 >= p.rows) return;
+  const int wave = threadIdx.x >> 6;
+  // the workgroup's four waves share the same rows and split K: wave w takes the 8-element
+  // chunks w*64 + lane, (w + 4)*64 + lane, ...
+  const int r0 = blockIdx.x * kGvRows;
   const char* rowp[NR];
 #pragma unroll
   for (int j = 0; j < kGvRows; ++j) {
@@ -367,16 +371,17 @@ __global__ __launch_bounds__(256) void gemv_epi_kernel(GemvParams p) {
   float acc[NR];
 #pragma unroll
   for (int j = 0; j < NR; ++j) acc[j] = 0.f;
-  for (int i0 = lane * 8; i0 < p.K; i0 += 64 * 8 * U) {
+  constexpr int STEP = 4 * 64 * 8;   // elements per pass of the four waves
+  for (int i0 = (wave * 64 + lane) * 8; i0 < p.K; i0 += STEP * U) {
     Raw8<DT> w[U][NR];
     float xv[U][8];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int i = min(i0 + u * 512, p.K - 8);   // chunks past the end repeat the last, weighted 0
+      const int i = min(i0 + u * STEP, p.K - 8);   // chunks past the end repeat the last, weighted 0
 #pragma unroll
       for (int j = 0; j < NR; ++j) w[u][j] = load_raw8<DT>(rowp[j], i);
       load8<DT_F32>(p.x, i, xv[u]);
-      if (i0 + u * 512 >= p.K) {
+      if (i0 + u * STEP >= p.K) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) xv[u][e] = 0.f;
       }
@@ -388,15 +393,23 @@ __global__ __launch_bounds__(256) void gemv_epi_kernel(GemvParams p) {
   }
 #pragma unroll
   for (int j = 0; j < NR; ++j) acc[j] = wave_sum(acc[j]);
-  if (lane < kGvRows && r0 + lane < p.rows) {
-    float v = acc[0];
+  if (lane == 0) {
 #pragma unroll
-    for (int j = 1; j < kGvRows; ++j) v = lane == j ? acc[j] : v;
+    for (int j = 0; j < NR; ++j) red[wave][j] = acc[j];
+  }
+  __syncthreads();
+  if (wave == 0 && lane < kGvRows && r0 + lane < p.rows) {
+    float tot[NR];
+#pragma unroll
+    for (int j = 0; j < NR; ++j) tot[j] = (red[0][j] + red[1][j]) + (red[2][j] + red[3][j]);
+    float v = tot[0];
+#pragma unroll
+    for (int j = 1; j < kGvRows; ++j) v = lane == j ? tot[j] : v;
     const int r = r0 + lane;
     if (EPI == GV_SWIGLU) {
-      float u = acc[kGvRows];
+      float u = tot[kGvRows];
 #pragma unroll
-      for (int j = 1; j < kGvRows; ++j) u = lane == j ? acc[kGvRows + j] : u;
+      for (int j = 1; j < kGvRows; ++j) u = lane == j ? tot[kGvRows + j] : u;
       v = v / (1.f + __expf(-v)) * u;
     } else if (EPI == GV_RESID) {
       v += p.R[r];
@@ -417,7 +430,7 @@ static hipError_t gemv_dt(const GemvParams& p, int dt, unsigned blocks, hipStrea
 hipError_t launch_gemv(const GemvParams& p, int epi, int wdt, hipStream_t s) {
   if (p.rows <= 0) return hipSuccess;
   if (p.K % 8 != 0 || p.K <= 0) return hipErrorInvalidValue;
-  const unsigned blocks = static_cast<unsigned>((p.rows + 4 * kGvRows - 1) / (4 * kGvRows));
+  const unsigned blocks = static_cast<unsigned>((p.rows + kGvRows - 1) / kGvRows);
   if (epi == GV_STORE) return gemv_dt<GV_STORE>(p, wdt, blocks, s);
   if (epi == GV_RESID) return gemv_dt<GV_RESID>(p, wdt, blocks, s);
   if (epi == GV_SWIGLU) return gemv_dt<GV_SWIGLU>(p, wdt, blocks, s);
