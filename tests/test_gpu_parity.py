@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 import synth
-from util import ALLOW16, TOL, TOL16, dev, dev_i32, dev_weights, err16, host, log_err, rel_err
+from util import ALLOW16, ALLOW_ATTN16, TOL, TOL16, dev, dev_i32, dev_weights, err16, host, log_err, rel_err
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -105,7 +105,7 @@ def test_attention_16bit(fmt, s, nh, nkv):
     torch.cuda.synchronize()
     ref = oracle.causal_gqa_attention(q, k, v)
     log_err(f"attention[{fmt},S{s},{nh}/{nkv}]", rel_err(host(o), ref))
-    assert err16(host(o), ref, fmt) <= ALLOW16[fmt]
+    assert err16(host(o), ref, fmt) <= ALLOW_ATTN16[fmt]
 
 
 @pytest.mark.parametrize("s,nh,nkv,hd", [(33, 4, 2, 64), (100, 6, 3, 128), (1, 2, 2, 64)])
@@ -131,7 +131,7 @@ def test_attention_64bit_address_path(monkeypatch, fmt, s, nh, nkv):
     torch.cuda.synchronize()
     assert torch.equal(o_buf, o_64)
     ref = oracle.causal_gqa_attention(host(q), host(k), host(v))
-    assert err16(host(o_64), ref, fmt) <= ALLOW16[fmt]
+    assert err16(host(o_64), ref, fmt) <= ALLOW_ATTN16[fmt]
 
 
 def test_attention_gqa_equals_mha_with_repeated_kv():

@@ -29,7 +29,8 @@
 // its own MFMAs with its own softmax arithmetic. Iteration t, one barrier per iteration:
 //   A  S^T(t) = K(t) Q^T                  || P(t-1) = exp2(S(t-1) c - m), row sums, packing
 //   B  O^T += V^T(t-1) P^T(t-1)           || row maxima of S(t) (after the causal mask)
-//   C  running maximum update; O and the sums rescaled when it moved
+//   C  running maximum update; O and the sums rescaled when a row's maximum passed it (fp16:
+//      by more than 8 in log2 units, lazy rescaling)
 // S(t) and S(t-1) live in two register sets that swap roles every iteration.
 //
 // LDS: K and V^T tiles, two slots each. Rows are padded instead of XOR-swizzled, so every
@@ -49,10 +50,14 @@
 #include "common.h"
 #include "kernels.h"
 
-// Exponent-offset slack (log2 units): the running maximum moves only when a row's maximum
-// exceeds it by more than this. 0 keeps the row maximum's probability exactly 1.
+// Exponent-offset slack (log2 units) for fp16 operands: the running maximum (and with it the
+// rescale of O and of the row sums) moves only when a row's maximum exceeds it by more than
+// this, so after the first tiles almost no tile pays for a rescale. Probabilities then reach up
+// to 2^8 before packing to fp16 (11-bit significand at any magnitude); the largest one is no
+// longer exactly 1, which fp16 absorbs but bf16's 8-bit significand does not, so bf16 operands
+// rescale on every increase.
 #ifndef Q3_ATTN_LAZY
-#define Q3_ATTN_LAZY 0
+#define Q3_ATTN_LAZY 8
 #endif
 
 namespace q3 {
@@ -282,7 +287,7 @@ void attn_fwd_kernel(const AttnParams p) {
       for (int e = 0; e < 16; ++e) mt = fmaxf(mt, sc[b][e]);
     mt = max_halves(mt) * p.scale_log2;
     // C
-    if (__builtin_amdgcn_ballot_w64(mt > m_run + static_cast<float>(Q3_ATTN_LAZY))) {
+    if (__builtin_amdgcn_ballot_w64(mt > m_run + (OP == OP_F16 ? static_cast<float>(Q3_ATTN_LAZY) : 0.f))) {
       const float m_new = fmaxf(m_run, mt);
       const float alpha = fast_exp2(m_run - m_new);
       l_part *= alpha;
