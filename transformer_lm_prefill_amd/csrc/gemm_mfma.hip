@@ -133,7 +133,9 @@ __device__ __forceinline__ void b_seg(const GemmParams& p, int tn, int r, const 
   }
 }
 
-__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
+// silu(g) = g / (1 + e^-g), the quotient through the hardware reciprocal (about 1 ulp of fp32,
+// far below the 16-bit rounding of the stored product)
+__device__ __forceinline__ float silu_f(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
 // Epilogue shared by the kernels: stores a wave's accumulators. Accumulator element e of
 // block (mi, ni) in lane l holds row 8*(e/4) + 4*(l/32) + e%4 and column l%32 of that block.
@@ -194,21 +196,26 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p,
   const int row_base = tm * kBM + wm * (32 * MI) + 4 * (lane >> 5);
   if (EPI == EPI_SWIGLU_16) {
     uint16_t* C = static_cast<uint16_t*>(p.C);
+    // tiles wholly inside M (all but a ragged last row of tiles) store without per-row checks
+    auto store_all = [&](auto check) {
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+      for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < NI / 2; ++ni) {
-        const int f = tn * (BN / 2) + wn * (16 * NI) + ni * 32 + col_in_blk;
+        for (int ni = 0; ni < NI / 2; ++ni) {
+          const int f = tn * (BN / 2) + wn * (16 * NI) + ni * 32 + col_in_blk;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int m = row_base + mi * 32 + 8 * (e >> 2) + (e & 3);
-          if (m < p.M) {
-            const float g = acc[mi][ni][e];
-            const float u = acc[mi][ni + NI / 2][e];
-            C[static_cast<int64_t>(m) * p.ldc + f] = F::from_f32(silu_f(g) * u);
+          for (int e = 0; e < 16; ++e) {
+            const int m = row_base + mi * 32 + 8 * (e >> 2) + (e & 3);
+            if (!check.value || m < p.M) {
+              const float g = acc[mi][ni][e];
+              const float u = acc[mi][ni + NI / 2][e];
+              C[static_cast<int64_t>(m) * p.ldc + f] = F::from_f32(silu_f(g) * u);
+            }
           }
         }
-      }
+    };
+    if (tm * kBM + kBM <= p.M) store_all(std::false_type{});
+    else store_all(std::true_type{});
   } else {
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
