@@ -217,26 +217,30 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p,
     if (tm * kBM + kBM <= p.M) store_all(std::false_type{});
     else store_all(std::true_type{});
   } else {
+    auto store_all = [&](auto check) {
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+      for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni) {
-        const int n = tn * BN + wn * 32 * NI + ni * 32 + col_in_blk;
+        for (int ni = 0; ni < NI; ++ni) {
+          const int n = tn * BN + wn * 32 * NI + ni * 32 + col_in_blk;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int m = row_base + mi * 32 + 8 * (e >> 2) + (e & 3);
-          if (m < p.M) {
-            const float v = acc[mi][ni][e];
-            if (EPI == EPI_STORE_16) {
-              static_cast<uint16_t*>(p.C)[static_cast<int64_t>(m) * p.ldc + n] = F::from_f32(v);
-            } else {
-              float r = 0.f;
-              if (p.R) r = p.R[static_cast<int64_t>(m) * p.ldr + n];
-              static_cast<float*>(p.C)[static_cast<int64_t>(m) * p.ldc + n] = r + v;
+          for (int e = 0; e < 16; ++e) {
+            const int m = row_base + mi * 32 + 8 * (e >> 2) + (e & 3);
+            if (!check.value || m < p.M) {
+              const float v = acc[mi][ni][e];
+              if (EPI == EPI_STORE_16) {
+                static_cast<uint16_t*>(p.C)[static_cast<int64_t>(m) * p.ldc + n] = F::from_f32(v);
+              } else {
+                float r = 0.f;
+                if (p.R) r = p.R[static_cast<int64_t>(m) * p.ldr + n];
+                static_cast<float*>(p.C)[static_cast<int64_t>(m) * p.ldc + n] = r + v;
+              }
             }
           }
         }
-      }
+    };
+    if (tm * kBM + kBM <= p.M) store_all(std::false_type{});
+    else store_all(std::true_type{});
   }
 }
 
