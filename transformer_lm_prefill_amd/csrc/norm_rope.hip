@@ -137,8 +137,9 @@ hipError_t launch_deepstack_add(float* y, const int32_t* rows, const void* ds, i
 // consecutive rotation pairs (x_i, x_{i+hd/2}), i = i0 .. i0+3, of one head row, read and written
 // with 8-byte (16-bit types) or 16-byte (fp32) accesses, so the rotation is lane-local and the
 // hd/8 lanes of a row reduce the sum of squares with cross-lane shuffles. The angle of pair i
-// depends on the token only (not the head), so each lane forms its four cos/sin once and applies
-// them to every q and k head of the token; the norm weights are read once per lane.
+// depends on the token only (not the head): the workgroup forms the token's hd/2 cos/sin pairs
+// once, in LDS, and every lane applies its four to each q and k head row it owns; the norm
+// weights are read once per lane.
 //
 // Angle precision: theta^(-2i/hd) is formed in double on the host, phi = pos * theta^(-2i/hd)
 // in double and reduced to [-pi, pi] in double before the single-precision sincos, so its
@@ -189,10 +190,10 @@ __global__ __launch_bounds__(256) void qk_norm_mrope_kernel(const RopeParams p, 
   const int i0 = 4 * (lane % LPR);
   const int sub = (threadIdx.x >> 6) * ROWS_PER_WAVE + lane / LPR;
 
-  float cs[4], sn[4], qa[4], qb[4], ka[4], kb[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int i = i0 + e;
+  // the token's hd/2 angles, each formed once (by the first hd/2 threads) and shared via LDS
+  __shared__ float s_cs[HALF], s_sn[HALF];
+  if (threadIdx.x < HALF) {
+    const int i = threadIdx.x;
     int axis = 0;
     if (i % 3 == 1 && i < 3 * p.sec_h) axis = 1;
     else if (i % 3 == 2 && i < 3 * p.sec_w) axis = 2;
@@ -200,7 +201,15 @@ __global__ __launch_bounds__(256) void qk_norm_mrope_kernel(const RopeParams p, 
     const double phi = pos * inv_freq[i];
     const double two_pi = 6.283185307179586476925286766559;
     const double red = fma(-two_pi, rint(phi * (1.0 / two_pi)), phi);
-    sincosf(static_cast<float>(red), &sn[e], &cs[e]);
+    sincosf(static_cast<float>(red), &s_sn[i], &s_cs[i]);
+  }
+  __syncthreads();
+  float cs[4], sn[4], qa[4], qb[4], ka[4], kb[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int i = i0 + e;
+    cs[e] = s_cs[i];
+    sn[e] = s_sn[i];
     qa[e] = load_elem(p.q_norm, i, p.norm_dt);
     qb[e] = load_elem(p.q_norm, i + HALF, p.norm_dt);
     ka[e] = load_elem(p.k_norm, i, p.norm_dt);
