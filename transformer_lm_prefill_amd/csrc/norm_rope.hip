@@ -133,17 +133,20 @@ hipError_t launch_deepstack_add(float* y, const int32_t* rows, const void* ds, i
 }
 
 // ------------------------------------------------------------------------------------------
-// q/k RMSNorm + interleaved MRoPE. One 256-thread workgroup per token. A lane owns four
+// q/k RMSNorm + interleaved MRoPE. One 256-thread workgroup per four tokens. A lane owns four
 // consecutive rotation pairs (x_i, x_{i+hd/2}), i = i0 .. i0+3, of one head row, read and written
 // with 8-byte (16-bit types) or 16-byte (fp32) accesses, so the rotation is lane-local and the
 // hd/8 lanes of a row reduce the sum of squares with cross-lane shuffles. The angle of pair i
-// depends on the token only (not the head): the workgroup forms the token's hd/2 cos/sin pairs
-// once, in LDS, and every lane applies its four to each q and k head row it owns; the norm
-// weights are read once per lane.
+// depends on the token only (not the head): the workgroup forms each of its tokens' hd/2
+// cos/sin pairs once, in LDS, and every lane applies its four to each q and k head row it owns;
+// the norm weights are read once per lane.
 //
 // Angle precision: theta^(-2i/hd) is formed in double on the host, phi = pos * theta^(-2i/hd)
 // in double and reduced to [-pi, pi] in double before the single-precision sincos, so its
 // error does not grow with the position.
+// tokens per workgroup: the norm weights and the workgroup set-up are shared by this many
+// tokens (four: 32 -> 24 us for the 8B q/k at 4096 tokens, against one token per workgroup)
+constexpr int kRopeTokens = 4;
 struct RopeFreqs {
   double inv[64];
 };
@@ -178,46 +181,56 @@ __device__ __forceinline__ void store4(void* row, int i, const float (&v)[4]) {
   }
 }
 
-template <int DT, int HD>
+template <int DT, int HD, int TPW>
 __global__ __launch_bounds__(256) void qk_norm_mrope_kernel(const RopeParams p, const RopeFreqs f) {
   const double* inv_freq = f.inv;
   constexpr int HALF = HD / 2;
   constexpr int LPR = HALF / 4;                     // lanes per head row
   constexpr int ROWS_PER_WAVE = 64 / LPR;           // 4 (hd 128) or 8 (hd 64)
   constexpr int ROWS_PER_PASS = 4 * ROWS_PER_WAVE;  // 4 waves
-  const int s = blockIdx.x;
+  static_assert(TPW * HALF <= 256, "one angle per thread");
+  const int s0 = blockIdx.x * TPW;
   const int lane = threadIdx.x & 63;
   const int i0 = 4 * (lane % LPR);
   const int sub = (threadIdx.x >> 6) * ROWS_PER_WAVE + lane / LPR;
 
-  // the token's hd/2 angles, each formed once (by the first hd/2 threads) and shared via LDS
-  __shared__ float s_cs[HALF], s_sn[HALF];
-  if (threadIdx.x < HALF) {
-    const int i = threadIdx.x;
-    int axis = 0;
-    if (i % 3 == 1 && i < 3 * p.sec_h) axis = 1;
-    else if (i % 3 == 2 && i < 3 * p.sec_w) axis = 2;
-    const double pos = static_cast<double>(p.pos[static_cast<int64_t>(axis) * p.S + s]);
-    const double phi = pos * inv_freq[i];
-    const double two_pi = 6.283185307179586476925286766559;
-    const double red = fma(-two_pi, rint(phi * (1.0 / two_pi)), phi);
-    sincosf(static_cast<float>(red), &s_sn[i], &s_cs[i]);
+  // the hd/2 angles of each of the workgroup's TPW tokens, each formed once (thread
+  // t*hd/2 + i forms angle i of token s0 + t) and shared through LDS
+  __shared__ __attribute__((aligned(16))) float s_cs[TPW][HALF];
+  __shared__ __attribute__((aligned(16))) float s_sn[TPW][HALF];
+  if (threadIdx.x < TPW * HALF) {
+    const int tt = threadIdx.x / HALF;
+    const int i = threadIdx.x % HALF;
+    const int s = s0 + tt;
+    if (s < p.S) {
+      int axis = 0;
+      if (i % 3 == 1 && i < 3 * p.sec_h) axis = 1;
+      else if (i % 3 == 2 && i < 3 * p.sec_w) axis = 2;
+      const double pos = static_cast<double>(p.pos[static_cast<int64_t>(axis) * p.S + s]);
+      const double phi = pos * inv_freq[i];
+      const double two_pi = 6.283185307179586476925286766559;
+      const double red = fma(-two_pi, rint(phi * (1.0 / two_pi)), phi);
+      sincosf(static_cast<float>(red), &s_sn[tt][i], &s_cs[tt][i]);
+    }
   }
   __syncthreads();
-  float cs[4], sn[4], qa[4], qb[4], ka[4], kb[4];
+  float qa[4], qb[4], ka[4], kb[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int i = i0 + e;
-    cs[e] = s_cs[i];
-    sn[e] = s_sn[i];
     qa[e] = load_elem(p.q_norm, i, p.norm_dt);
     qb[e] = load_elem(p.q_norm, i + HALF, p.norm_dt);
     ka[e] = load_elem(p.k_norm, i, p.norm_dt);
     kb[e] = load_elem(p.k_norm, i + HALF, p.norm_dt);
   }
 
+  // head rows of the TPW tokens in token order: row index hh = token * (nh + nkv) + head
   const int nrows = p.nh + p.nkv;
-  for (int h = sub; h < nrows; h += ROWS_PER_PASS) {
+  for (int hh = sub; hh < TPW * nrows; hh += ROWS_PER_PASS) {
+    const int tt = TPW == 1 ? 0 : hh / nrows;
+    const int h = TPW == 1 ? hh : hh - tt * nrows;
+    const int s = s0 + tt;
+    if (s >= p.S) break;
     const bool is_q = h < p.nh;
     void* row = is_q ? static_cast<void*>(static_cast<char*>(p.q) +
                                           (static_cast<int64_t>(s) * p.q_stride + static_cast<int64_t>(h) * HD) *
@@ -229,6 +242,8 @@ __global__ __launch_bounds__(256) void qk_norm_mrope_kernel(const RopeParams p, 
     float a[4], b[4];
     load4<DT>(row, i0, a);
     load4<DT>(row, i0 + HALF, b);
+    const f32x4 cs = *reinterpret_cast<const f32x4*>(&s_cs[tt][i0]);
+    const f32x4 sn = *reinterpret_cast<const f32x4*>(&s_sn[tt][i0]);
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) ss = fmaf(a[e], a[e], fmaf(b[e], b[e], ss));
@@ -249,14 +264,15 @@ __global__ __launch_bounds__(256) void qk_norm_mrope_kernel(const RopeParams p, 
 
 template <int HD>
 static hipError_t rope_launch(const RopeParams& p, int dt, hipStream_t s) {
-  dim3 grid(p.S), block(256);
+  constexpr int TPW = kRopeTokens;
+  dim3 grid((p.S + TPW - 1) / TPW), block(256);
   // theta^(-2i/hd) for i < hd/2, in double on the host, passed with the launch
   RopeFreqs f;
   for (int i = 0; i < HD / 2; ++i) f.inv[i] = std::exp2(-(2.0 * i / HD) * p.log2_theta);
   switch (dt) {
-    case DT_F32: qk_norm_mrope_kernel<DT_F32, HD><<<grid, block, 0, s>>>(p, f); break;
-    case DT_BF16: qk_norm_mrope_kernel<DT_BF16, HD><<<grid, block, 0, s>>>(p, f); break;
-    case DT_F16: qk_norm_mrope_kernel<DT_F16, HD><<<grid, block, 0, s>>>(p, f); break;
+    case DT_F32: qk_norm_mrope_kernel<DT_F32, HD, TPW><<<grid, block, 0, s>>>(p, f); break;
+    case DT_BF16: qk_norm_mrope_kernel<DT_BF16, HD, TPW><<<grid, block, 0, s>>>(p, f); break;
+    case DT_F16: qk_norm_mrope_kernel<DT_F16, HD, TPW><<<grid, block, 0, s>>>(p, f); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
