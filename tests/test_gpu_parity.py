@@ -30,7 +30,10 @@ def _normal(seed, shape, std=1.0, mean=0.0, dtype="bf16"):
 
 @pytest.mark.parametrize("wdt,ydt,rows,hidden", [("bf16", "bf16", 37, 2048), ("bf16", "f16", 5, 5120),
                                                  ("f32", "f32", 33, 256), ("f32", "f32", 3, 4096),
-                                                 ("bf16", "f32", 7, 16384)])
+                                                 ("bf16", "f32", 7, 16384),
+                                                 # more rows than the RMSNorm grid: each
+                                                 # workgroup walks two or three rows
+                                                 ("bf16", "f16", 3001, 1024)])
 def test_rms_norm_rows(wdt, ydt, rows, hidden):
     from transformer_lm_prefill_amd.ops import TORCH_DTYPES
     x = _normal(1, (rows, hidden), dtype="f32") * 3

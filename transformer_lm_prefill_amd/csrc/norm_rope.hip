@@ -14,9 +14,10 @@
 namespace q3 {
 
 // ------------------------------------------------------------------------------------------
-// RMSNorm: one 256-thread workgroup per row; the row stays in registers between the
+// RMSNorm: 256-thread workgroups, one row at a time; a row stays in registers between the
 // sum-of-squares pass and the scaling pass, so x is read from HBM once.
 constexpr int kNormThreads = 256;
+constexpr int kNormGrid = 1024;  // workgroups of the streaming RMSNorm (4 per CU)
 constexpr int kNormMaxVec = 16;  // float4 per thread: hidden <= 16384
 
 // Load 4 consecutive elements (index 4c .. 4c+3) of a vector stored as dtype DT, as floats.
@@ -41,51 +42,84 @@ __device__ __forceinline__ void store4(void* p, int64_t c, f32x4 v) {
   }
 }
 
-template <int W_DT, int Y_DT>
-__global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(const float* __restrict__ x,
-                                                               const void* __restrict__ w,
-                                                               void* __restrict__ y, int hidden,
-                                                               float eps) {
-  const int row = blockIdx.x;
+// Streaming form: a fixed grid of workgroups walks the rows (row r, r + grid, ...), loading the
+// next row into registers while the current one is reduced and written, so reads and writes
+// overlap instead of alternating in bursts. NV float4 per thread per row.
+template <int W_DT, int Y_DT, int NV>
+__global__ __launch_bounds__(kNormThreads) void rmsnorm_stream_kernel(const float* __restrict__ x,
+                                                                      const void* __restrict__ w,
+                                                                      void* __restrict__ y, int rows,
+                                                                      int hidden, float eps) {
   const int nv = hidden >> 2;
-  const f32x4* xr = reinterpret_cast<const f32x4*>(x + static_cast<int64_t>(row) * hidden);
-  f32x4 v[kNormMaxVec];
-  float ss = 0.f;
+  f32x4 g[NV], cur[NV], nxt[NV];
 #pragma unroll
-  for (int i = 0; i < kNormMaxVec; ++i) {
+  for (int i = 0; i < NV; ++i) {
     const int c = threadIdx.x + i * kNormThreads;
-    if (c < nv) {
-      v[i] = __builtin_nontemporal_load(xr + c);
-      ss += v[i][0] * v[i][0] + v[i][1] * v[i][1] + v[i][2] * v[i][2] + v[i][3] * v[i][3];
-    }
+    if (c < nv) g[i] = load4<W_DT>(w, c);
   }
-  __shared__ float red[kNormThreads / 64];
-  ss = wave_sum(ss);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
-  __syncthreads();
-  float tot = 0.f;
+  auto load_row = [&](f32x4 (&v)[NV], int row) {
+    const f32x4* xr = reinterpret_cast<const f32x4*>(x + static_cast<int64_t>(row) * hidden);
 #pragma unroll
-  for (int i = 0; i < kNormThreads / 64; ++i) tot += red[i];
-  const float r = 1.0f / sqrtf(tot / static_cast<float>(hidden) + eps);
-#pragma unroll
-  for (int i = 0; i < kNormMaxVec; ++i) {
-    const int c = threadIdx.x + i * kNormThreads;
-    if (c < nv) {
-      const f32x4 g = load4<W_DT>(w, c);
-      const f32x4 o = {v[i][0] * r * g[0], v[i][1] * r * g[1], v[i][2] * r * g[2], v[i][3] * r * g[3]};
-      store4<Y_DT>(y, static_cast<int64_t>(row) * nv + c, o);
+    for (int i = 0; i < NV; ++i) {
+      const int c = threadIdx.x + i * kNormThreads;
+      if (c < nv) v[i] = xr[c];
     }
+  };
+  __shared__ float red[2][kNormThreads / 64];
+  int row = blockIdx.x;
+  if (row < rows) load_row(cur, row);
+  for (int it = 0; row < rows; row += gridDim.x, ++it) {
+    const int rn = row + gridDim.x;
+    if (rn < rows) load_row(nxt, rn);
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int c = threadIdx.x + i * kNormThreads;
+      if (c < nv) ss += cur[i][0] * cur[i][0] + cur[i][1] * cur[i][1] + cur[i][2] * cur[i][2] + cur[i][3] * cur[i][3];
+    }
+    ss = wave_sum(ss);
+    // two reduction slots by row parity: a slot is rewritten two rows later, after every thread
+    // has passed the barrier of the row in between
+    if ((threadIdx.x & 63) == 0) red[it & 1][threadIdx.x >> 6] = ss;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int i = 0; i < kNormThreads / 64; ++i) tot += red[it & 1][i];
+    const float r = 1.0f / sqrtf(tot / static_cast<float>(hidden) + eps);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int c = threadIdx.x + i * kNormThreads;
+      if (c < nv) {
+        const f32x4 o = {cur[i][0] * r * g[i][0], cur[i][1] * r * g[i][1], cur[i][2] * r * g[i][2],
+                         cur[i][3] * r * g[i][3]};
+        store4<Y_DT>(y, static_cast<int64_t>(row) * nv + c, o);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) cur[i] = nxt[i];
+  }
+}
+
+template <int W_DT, int Y_DT>
+static void rms_launch_k(const float* x, const void* w, void* y, int rows, int hidden, float eps,
+                         hipStream_t s) {
+  const int grid = rows < kNormGrid ? rows : kNormGrid;
+  if (hidden <= 4 * kNormThreads * 4) {
+    rmsnorm_stream_kernel<W_DT, Y_DT, 4><<<grid, kNormThreads, 0, s>>>(x, w, y, rows, hidden, eps);
+  } else if (hidden <= 4 * kNormThreads * 8) {
+    rmsnorm_stream_kernel<W_DT, Y_DT, 8><<<grid, kNormThreads, 0, s>>>(x, w, y, rows, hidden, eps);
+  } else {
+    rmsnorm_stream_kernel<W_DT, Y_DT, 16><<<grid, kNormThreads, 0, s>>>(x, w, y, rows, hidden, eps);
   }
 }
 
 template <int W_DT>
 static hipError_t rms_launch_y(const float* x, const void* w, void* y, int y_dt, int rows, int hidden,
                                float eps, hipStream_t s) {
-  dim3 grid(rows), block(kNormThreads);
   switch (y_dt) {
-    case DT_F32: rmsnorm_kernel<W_DT, DT_F32><<<grid, block, 0, s>>>(x, w, y, hidden, eps); break;
-    case DT_BF16: rmsnorm_kernel<W_DT, DT_BF16><<<grid, block, 0, s>>>(x, w, y, hidden, eps); break;
-    case DT_F16: rmsnorm_kernel<W_DT, DT_F16><<<grid, block, 0, s>>>(x, w, y, hidden, eps); break;
+    case DT_F32: rms_launch_k<W_DT, DT_F32>(x, w, y, rows, hidden, eps, s); break;
+    case DT_BF16: rms_launch_k<W_DT, DT_BF16>(x, w, y, rows, hidden, eps, s); break;
+    case DT_F16: rms_launch_k<W_DT, DT_F16>(x, w, y, rows, hidden, eps, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
