@@ -424,21 +424,23 @@ static int layer_prefill_impl(const qwen3_layer_cfg* cfg, const LayerW& w, const
     if ((st = run_gemm("gemm_qkv", p, dt == QWEN3_F32 ? q3::EPI_STORE_F32 : q3::EPI_STORE_16, bdt, dt, s)))
       return st;
   }
-  // a3+a4: per-head RMSNorm and interleaved MRoPE on q and k, in place
+  // a3+a4: per-head RMSNorm and interleaved MRoPE on q and k, in place; with caches, the same
+  // launch appends k' and v of every position (rows 0..S-1)
   {
     q3::RopeParams p{qkv, qkv + static_cast<size_t>(q_dim) * e, qkv_dim, qkv_dim, S, nh, nkv,
                      w.q_norm, w.k_norm, wdt, positions, cfg->rms_eps,
                      std::log2(static_cast<double>(cfg->rope_theta)), cfg->mrope_section[1],
                      cfg->mrope_section[2]};
+    if (k_cache) {
+      p.kc = k_cache;
+      p.vc = v_cache;
+      p.v = qkv + static_cast<size_t>(q_dim + kv_dim) * e;
+      p.v_stride = qkv_dim;
+      p.capacity = capacity;
+      p.row0 = 0;
+      p.cache_dt = dt;
+    }
     if ((st = run_qk_norm_mrope(p, hd, dt, s))) return st;
-  }
-  // k' and v of every position into the caches
-  if (k_cache) {
-    KTimer t("kv_cache_write", s);
-    q3::KvWriteParams kp{qkv + static_cast<size_t>(q_dim) * e, qkv + static_cast<size_t>(q_dim + kv_dim) * e,
-                         qkv_dim, qkv_dim, S, nkv, hd, k_cache, v_cache, capacity, 0};
-    const hipError_t he = q3::launch_kv_cache_write(kp, dt, dt, s);
-    if (he != hipSuccess) return hip_fail(he, "kv_cache_write launch");
   }
   // a5: causal GQA attention -> o [S, q_dim]
   if ((st = run_attention(qkv, qkv + static_cast<size_t>(q_dim) * e, qkv + static_cast<size_t>(q_dim + kv_dim) * e,
@@ -1106,28 +1108,36 @@ static int layer_decode_impl(const qwen3_layer_cfg* cfg, const LayerW& w, const 
   float* o = reinterpret_cast<float*>(ws + L.o);
   float* act = reinterpret_cast<float*>(ws + L.act);
 
-  // input RMSNorm of the new row (fp32)
-  if ((st = run_rmsnorm(x_in, w.attn_norm, wdt, xn, QWEN3_F32, 1, H, cfg->rms_eps, s))) return st;
+  // input RMSNorm of the new row: folded into the q | k | v product for dense weights (the
+  // product runs on x * attn_norm and is scaled by 1/rms), a separate fp32 row otherwise
+  const bool fold_norm = !quant;
+  if (!fold_norm && (st = run_rmsnorm(x_in, w.attn_norm, wdt, xn, QWEN3_F32, 1, H, cfg->rms_eps, s))) return st;
   // q | k | v of the new token
   {
     const MatW* g[3] = {&w.wq, &w.wk, &w.wv};
-    q3::GemvParams p{nullptr, nullptr, nullptr, q_dim, q_dim + kv_dim, xn, qkv, nullptr, qkv_dim, H};
+    q3::GemvParams p{nullptr, nullptr, nullptr, q_dim, q_dim + kv_dim, fold_norm ? x_in : xn, qkv, nullptr,
+                     qkv_dim, H};
+    if (fold_norm) {
+      p.norm_w = w.attn_norm;
+      p.norm_dt = wdt;
+      p.eps = cfg->rms_eps;
+    }
     if ((st = run_gemv("gemv_qkv", g, 3, p, q3::GV_STORE, wdt, s))) return st;
   }
-  // per-head RMSNorm + interleaved MRoPE at the token's position
+  // per-head RMSNorm + interleaved MRoPE at the token's position; the same launch appends k'
+  // and v at row len of the caches
   {
     q3::RopeParams p{qkv, qkv + q_dim, qkv_dim, qkv_dim, 1, nh, nkv, w.q_norm, w.k_norm, wdt, position,
                      cfg->rms_eps, std::log2(static_cast<double>(cfg->rope_theta)), cfg->mrope_section[1],
                      cfg->mrope_section[2]};
+    p.kc = k_cache;
+    p.vc = v_cache;
+    p.v = qkv + q_dim + kv_dim;
+    p.v_stride = qkv_dim;
+    p.capacity = capacity;
+    p.row0 = len;
+    p.cache_dt = cdt;
     if ((st = run_qk_norm_mrope(p, hd, QWEN3_F32, s))) return st;
-  }
-  // append k' and v at row len
-  {
-    KTimer t("kv_cache_write", s);
-    q3::KvWriteParams kp{qkv + q_dim, qkv + q_dim + kv_dim, qkv_dim, qkv_dim, 1, nkv, hd, k_cache, v_cache,
-                         capacity, len};
-    const hipError_t he = q3::launch_kv_cache_write(kp, QWEN3_F32, cdt, s);
-    if (he != hipSuccess) return hip_fail(he, "kv_cache_write launch");
   }
   // the new query over the len + 1 cached keys
   if ((st = run_decode_attention(qkv, k_cache, v_cache, capacity, len + 1, nh, nkv, hd,
@@ -1139,10 +1149,15 @@ static int layer_decode_impl(const qwen3_layer_cfg* cfg, const LayerW& w, const 
     q3::GemvParams p{nullptr, nullptr, nullptr, H, H, o, x_out, x_in, H, q_dim};
     if ((st = run_gemv("gemv_o_resid", g, 1, p, q3::GV_RESID, wdt, s))) return st;
   }
-  if ((st = run_rmsnorm(x_out, w.ffn_norm, wdt, xn, QWEN3_F32, 1, H, cfg->rms_eps, s))) return st;
+  if (!fold_norm && (st = run_rmsnorm(x_out, w.ffn_norm, wdt, xn, QWEN3_F32, 1, H, cfg->rms_eps, s))) return st;
   {
     const MatW* g[2] = {&w.wg, &w.wu};
-    q3::GemvParams p{nullptr, nullptr, nullptr, F, F, xn, act, nullptr, F, H};
+    q3::GemvParams p{nullptr, nullptr, nullptr, F, F, fold_norm ? x_out : xn, act, nullptr, F, H};
+    if (fold_norm) {
+      p.norm_w = w.ffn_norm;
+      p.norm_dt = wdt;
+      p.eps = cfg->rms_eps;
+    }
     if ((st = run_gemv("gemv_gate_up_swiglu", g, 2, p, q3::GV_SWIGLU, wdt, s))) return st;
   }
   {

@@ -371,6 +371,10 @@ __global__ __launch_bounds__(256) void gemv_epi_kernel(GemvParams p) {
   float acc[NR];
 #pragma unroll
   for (int j = 0; j < NR; ++j) acc[j] = 0.f;
+  // folded RMSNorm: the product runs on x * norm_w; sum of x^2 alongside, the row scale
+  // 1/sqrt(mean + eps) applied to the finished dot products
+  const bool nrm = p.norm_w != nullptr;
+  float ss = 0.f;
   constexpr int STEP = 4 * 64 * 8;   // elements per pass of the four waves
   for (int i0 = (wave * 64 + lane) * 8; i0 < p.K; i0 += STEP * U) {
     Raw8<DT> w[U][NR];
@@ -385,6 +389,17 @@ __global__ __launch_bounds__(256) void gemv_epi_kernel(GemvParams p) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) xv[u][e] = 0.f;
       }
+      if (nrm) {
+        float gv[8];
+        if (p.norm_dt == DT_BF16) load8<DT_BF16>(p.norm_w, i, gv);
+        else if (p.norm_dt == DT_F16) load8<DT_F16>(p.norm_w, i, gv);
+        else load8<DT_F32>(p.norm_w, i, gv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          ss = fmaf(xv[u][e], xv[u][e], ss);
+          xv[u][e] *= gv[e];
+        }
+      }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -393,15 +408,24 @@ __global__ __launch_bounds__(256) void gemv_epi_kernel(GemvParams p) {
   }
 #pragma unroll
   for (int j = 0; j < NR; ++j) acc[j] = wave_sum(acc[j]);
+  __shared__ float red_ss[4];
+  if (nrm) ss = wave_sum(ss);
   if (lane == 0) {
 #pragma unroll
     for (int j = 0; j < NR; ++j) red[wave][j] = acc[j];
+    red_ss[wave] = ss;
   }
   __syncthreads();
   if (wave == 0 && lane < kGvRows && r0 + lane < p.rows) {
     float tot[NR];
 #pragma unroll
     for (int j = 0; j < NR; ++j) tot[j] = (red[0][j] + red[1][j]) + (red[2][j] + red[3][j]);
+    if (nrm) {
+      const float sum_sq = (red_ss[0] + red_ss[1]) + (red_ss[2] + red_ss[3]);
+      const float r = 1.0f / sqrtf(sum_sq / static_cast<float>(p.K) + p.eps);
+#pragma unroll
+      for (int j = 0; j < NR; ++j) tot[j] *= r;
+    }
     float v = tot[0];
 #pragma unroll
     for (int j = 1; j < kGvRows; ++j) v = lane == j ? tot[j] : v;

@@ -80,6 +80,11 @@ struct GemvParams {
   float* y;
   const float* R;                 // GV_RESID: y[r] = R[r] + product (R may alias y)
   int rows, K;
+  // Optional RMSNorm of x folded in (dense weights only): with norm_w set the product uses
+  // x * norm_w / sqrt(mean(x^2) + eps) in place of x (norm_w [K] of norm_dt).
+  const void* norm_w = nullptr;
+  int norm_dt = 0;
+  float eps = 0.f;
 };
 hipError_t launch_gemv(const GemvParams& p, int epi, int wdt, hipStream_t s);
 
@@ -110,6 +115,16 @@ struct RopeParams {
   float eps;
   double log2_theta;
   int sec_h, sec_w;    // interleave bounds: h pairs i%3==1 && i<3*sec_h, w pairs i%3==2 && i<3*sec_w
+  // Optional KV-cache append: with kc set, token t's rotated k rows and its v rows (v + t*v_stride
+  // + h*hd) are also written, in cache_dt, to row row0 + t of the head-major caches kc / vc
+  // ([nkv][capacity][hd]).
+  void* kc = nullptr;
+  void* vc = nullptr;
+  const void* v = nullptr;
+  int64_t v_stride = 0;
+  int64_t capacity = 0;
+  int row0 = 0;
+  int cache_dt = 0;
 };
 hipError_t launch_qk_norm_mrope(const RopeParams& p, int head_dim, int data_dt, hipStream_t s);
 

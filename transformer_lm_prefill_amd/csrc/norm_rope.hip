@@ -215,6 +215,13 @@ __device__ __forceinline__ void store4(void* row, int i, const float (&v)[4]) {
   }
 }
 
+// 4 floats to row element i of a vector of runtime type dt (cache rows)
+__device__ __forceinline__ void store4_dt(void* row, int i, const float (&v)[4], int dt) {
+  if (dt == DT_F32) store4<DT_F32>(row, i, v);
+  else if (dt == DT_BF16) store4<DT_BF16>(row, i, v);
+  else store4<DT_F16>(row, i, v);
+}
+
 template <int DT, int HD, int TPW>
 __global__ __launch_bounds__(256) void qk_norm_mrope_kernel(const RopeParams p, const RopeFreqs f) {
   const double* inv_freq = f.inv;
@@ -293,6 +300,31 @@ __global__ __launch_bounds__(256) void qk_norm_mrope_kernel(const RopeParams p, 
     }
     store4<DT>(row, i0, ra);
     store4<DT>(row, i0 + HALF, rb);
+    if (p.kc && !is_q) {
+      const int es = p.cache_dt == DT_F32 ? 4 : 2;
+      void* crow = static_cast<char*>(p.kc) +
+                   ((static_cast<int64_t>(h - p.nh) * p.capacity + p.row0 + s) * HD) * es;
+      store4_dt(crow, i0, ra, p.cache_dt);
+      store4_dt(crow, i0 + HALF, rb, p.cache_dt);
+    }
+  }
+  // cache append of the tokens' v rows (same lane layout, no arithmetic)
+  if (p.kc) {
+    for (int hh = sub; hh < TPW * p.nkv; hh += ROWS_PER_PASS) {
+      const int tt = TPW == 1 ? 0 : hh / p.nkv;
+      const int g = hh - tt * p.nkv;
+      const int s = s0 + tt;
+      if (s >= p.S) break;
+      const void* vrow = static_cast<const char*>(p.v) +
+                         (static_cast<int64_t>(s) * p.v_stride + static_cast<int64_t>(g) * HD) * (DT == DT_F32 ? 4 : 2);
+      float a[4], b[4];
+      load4<DT>(vrow, i0, a);
+      load4<DT>(vrow, i0 + HALF, b);
+      const int es = p.cache_dt == DT_F32 ? 4 : 2;
+      void* crow = static_cast<char*>(p.vc) + ((static_cast<int64_t>(g) * p.capacity + p.row0 + s) * HD) * es;
+      store4_dt(crow, i0, a, p.cache_dt);
+      store4_dt(crow, i0 + HALF, b, p.cache_dt);
+    }
   }
 }
 

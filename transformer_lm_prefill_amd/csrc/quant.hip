@@ -329,6 +329,7 @@ __global__ __launch_bounds__(256) void gemv_q8_row_kernel(GemvParams p, const fl
 
 hipError_t launch_gemv_quant(const GemvParams& p, int epi, int fmt, const float* rs0, const float* rs1,
                              const float* rs2, hipStream_t s) {
+  if (p.norm_w != nullptr) return hipErrorInvalidValue;  // the folded RMSNorm is dense-only
   if (p.rows <= 0) return hipSuccess;
   const unsigned blocks = static_cast<unsigned>((p.rows + 4 * kQvRows - 1) / (4 * kQvRows));
   if (fmt == WF_Q4_0) {
