@@ -80,7 +80,7 @@ __device__ __forceinline__ void tile_coords(int bid, int nwg, int tiles_m, int t
                                             int& tn) {
   int L = bid;
   if ((nwg & 7) == 0) L = (bid & 7) * (nwg >> 3) + (bid >> 3);
-  constexpr int GM = 8;
+  constexpr int GM = 4;  // 4 measured best on the 8B shapes (o-proj 3-5% faster than 8 or 16)
   const int per_group = GM * tiles_n;
   const int group = L / per_group;
   const int first_m = group * GM;
