@@ -36,13 +36,16 @@ def test_vision_rope_tables_match_oracle(layout, grid, merge, hd):
     assert np.max(np.abs(host(cos) - rc)) <= 1e-6 and np.max(np.abs(host(sin) - rs)) <= 1e-6
 
 
-@pytest.mark.parametrize("pairing,fmt", [("split", "f32"), ("split", "bf16"), ("adjacent", "f16"),
-                                         ("adjacent", "f32"), ("split", "f16")])
-def test_apply_rope_tables_matches_oracle(pairing, fmt):
+@pytest.mark.parametrize("pairing,fmt,pad", [("split", "f32", 0), ("split", "bf16", 0), ("adjacent", "f16", 0),
+                                             ("adjacent", "f32", 0), ("split", "f16", 0),
+                                             # a row stride off the 8-element grid: the scalar form
+                                             ("split", "f16", 4), ("adjacent", "bf16", 4)])
+def test_apply_rope_tables_matches_oracle(pairing, fmt, pad):
     n, heads, hd = 200, 6, 64
     r = _rng(100)
-    # q lives in the first third of a [n, 3 * heads * hd] row (a strided view, as in a qkv buffer)
-    rows = _round(r.standard_normal((n, 3 * heads * hd)), fmt)
+    # q lives in the first third of a [n, 3 * heads * hd (+ pad)] row (a strided view, as in a
+    # qkv buffer)
+    rows = _round(r.standard_normal((n, 3 * heads * hd + pad)), fmt)
     phi = r.uniform(-6, 6, (n, hd))
     cos_t, sin_t = np.cos(phi).astype(np.float32), np.sin(phi).astype(np.float32)
     x = dev(rows, fmt)

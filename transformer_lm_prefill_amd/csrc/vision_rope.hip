@@ -78,7 +78,8 @@ __device__ __forceinline__ void st(void* x, int64_t i, float v) {
   else static_cast<uint16_t*>(x)[i] = DT == DT_BF16 ? f2bf(v) : f2h(v);
 }
 
-// One thread per (patch, head, pair).
+// One thread per (patch, head, pair): the general form, for strides or alignments the vector
+// form does not take.
 template <int DT, int PAIRING>
 __global__ __launch_bounds__(256) void apply_rope_tables_kernel(void* x, int n, int heads, int hd,
                                                                 int64_t row_stride, const float* cosv,
@@ -100,6 +101,60 @@ __global__ __launch_bounds__(256) void apply_rope_tables_kernel(void* x, int n, 
   st<DT>(x, base + b, xb * c[b] + xa * s[b]);
 }
 
+// Vector form: one thread per run of 8 elements of a head row (pairing 0: pairs i .. i+7, runs
+// at i and i + half; pairing 1: 4 adjacent pairs), 16-byte accesses of x (two for fp32) and of
+// the tables. Needs hd % 16 == 0, a row stride that is a multiple of 8 elements and 16-byte
+// aligned x and tables.
+__device__ __forceinline__ void tab8(const float* t, float (&v)[8]) {
+  const f32x4 p = *reinterpret_cast<const f32x4*>(t), q = *reinterpret_cast<const f32x4*>(t + 4);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[e] = p[e];
+    v[4 + e] = q[e];
+  }
+}
+
+template <int DT, int PAIRING>
+__global__ __launch_bounds__(256) void apply_rope_tables8_kernel(void* x, int n, int heads, int hd,
+                                                                 int64_t row_stride, const float* cosv,
+                                                                 const float* sinv) {
+  const int half = hd / 2;
+  const int runs = PAIRING == 0 ? half / 8 : hd / 8;  // threads per head row
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t per_tok = static_cast<int64_t>(heads) * runs;
+  if (idx >= per_tok * n) return;
+  const int64_t tok = idx / per_tok;
+  const int hh = static_cast<int>((idx % per_tok) / runs);
+  const int a = 8 * static_cast<int>(idx % runs);
+  const int64_t base = tok * row_stride + static_cast<int64_t>(hh) * hd;
+  const float* c = cosv + tok * hd;
+  const float* sn = sinv + tok * hd;
+  if (PAIRING == 0) {
+    const int b = a + half;
+    float xa[8], xb[8], ca[8], cb[8], sa[8], sb[8], ya[8], yb[8];
+    load8<DT>(x, base + a, xa);
+    load8<DT>(x, base + b, xb);
+    tab8(c + a, ca); tab8(c + b, cb); tab8(sn + a, sa); tab8(sn + b, sb);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      ya[e] = xa[e] * ca[e] - xb[e] * sa[e];
+      yb[e] = xb[e] * cb[e] + xa[e] * sb[e];
+    }
+    store8<DT>(x, base + a, ya);
+    store8<DT>(x, base + b, yb);
+  } else {
+    float v[8], cc[8], ss[8], y[8];
+    load8<DT>(x, base + a, v);
+    tab8(c + a, cc); tab8(sn + a, ss);
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      y[e] = v[e] * cc[e] - v[e + 1] * ss[e];
+      y[e + 1] = v[e + 1] * cc[e + 1] + v[e] * ss[e + 1];
+    }
+    store8<DT>(x, base + a, y);
+  }
+}
+
 hipError_t launch_vision_rope_tables(int layout, int t, int h, int w, int merge, int hd, double log2_theta,
                                      float* cosv, float* sinv, hipStream_t s) {
   const int64_t work = static_cast<int64_t>(t) * h * w * (hd / 2);
@@ -114,8 +169,18 @@ hipError_t launch_vision_rope_tables(int layout, int t, int h, int w, int merge,
 template <int DT>
 static hipError_t launch_apply_dt(void* x, int n, int heads, int hd, int64_t rs, const float* c, const float* sn,
                                   int pairing, unsigned blocks, hipStream_t s) {
-  if (pairing == 0) apply_rope_tables_kernel<DT, 0><<<blocks, 256, 0, s>>>(x, n, heads, hd, rs, c, sn);
-  else apply_rope_tables_kernel<DT, 1><<<blocks, 256, 0, s>>>(x, n, heads, hd, rs, c, sn);
+  const bool vec = hd % 16 == 0 && rs % 8 == 0 && reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(c) % 16 == 0 && reinterpret_cast<uintptr_t>(sn) % 16 == 0;
+  if (vec) {
+    const int64_t work = static_cast<int64_t>(n) * heads * (pairing == 0 ? hd / 16 : hd / 8);
+    const unsigned b8 = static_cast<unsigned>((work + 255) / 256);
+    if (pairing == 0) apply_rope_tables8_kernel<DT, 0><<<b8, 256, 0, s>>>(x, n, heads, hd, rs, c, sn);
+    else apply_rope_tables8_kernel<DT, 1><<<b8, 256, 0, s>>>(x, n, heads, hd, rs, c, sn);
+  } else if (pairing == 0) {
+    apply_rope_tables_kernel<DT, 0><<<blocks, 256, 0, s>>>(x, n, heads, hd, rs, c, sn);
+  } else {
+    apply_rope_tables_kernel<DT, 1><<<blocks, 256, 0, s>>>(x, n, heads, hd, rs, c, sn);
+  }
   return hipGetLastError();
 }
 
