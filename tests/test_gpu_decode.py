@@ -128,14 +128,16 @@ def test_prefill_kv_writes_the_oracle_cache(name, s0):
     assert ek <= CACHE_TOL[act] and ev <= CACHE_TOL[act], (ek, ev)
 
 
-@pytest.mark.parametrize("name,s0,steps", [("tiny_f32", 20, 6), ("qwen3vl_2b_text", 300, 3),
-                                           ("qwen3vl_2b_image", 1500, 3), ("qwen3vl_2b_text", 0, 2)])
-def test_decode_steps_continue_the_prefill(name, s0, steps):
+@pytest.mark.parametrize("name,s0,steps,act", [("tiny_f32", 20, 6, ""), ("qwen3vl_2b_text", 300, 3, ""),
+                                               ("qwen3vl_2b_image", 1500, 3, ""), ("qwen3vl_2b_text", 0, 2, ""),
+                                               # bf16 operands and cache
+                                               ("qwen3vl_2b_text", 200, 2, "bf16")])
+def test_decode_steps_continue_the_prefill(name, s0, steps, act):
     """Prefill s0 tokens with the cache, then decode tokens s0 .. s0+steps-1 one at a time: every
     decode output equals the oracle's prefill row of that position (image positions included)."""
     cfg, w, x, pos = _layer_case(name)
     full = s0 + steps
-    spec = q3.LayerSpec.of(cfg)
+    spec = q3.LayerSpec.of(cfg, act)
     dw = dev_weights(w, cfg.dtype)
     kc, vc = q3.kv_cache_alloc(spec, full + 3)
     if s0 > 0:
@@ -148,7 +150,7 @@ def test_decode_steps_continue_the_prefill(name, s0, steps):
         outs.append(host(y))
     ref = oracle.layer_prefill_rows(x[:full], w, cfg, pos[:, :full], np.arange(s0, full))
     err = rel_err(np.stack(outs), ref)
-    log_err(f"layer_decode[{name},S0={s0},+{steps}]", err)
+    log_err(f"layer_decode[{name},S0={s0},+{steps}{',' + act if act else ''}]", err)
     print(f"{name}: decode after {s0}: max|err|/rms = {err:.3e}")
     assert err <= TOL[cfg.dtype]
     # the rows the decode steps appended are the oracle's k', v of those positions
