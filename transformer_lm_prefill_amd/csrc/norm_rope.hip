@@ -167,10 +167,10 @@ hipError_t launch_deepstack_add(float* y, const int32_t* rows, const void* ds, i
 }
 
 // ------------------------------------------------------------------------------------------
-// q/k RMSNorm + interleaved MRoPE. One 256-thread workgroup per four tokens. A lane owns four
-// consecutive rotation pairs (x_i, x_{i+hd/2}), i = i0 .. i0+3, of one head row, read and written
-// with 8-byte (16-bit types) or 16-byte (fp32) accesses, so the rotation is lane-local and the
-// hd/8 lanes of a row reduce the sum of squares with cross-lane shuffles. The angle of pair i
+// q/k RMSNorm + interleaved MRoPE. One 256-thread workgroup per four tokens. A lane owns eight
+// consecutive rotation pairs (x_i, x_{i+hd/2}), i = i0 .. i0+7, of one head row, read and written
+// with 16-byte accesses (two for fp32), so the rotation is lane-local and the hd/16 lanes of a row
+// reduce the sum of squares with cross-lane shuffles. The angle of pair i
 // depends on the token only (not the head): the workgroup forms each of its tokens' hd/2
 // cos/sin pairs once, in LDS, and every lane applies its four to each q and k head row it owns;
 // the norm weights are read once per lane.
@@ -181,6 +181,8 @@ hipError_t launch_deepstack_add(float* y, const int32_t* rows, const void* ds, i
 // tokens per workgroup: the norm weights and the workgroup set-up are shared by this many
 // tokens (four: 32 -> 24 us for the 8B q/k at 4096 tokens, against one token per workgroup)
 constexpr int kRopeTokens = 4;
+// rotation pairs per lane: 8 (16-byte accesses for 16-bit rows; 6% faster than 4 at the 8B shape)
+constexpr int kRopePairs = 8;
 struct RopeFreqs {
   double inv[64];
 };
@@ -215,24 +217,36 @@ __device__ __forceinline__ void store4(void* row, int i, const float (&v)[4]) {
   }
 }
 
-// 4 floats to row element i of a vector of runtime type dt (cache rows)
-__device__ __forceinline__ void store4_dt(void* row, int i, const float (&v)[4], int dt) {
-  if (dt == DT_F32) store4<DT_F32>(row, i, v);
-  else if (dt == DT_BF16) store4<DT_BF16>(row, i, v);
-  else store4<DT_F16>(row, i, v);
+// PPL consecutive elements (4 or 8) of a row at element i, as floats, and back
+template <int DT, int PPL>
+__device__ __forceinline__ void ld_run(const void* row, int i, float (&v)[PPL]) {
+  if constexpr (PPL == 4) load4<DT>(row, i, v);
+  else load8<DT>(row, i, v);
+}
+template <int DT, int PPL>
+__device__ __forceinline__ void st_run(void* row, int i, const float (&v)[PPL]) {
+  if constexpr (PPL == 4) store4<DT>(row, i, v);
+  else store8<DT>(row, i, v);
+}
+// the same store for a row of runtime type dt (cache rows)
+template <int PPL>
+__device__ __forceinline__ void st_run_dt(void* row, int i, const float (&v)[PPL], int dt) {
+  if (dt == DT_F32) st_run<DT_F32, PPL>(row, i, v);
+  else if (dt == DT_BF16) st_run<DT_BF16, PPL>(row, i, v);
+  else st_run<DT_F16, PPL>(row, i, v);
 }
 
-template <int DT, int HD, int TPW>
+template <int DT, int HD, int TPW, int PPL>
 __global__ __launch_bounds__(256) void qk_norm_mrope_kernel(const RopeParams p, const RopeFreqs f) {
   const double* inv_freq = f.inv;
   constexpr int HALF = HD / 2;
-  constexpr int LPR = HALF / 4;                     // lanes per head row
-  constexpr int ROWS_PER_WAVE = 64 / LPR;           // 4 (hd 128) or 8 (hd 64)
+  constexpr int LPR = HALF / PPL;                   // lanes per head row
+  constexpr int ROWS_PER_WAVE = 64 / LPR;
   constexpr int ROWS_PER_PASS = 4 * ROWS_PER_WAVE;  // 4 waves
   static_assert(TPW * HALF <= 256, "one angle per thread");
   const int s0 = blockIdx.x * TPW;
   const int lane = threadIdx.x & 63;
-  const int i0 = 4 * (lane % LPR);
+  const int i0 = PPL * (lane % LPR);
   const int sub = (threadIdx.x >> 6) * ROWS_PER_WAVE + lane / LPR;
 
   // the hd/2 angles of each of the workgroup's TPW tokens, each formed once (thread
@@ -255,9 +269,9 @@ __global__ __launch_bounds__(256) void qk_norm_mrope_kernel(const RopeParams p, 
     }
   }
   __syncthreads();
-  float qa[4], qb[4], ka[4], kb[4];
+  float qa[PPL], qb[PPL], ka[PPL], kb[PPL];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
+  for (int e = 0; e < PPL; ++e) {
     const int i = i0 + e;
     qa[e] = load_elem(p.q_norm, i, p.norm_dt);
     qb[e] = load_elem(p.q_norm, i + HALF, p.norm_dt);
@@ -280,32 +294,41 @@ __global__ __launch_bounds__(256) void qk_norm_mrope_kernel(const RopeParams p, 
                                           (static_cast<int64_t>(s) * p.k_stride +
                                            static_cast<int64_t>(h - p.nh) * HD) *
                                               (DT == DT_F32 ? 4 : 2));
-    float a[4], b[4];
-    load4<DT>(row, i0, a);
-    load4<DT>(row, i0 + HALF, b);
-    const f32x4 cs = *reinterpret_cast<const f32x4*>(&s_cs[tt][i0]);
-    const f32x4 sn = *reinterpret_cast<const f32x4*>(&s_sn[tt][i0]);
+    float a[PPL], b[PPL];
+    ld_run<DT, PPL>(row, i0, a);
+    ld_run<DT, PPL>(row, i0 + HALF, b);
+    float cs[PPL], sn[PPL];
+#pragma unroll
+    for (int e4 = 0; e4 < PPL; e4 += 4) {
+      const f32x4 c4 = *reinterpret_cast<const f32x4*>(&s_cs[tt][i0 + e4]);
+      const f32x4 n4 = *reinterpret_cast<const f32x4*>(&s_sn[tt][i0 + e4]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        cs[e4 + e] = c4[e];
+        sn[e4 + e] = n4[e];
+      }
+    }
     float ss = 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) ss = fmaf(a[e], a[e], fmaf(b[e], b[e], ss));
+    for (int e = 0; e < PPL; ++e) ss = fmaf(a[e], a[e], fmaf(b[e], b[e], ss));
     ss = group_sum(ss, LPR);
     const float r = 1.0f / sqrtf(ss / static_cast<float>(HD) + p.eps);
-    float ra[4], rb[4];
+    float ra[PPL], rb[PPL];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < PPL; ++e) {
       const float x = a[e] * r * (is_q ? qa[e] : ka[e]);
       const float y = b[e] * r * (is_q ? qb[e] : kb[e]);
       ra[e] = x * cs[e] - y * sn[e];
       rb[e] = x * sn[e] + y * cs[e];
     }
-    store4<DT>(row, i0, ra);
-    store4<DT>(row, i0 + HALF, rb);
+    st_run<DT, PPL>(row, i0, ra);
+    st_run<DT, PPL>(row, i0 + HALF, rb);
     if (p.kc && !is_q) {
       const int es = p.cache_dt == DT_F32 ? 4 : 2;
       void* crow = static_cast<char*>(p.kc) +
                    ((static_cast<int64_t>(h - p.nh) * p.capacity + p.row0 + s) * HD) * es;
-      store4_dt(crow, i0, ra, p.cache_dt);
-      store4_dt(crow, i0 + HALF, rb, p.cache_dt);
+      st_run_dt<PPL>(crow, i0, ra, p.cache_dt);
+      st_run_dt<PPL>(crow, i0 + HALF, rb, p.cache_dt);
     }
   }
   // cache append of the tokens' v rows (same lane layout, no arithmetic)
@@ -317,13 +340,13 @@ __global__ __launch_bounds__(256) void qk_norm_mrope_kernel(const RopeParams p, 
       if (s >= p.S) break;
       const void* vrow = static_cast<const char*>(p.v) +
                          (static_cast<int64_t>(s) * p.v_stride + static_cast<int64_t>(g) * HD) * (DT == DT_F32 ? 4 : 2);
-      float a[4], b[4];
-      load4<DT>(vrow, i0, a);
-      load4<DT>(vrow, i0 + HALF, b);
+      float a[PPL], b[PPL];
+      ld_run<DT, PPL>(vrow, i0, a);
+      ld_run<DT, PPL>(vrow, i0 + HALF, b);
       const int es = p.cache_dt == DT_F32 ? 4 : 2;
       void* crow = static_cast<char*>(p.vc) + ((static_cast<int64_t>(g) * p.capacity + p.row0 + s) * HD) * es;
-      store4_dt(crow, i0, a, p.cache_dt);
-      store4_dt(crow, i0 + HALF, b, p.cache_dt);
+      st_run_dt<PPL>(crow, i0, a, p.cache_dt);
+      st_run_dt<PPL>(crow, i0 + HALF, b, p.cache_dt);
     }
   }
 }
@@ -336,9 +359,9 @@ static hipError_t rope_launch(const RopeParams& p, int dt, hipStream_t s) {
   RopeFreqs f;
   for (int i = 0; i < HD / 2; ++i) f.inv[i] = std::exp2(-(2.0 * i / HD) * p.log2_theta);
   switch (dt) {
-    case DT_F32: qk_norm_mrope_kernel<DT_F32, HD, TPW><<<grid, block, 0, s>>>(p, f); break;
-    case DT_BF16: qk_norm_mrope_kernel<DT_BF16, HD, TPW><<<grid, block, 0, s>>>(p, f); break;
-    case DT_F16: qk_norm_mrope_kernel<DT_F16, HD, TPW><<<grid, block, 0, s>>>(p, f); break;
+    case DT_F32: qk_norm_mrope_kernel<DT_F32, HD, TPW, kRopePairs><<<grid, block, 0, s>>>(p, f); break;
+    case DT_BF16: qk_norm_mrope_kernel<DT_BF16, HD, TPW, kRopePairs><<<grid, block, 0, s>>>(p, f); break;
+    case DT_F16: qk_norm_mrope_kernel<DT_F16, HD, TPW, kRopePairs><<<grid, block, 0, s>>>(p, f); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
