@@ -139,7 +139,7 @@ __device__ __forceinline__ float silu_f(float g) { return g * __builtin_amdgcn_r
 
 // Epilogue shared by the kernels: stores a wave's accumulators. Accumulator element e of
 // block (mi, ni) in lane l holds row 8*(e/4) + 4*(l/32) + e%4 and column l%32 of that block.
-template <int BN, int WM, int WN, int EPI, int OP, bool TRANS = false>
+template <int BN, int WM, int WN, int EPI, int OP, bool TRANS = false, bool RIN = false>
 __device__ __forceinline__ void gemm_epilogue(const GemmParams& p,
                                               f32x16 (&acc)[kBM / WM / 32][BN / WN / 32], int tm,
                                               int tn, int wm, int wn, int lane) {
@@ -181,7 +181,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p,
                   u32x2{F::pack2(a[4 * q], a[4 * q + 1]), F::pack2(a[4 * q + 2], a[4 * q + 3])};
             } else {
               f32x4 v = {a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
-              if (p.R) {
+              if (!RIN && p.R) {
                 const f32x4 r = *reinterpret_cast<const f32x4*>(p.R + static_cast<int64_t>(row) * p.ldr + n);
                 v += r;
               }
@@ -486,6 +486,27 @@ void gemm_d2l_kernel(const GemmParams p) {
     for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.f;
+  // fp32 output with a residual: the accumulators start from R (C^T layout: lane l, elements
+  // 4q..4q+3 of block (mi, ni) = R[row l%32 of block mi][4 columns 8q + 4*(l/32) ..]), loaded
+  // here, behind the ring's first tile loads, so the epilogue only stores; rows past M load a
+  // clamped valid row and are never stored
+  const bool rin = TRANS && p.R != nullptr;
+  if (rin) {
+    const int c4 = 4 * (lane >> 5);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      const int row = min(tm * kBM + wm * (32 * MI) + mi * 32 + (lane & 31), p.M - 1);
+      const float* rr = p.R + static_cast<int64_t>(row) * p.ldr;
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 r = *reinterpret_cast<const f32x4*>(rr + tn * BN + wn * 32 * NI + ni * 32 + 8 * q + c4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[mi][ni][4 * q + e] = r[e];
+        }
+    }
+  }
 
   const int nk = p.K / kBK2;
   auto issue = [&](int st, int kt) {
@@ -612,7 +633,8 @@ void gemm_d2l_kernel(const GemmParams p) {
 
   // the trailing reloads of the last tile must land before this workgroup's LDS is released
   Q3_WAIT_VMCNT(0);
-  gemm_epilogue<BN, WM, WN, EPI, OP, TRANS>(p, acc, tm, tn, wm, wn, lane);
+  if (rin) gemm_epilogue<BN, WM, WN, EPI, OP, TRANS, true>(p, acc, tm, tn, wm, wn, lane);
+  else gemm_epilogue<BN, WM, WN, EPI, OP, TRANS>(p, acc, tm, tn, wm, wn, lane);
 }
 
 // Buffer-descriptor loads address A and each B segment with 32-bit byte offsets, and one load
