@@ -65,6 +65,10 @@
 #ifndef Q3_GEMM_TRANS
 #define Q3_GEMM_TRANS 1
 #endif
+// 1: fp32 outputs of the 256 x 256 tile leave through LDS as whole 256-byte row segments
+#ifndef Q3_GEMM_LDS_EPI
+#define Q3_GEMM_LDS_EPI 1
+#endif
 
 namespace q3 {
 
@@ -633,8 +637,49 @@ void gemm_d2l_kernel(const GemmParams p) {
 
   // the trailing reloads of the last tile must land before this workgroup's LDS is released
   Q3_WAIT_VMCNT(0);
-  if (rin) gemm_epilogue<BN, WM, WN, EPI, OP, TRANS, true>(p, acc, tm, tn, wm, wn, lane);
-  else gemm_epilogue<BN, WM, WN, EPI, OP, TRANS>(p, acc, tm, tn, wm, wn, lane);
+  constexpr bool LDS_EPI = Q3_GEMM_LDS_EPI && TRANS && EPI == EPI_STORE_F32 && WM == 2 && WN == 4 && BN == 256;
+  if constexpr (LDS_EPI) {
+    // fp32 output (residual already in the accumulators) through LDS: each wave owns one 16 KiB
+    // ring array and stages half of its 128 x 64 block at a time (chunk of 4 columns XOR-permuted
+    // by row), then writes whole 256-byte row segments (16 lanes per row)
+    barrier();  // every wave is past its last fragment reads of the ring
+    u32x4* buf = wave == 0 ? sA0 : wave == 1 ? sA1 : wave == 2 ? sA2 : wave == 3 ? sA3
+               : wave == 4 ? sB0 : wave == 5 ? sB1 : wave == 6 ? sB2 : sB3;
+    float* C = static_cast<float*>(p.C);
+#pragma unroll
+    for (int half = 0; half < MI / 2; ++half) {
+#pragma unroll
+      for (int m2 = 0; m2 < 2; ++m2) {
+        const int r = m2 * 32 + fr;
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int ch = ni * 8 + 2 * q + fh;
+            const f32x16& a = acc[half * 2 + m2][ni];
+            buf[r * 16 + (ch ^ (r & 15))] =
+                __builtin_bit_cast(u32x4, f32x4{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]});
+          }
+      }
+      __builtin_amdgcn_s_waitcnt((0x7 << 4) | 0xF | (0x3 << 14));  // lgkmcnt(0): own writes done
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int it = 0; it < 16; ++it) {
+        const int idx = it * 64 + lane;
+        const int r = idx >> 4, c = idx & 15;
+        const u32x4 v = buf[r * 16 + (c ^ (r & 15))];
+        const int grow = tm * kBM + wm * (32 * MI) + half * 64 + r;
+        if (grow < p.M)
+          *reinterpret_cast<u32x4*>(C + static_cast<int64_t>(grow) * p.ldc + tn * BN + wn * 32 * NI + 4 * c) = v;
+      }
+      __builtin_amdgcn_s_waitcnt((0x7 << 4) | 0xF | (0x3 << 14));  // reads done before the next pass
+      __builtin_amdgcn_wave_barrier();
+    }
+  } else if (rin) {
+    gemm_epilogue<BN, WM, WN, EPI, OP, TRANS, true>(p, acc, tm, tn, wm, wn, lane);
+  } else {
+    gemm_epilogue<BN, WM, WN, EPI, OP, TRANS>(p, acc, tm, tn, wm, wn, lane);
+  }
 }
 
 // Buffer-descriptor loads address A and each B segment with 32-bit byte offsets, and one load
