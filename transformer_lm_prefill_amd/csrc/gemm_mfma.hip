@@ -66,6 +66,10 @@
 #define Q3_GEMM_TRANS 1
 #endif
 // 1: fp32 outputs of the 256 x 256 tile leave through LDS as whole 256-byte row segments
+// 1: GEMMs with 16-bit outputs run as persistent workgroups (one per CU, several tiles each)
+#ifndef Q3_GEMM_PERSIST
+#define Q3_GEMM_PERSIST 1
+#endif
 #ifndef Q3_GEMM_LDS_EPI
 #define Q3_GEMM_LDS_EPI 1
 #endif
@@ -432,56 +436,69 @@ void gemm_d2l_kernel(const GemmParams p) {
   const int wn = wave % WN;
   const int tiles_m = (p.M + kBM - 1) / kBM;
   const int tiles_n = p.N / BN;
-  int tm, tn;
-  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  const int ntiles = tiles_m * tiles_n;
+  // Persistent form (16-bit outputs): a grid smaller than the tile count walks tiles
+  // blockIdx.x, + gridDim.x, ... (each the tile a one-tile-per-workgroup launch would give that
+  // workgroup id, on the same XCD when gridDim.x % 8 == 0); the LDS ring runs on across tile
+  // boundaries, so the next tile's first K steps load during this tile's last ones and its
+  // epilogue. The host launches it only when 4 divides the K steps of a tile.
+  const int my_tiles = (ntiles - static_cast<int>(blockIdx.x) + static_cast<int>(gridDim.x) - 1) /
+                       static_cast<int>(gridDim.x);
+  int tm, tn;  // the tile being computed
+  tile_coords(blockIdx.x, ntiles, tiles_m, tiles_n, tm, tn);
 
   // Load slot of this lane in pass j: the wave's 64 consecutive slots starting at
   // (wave + j*waves)*64; slot -> tile row slot/4, stored chunk slot%4, global chunk
-  // (slot%4) ^ swz4(row).
+  // (slot%4) ^ swz4(row). The per-tile part (rows of A, rows of B) is set by set_issue_tile
+  // for the tile whose K steps are being requested.
   const uint16_t* a_src[AJ];
-#pragma unroll
-  for (int j = 0; j < AJ; ++j) {
-    const int slot = (wave + j * WAVES) * 64 + lane;
-    const int row = slot >> 2;
-    const int r = min(tm * kBM + row, p.M - 1);  // rows past M are read, never stored
-    a_src[j] = p.A + static_cast<int64_t>(r) * p.lda + ((slot & 3) ^ swz4(row)) * 8;
-  }
   const uint16_t* b_src[BJ];
-#pragma unroll
-  for (int j = 0; j < BJ; ++j) {
-    int slot = (wave + j * WAVES) * 64 + lane;
-    if (slot >= BSLOT) slot = lane;  // sink load: a valid row
-    const int row = slot >> 2;
-    b_src[j] = b_row<BN, WN, EPI>(p, tn, row) + ((slot & 3) ^ swz4(row)) * 8;
-  }
   // BUF: the same loads through buffer descriptors. A load instruction covers 16 tile rows
   // (one B segment: the host checks segment bounds are multiples of 16), so its descriptor is
-  // uniform; per-lane byte offsets are loop invariant and the K step goes into the scalar
+  // uniform; per-lane byte offsets are fixed for a tile and the K step goes into the scalar
   // offset, which leaves no address arithmetic in the loop.
   __amdgpu_buffer_rsrc_t rsrc_a, rsrc_b[BJ];
   uint32_t voff_a[AJ], voff_b[BJ];
-  if constexpr (BUF) {
+  if constexpr (BUF)
     rsrc_a = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.A), static_cast<short>(0),
                                                static_cast<int>(2 * static_cast<int64_t>(p.M) * p.lda), 0x00020000);
+  auto set_issue_tile = [&](int itm, int itn) {
 #pragma unroll
-    for (int j = 0; j < AJ; ++j)
-      voff_a[j] = static_cast<uint32_t>(2 * (a_src[j] - p.A));
+    for (int j = 0; j < AJ; ++j) {
+      const int slot = (wave + j * WAVES) * 64 + lane;
+      const int row = slot >> 2;
+      const int r = min(itm * kBM + row, p.M - 1);  // rows past M are read, never stored
+      a_src[j] = p.A + static_cast<int64_t>(r) * p.lda + ((slot & 3) ^ swz4(row)) * 8;
+    }
 #pragma unroll
     for (int j = 0; j < BJ; ++j) {
-      const int blk = wave + j * WAVES;
-      const int row0 = blk * 64 < BSLOT ? blk * 16 : 0;  // first tile row of this load (uniform)
-      int slot = blk * 64 + lane;
-      if (slot >= BSLOT) slot = lane;
+      int slot = (wave + j * WAVES) * 64 + lane;
+      if (slot >= BSLOT) slot = lane;  // sink load: a valid row
       const int row = slot >> 2;
-      const uint16_t* base;
-      int idx0, rows;
-      b_seg<BN, WN, EPI>(p, tn, row0, base, idx0, rows);
-      rsrc_b[j] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), static_cast<short>(0),
-                                                    static_cast<int>(2 * static_cast<int64_t>(rows) * p.ldb), 0x00020000);
-      voff_b[j] = static_cast<uint32_t>(2 * ((static_cast<int64_t>(idx0) + (row - row0)) * p.ldb +
-                                             ((slot & 3) ^ swz4(row)) * 8));
+      b_src[j] = b_row<BN, WN, EPI>(p, itn, row) + ((slot & 3) ^ swz4(row)) * 8;
     }
-  }
+    if constexpr (BUF) {
+#pragma unroll
+      for (int j = 0; j < AJ; ++j)
+        voff_a[j] = static_cast<uint32_t>(2 * (a_src[j] - p.A));
+#pragma unroll
+      for (int j = 0; j < BJ; ++j) {
+        const int blk = wave + j * WAVES;
+        const int row0 = blk * 64 < BSLOT ? blk * 16 : 0;  // first tile row of this load (uniform)
+        int slot = blk * 64 + lane;
+        if (slot >= BSLOT) slot = lane;
+        const int row = slot >> 2;
+        const uint16_t* base;
+        int idx0, rows;
+        b_seg<BN, WN, EPI>(p, itn, row0, base, idx0, rows);
+        rsrc_b[j] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), static_cast<short>(0),
+                                                      static_cast<int>(2 * static_cast<int64_t>(rows) * p.ldb), 0x00020000);
+        voff_b[j] = static_cast<uint32_t>(2 * ((static_cast<int64_t>(idx0) + (row - row0)) * p.ldb +
+                                               ((slot & 3) ^ swz4(row)) * 8));
+      }
+    }
+  };
+  set_issue_tile(tm, tn);
 
   f32x16 acc[MI][NI];
 #pragma unroll
@@ -513,8 +530,25 @@ void gemm_d2l_kernel(const GemmParams p) {
   }
 
   const int nk = p.K / kBK2;
-  auto issue = [&](int st, int kt) {
-    const int k0 = min(kt, nk - 1) * kBK2;  // past the end: reload the last tile (never used)
+  const int total = my_tiles * nk;  // K steps of all this workgroup's tiles, in order
+  // Requests go out one K step at a time in order: (iss_tile, iss_kt) is the next one; past
+  // the last step the last one is requested again (never used).
+  int iss_tile = 0, iss_kt = 0;
+  auto issue = [&](int st, int g) {
+    int k0;
+    if (g < total) {
+      if (iss_kt == nk) {
+        iss_kt = 0;
+        ++iss_tile;
+        int itm, itn;
+        tile_coords(blockIdx.x + iss_tile * gridDim.x, ntiles, tiles_m, tiles_n, itm, itn);
+        set_issue_tile(itm, itn);
+      }
+      k0 = iss_kt * kBK2;
+      ++iss_kt;
+    } else {
+      k0 = (nk - 1) * kBK2;
+    }
     if constexpr (BUF) {
 #pragma unroll
       for (int j = 0; j < AJ; ++j)
@@ -614,29 +648,53 @@ void gemm_d2l_kernel(const GemmParams p) {
   // its reads of stage kt-1), refill stage kt-1's buffer with step kt+NS-1, then the two
   // 16-wide sub-steps; the second one reads sub-step 0 of step kt+1, so the MFMAs after the
   // next barrier start on operands already in registers.
-  auto step = [&](int u, int kt) {
+  auto step = [&](int u, int g) {
     wait_vm(std::integral_constant<int, (NS - 3) * LPS>{});
     convert_own((u + 1) % NS);
     barrier();
-    issue((u + NS - 1) % NS, kt + NS - 1);
+    issue((u + NS - 1) % NS, g + NS - 1);
     fread(u, 1, 1);
     mfmas(0);
     fread((u + 1) % NS, 0, 0);
     mfmas(1);
   };
   // Whole groups of NS steps without any branch (stage indices are constants after unrolling),
-  // then the remaining steps.
-  int kt = 0;
-  for (; kt + NS <= nk; kt += NS) {
+  // then the remaining steps (one-tile launches whose K steps are not a multiple of NS). With
+  // several tiles per workgroup (NS divides a tile's K steps, so every tile ends with a group),
+  // a finished tile's epilogue runs right after its last group: the next tile's first sub-step
+  // fragments are already in registers and its first stages are on their way.
+  int g = 0;
+  int done = 0, cur = 0;
+  for (; g + NS <= total; g += NS) {
 #pragma unroll
-    for (int u = 0; u < NS; ++u) step(u, kt + u);
+    for (int u = 0; u < NS; ++u) step(u, g + u);
+    if constexpr (EPI != EPI_STORE_F32) {
+      if (my_tiles > 1) {
+        done += NS;
+        if (done == nk) {
+          done = 0;
+          gemm_epilogue<BN, WM, WN, EPI, OP, TRANS>(p, acc, tm, tn, wm, wn, lane);
+          if (g + NS < total) {
+            ++cur;
+            tile_coords(blockIdx.x + cur * gridDim.x, ntiles, tiles_m, tiles_n, tm, tn);
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+              for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.f;
+          }
+        }
+      }
+    }
   }
 #pragma unroll
   for (int u = 0; u < NS - 1; ++u)
-    if (kt + u < nk) step(u, kt + u);
+    if (g + u < total) step(u, g + u);
 
   // the trailing reloads of the last tile must land before this workgroup's LDS is released
   Q3_WAIT_VMCNT(0);
+  if (my_tiles > 1) return;  // every tile's epilogue already ran
   constexpr bool LDS_EPI = Q3_GEMM_LDS_EPI && TRANS && EPI == EPI_STORE_F32 && WM == 2 && WN == 4 && BN == 256;
   if constexpr (LDS_EPI) {
     // fp32 output (residual already in the accumulators) through LDS: each wave owns one 16 KiB
@@ -682,6 +740,19 @@ void gemm_d2l_kernel(const GemmParams p) {
   }
 }
 
+// Compute units of the current device (cached per device id).
+static int gemm_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 // Buffer-descriptor loads address A and each B segment with 32-bit byte offsets, and one load
 // instruction covers 16 consecutive B rows of a single segment. Q3_GEMM_ADDR64 (environment)
 // forces the 64-bit address path, so that it can be tested at small sizes.
@@ -723,10 +794,17 @@ static hipError_t launch_t(const GemmParams& p, hipStream_t s) {
   constexpr int NS = (Q3_GEMM_STAGES * (kBM + BN) * 64 + (BN % 128 ? 1024 : 0) <= 160 * 1024)
                          ? Q3_GEMM_STAGES : 4;
   if (Q3_GEMM_D2L && p.K % kBK2 == 0) {
+    // 16-bit outputs with whole groups of NS K steps per tile: one workgroup per CU walks
+    // several tiles (grid a multiple of 8, so a workgroup keeps the XCD its tiles map to)
+    int grid = tiles;
+    if (EPI != EPI_STORE_F32 && (p.K / kBK2) % NS == 0 && Q3_GEMM_PERSIST) {
+      const int cus = gemm_cu_count();
+      if (cus >= 8 && tiles > cus) grid = cus & ~7;
+    }
     if (gemm_buffer_ok(p, EPI))
-      gemm_d2l_kernel<BN, WM, WN, EPI, OP, CVT, NS, true><<<tiles, 64 * WM * WN, 0, s>>>(p);
+      gemm_d2l_kernel<BN, WM, WN, EPI, OP, CVT, NS, true><<<grid, 64 * WM * WN, 0, s>>>(p);
     else
-      gemm_d2l_kernel<BN, WM, WN, EPI, OP, CVT, NS, false><<<tiles, 64 * WM * WN, 0, s>>>(p);
+      gemm_d2l_kernel<BN, WM, WN, EPI, OP, CVT, NS, false><<<grid, 64 * WM * WN, 0, s>>>(p);
   }
   else gemm_mfma_kernel<BN, WM, WN, EPI, OP, CVT><<<tiles, 64 * WM * WN, 0, s>>>(p);
   return hipGetLastError();
