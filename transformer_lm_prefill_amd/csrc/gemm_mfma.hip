@@ -50,8 +50,10 @@
 // workgroup, by the thread whose load brought them (after its own wait, before the barrier
 // that publishes the stage); 0: always per fragment, by every wave after its read; 1: in LDS
 // for tiles whose B fragments are read by four or more waves, per fragment otherwise.
+// 0 measured best (the in-LDS pass adds a read and a write of the B tile to the LDS traffic
+// that bounds the kernel: QKV 5% slower with 1)
 #ifndef Q3_GEMM_CVT_LDS
-#define Q3_GEMM_CVT_LDS 1
+#define Q3_GEMM_CVT_LDS 0
 #endif
 // 1: for fp32 outputs (with residual), the direct-to-LDS kernel computes C^T blocks (weight
 // fragment as the MFMA A operand), so each lane ends up with runs of 4 consecutive output
@@ -585,8 +587,8 @@ void gemm_d2l_kernel(const GemmParams p) {
       fb[set][ni] = stB(st)[row * 4 + (ch ^ swz4(row))];
     }
   };
-  // Where the bf16 -> fp16 weight conversion happens: in LDS once per workgroup when four or
-  // more waves share each B fragment (WM >= 4), else per fragment after the read.
+  // Where the bf16 -> fp16 weight conversion happens (Q3_GEMM_CVT_LDS): per fragment after the
+  // read, or in LDS once per workgroup.
   constexpr bool CVT_IN_LDS = CVT && (Q3_GEMM_CVT_LDS == 1 ? WM >= 4 : Q3_GEMM_CVT_LDS == 2);
   constexpr bool CVT_FRAG = CVT && !CVT_IN_LDS;
   auto mfmas = [&](int set) {
