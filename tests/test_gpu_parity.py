@@ -167,7 +167,10 @@ def test_attention_causality_bitwise():
                                                  ("bf16", "bf16", 300, 2048, 1536, True),
                                                  ("bf16", "f16", 64, 256, 640, False),
                                                  ("f16", "f16", 100, 512, 256, True),
-                                                 ("f32", "f32", 40, 256, 512, True)])
+                                                 ("f32", "f32", 40, 256, 512, True),
+                                                 # 6 x 48 = 288 gate/up tiles with a ragged last
+                                                 # tile row: persistent workgroups walk 1-2 tiles
+                                                 ("bf16", "f16", 1500, 2048, 6144, True)])
 def test_swiglu_ffn(wdt, xdt, s, h, f, resid):
     x = _normal(50, (s, h), dtype="f32")
     x = synth.round_to_bf16(x) if xdt == "bf16" else (x.astype(np.float16).astype(np.float32) if xdt == "f16" else x)
@@ -374,6 +377,9 @@ _SHAPES = {
     "hd64_mha": (1024, 16, 16, 64, 2048, 300, (12, 10, 10)),
     "hd64_gqa4": (1024, 16, 4, 64, 2048, 333, (12, 10, 10)),
     "hd128_gqa8": (2048, 16, 2, 128, 2048, 200, (24, 20, 20)),
+    # 3 heads of 64: the o-projection has K = 192, 6 K steps per tile, not a multiple of the
+    # 4-stage ring (the GEMM's tail steps)
+    "hd64_mha3_k192": (256, 3, 3, 64, 256, 150, (12, 10, 10)),
 }
 
 
