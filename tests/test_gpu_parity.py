@@ -190,11 +190,13 @@ def test_swiglu_ffn(wdt, xdt, s, h, f, resid):
     assert err <= (TOL["f32"] if wdt == "f32" else TOL["bf16"])
 
 
-@pytest.mark.parametrize("wdt,out_dtype", [("bf16", None), ("f16", torch.float16)])
-def test_swiglu_ffn_64bit_address_path(monkeypatch, wdt, out_dtype):
+@pytest.mark.parametrize("wdt,out_dtype,s,h,f", [("bf16", None, 300, 512, 640), ("f16", torch.float16, 300, 512, 640),
+                                                 # 288 gate/up tiles: the persistent form walks
+                                                 # tiles on the 64-bit path too
+                                                 ("bf16", None, 1500, 2048, 6144)])
+def test_swiglu_ffn_64bit_address_path(monkeypatch, wdt, out_dtype, s, h, f):
     """GEMM operands fetched through 64-bit addresses (taken when an operand's byte extent
     exceeds the 32-bit range of buffer loads) give the same bits as the buffer-load path."""
-    s, h, f = 300, 512, 640
     x = dev(_normal(80, (s, h)), "f16")
     wg, wu, wd = (dev(_normal(81 + i, sh, std=0.02), wdt) for i, sh in enumerate(((f, h), (f, h), (h, f))))
     r = None if out_dtype is not None else dev(_normal(84, (s, h), dtype="f32"))
