@@ -387,8 +387,8 @@ def main():
         copy_calibration()
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the multi-GPU sequence-sharded path is a design, not an implementation)",
+        print(f"bench.py: the library runs on one GPU; --gpus {args.gpus} is not supported "
+              "(multi-GPU sequence sharding is designed, not implemented)",
               file=sys.stderr)
         sys.exit(2)
 
