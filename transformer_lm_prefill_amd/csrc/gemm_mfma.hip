@@ -43,9 +43,6 @@
 #ifndef Q3_GEMM_STAGES
 #define Q3_GEMM_STAGES 4
 #endif
-#ifndef Q3_GEMM_W4
-#define Q3_GEMM_W4 0
-#endif
 // Where bf16 weights become fp16 in the direct-to-LDS kernel: 2: always in LDS, once per
 // workgroup, by the thread whose load brought them (after its own wait, before the barrier
 // that publishes the stage); 0: always per fragment, by every wave after its read; 1: in LDS
@@ -68,7 +65,7 @@
 #define Q3_GEMM_TRANS 1
 #endif
 // 1: fp32 outputs of the 256 x 256 tile leave through LDS as whole 256-byte row segments
-// 1: GEMMs with 16-bit outputs run as persistent workgroups (one per CU, several tiles each)
+// 1: the gate/up SwiGLU GEMM runs as persistent workgroups (one per CU, several tiles each)
 #ifndef Q3_GEMM_PERSIST
 #define Q3_GEMM_PERSIST 1
 #endif
@@ -439,7 +436,7 @@ void gemm_d2l_kernel(const GemmParams p) {
   const int tiles_m = (p.M + kBM - 1) / kBM;
   const int tiles_n = p.N / BN;
   const int ntiles = tiles_m * tiles_n;
-  // Persistent form (16-bit outputs): a grid smaller than the tile count walks tiles
+  // Persistent form (SwiGLU output): a grid smaller than the tile count walks tiles
   // blockIdx.x, + gridDim.x, ... (each the tile a one-tile-per-workgroup launch would give that
   // workgroup id, on the same XCD when gridDim.x % 8 == 0); the LDS ring runs on across tile
   // boundaries, so the next tile's first K steps load during this tile's last ones and its
@@ -670,22 +667,21 @@ void gemm_d2l_kernel(const GemmParams p) {
   for (; g + NS <= total; g += NS) {
 #pragma unroll
     for (int u = 0; u < NS; ++u) step(u, g + u);
-    if constexpr (EPI != EPI_STORE_F32) {
-      if (my_tiles > 1) {
-        done += NS;
-        if (done == nk) {
-          done = 0;
-          gemm_epilogue<BN, WM, WN, EPI, OP, TRANS>(p, acc, tm, tn, wm, wn, lane);
-          if (g + NS < total) {
-            ++cur;
-            tile_coords(blockIdx.x + cur * gridDim.x, ntiles, tiles_m, tiles_n, tm, tn);
+    if constexpr (EPI == EPI_SWIGLU_16) {
+      const bool tile_end = my_tiles > 1 && done + NS == nk;
+      if (my_tiles > 1) done += NS;
+      if (tile_end) {
+        done = 0;
+        gemm_epilogue<BN, WM, WN, EPI, OP, TRANS>(p, acc, tm, tn, wm, wn, lane);
+        if (g + NS < total) {
+          ++cur;
+          tile_coords(blockIdx.x + cur * gridDim.x, ntiles, tiles_m, tiles_n, tm, tn);
 #pragma unroll
-            for (int mi = 0; mi < MI; ++mi)
+          for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-              for (int ni = 0; ni < NI; ++ni)
+            for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.f;
-          }
+              for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.f;
         }
       }
     }
@@ -796,10 +792,12 @@ static hipError_t launch_t(const GemmParams& p, hipStream_t s) {
   constexpr int NS = (Q3_GEMM_STAGES * (kBM + BN) * 64 + (BN % 128 ? 1024 : 0) <= 160 * 1024)
                          ? Q3_GEMM_STAGES : 4;
   if (Q3_GEMM_D2L && p.K % kBK2 == 0) {
-    // 16-bit outputs with whole groups of NS K steps per tile: one workgroup per CU walks
-    // several tiles (grid a multiple of 8, so a workgroup keeps the XCD its tiles map to)
+    // SwiGLU outputs with whole groups of NS K steps per tile: one workgroup per CU walks
+    // several tiles (grid a multiple of 8, so a workgroup keeps the XCD its tiles map to). The
+    // 16-bit store epilogue inside the loop pushed the QKV tiles past 256 registers (spills), so
+    // those stay one tile per workgroup.
     int grid = tiles;
-    if (EPI != EPI_STORE_F32 && (p.K / kBK2) % NS == 0 && Q3_GEMM_PERSIST) {
+    if (EPI == EPI_SWIGLU_16 && (p.K / kBK2) % NS == 0 && Q3_GEMM_PERSIST) {
       const int cus = gemm_cu_count();
       if (cus >= 8 && tiles > cus) grid = cus & ~7;
     }
@@ -815,10 +813,7 @@ static hipError_t launch_t(const GemmParams& p, hipStream_t s) {
 // nb selects the tile width 64*nb: 256 (8 waves, 2 x 4), 192 (8 waves, 4 x 2), 128 (8 waves, 4 x 2)
 template <int EPI, int OP, bool CVT>
 static hipError_t launch_nb(const GemmParams& p, int nb, hipStream_t s) {
-  if (nb == 4) {
-    if (Q3_GEMM_W4) return launch_t<256, 2, 2, EPI, OP, CVT>(p, s);
-    return launch_t<256, 2, 4, EPI, OP, CVT>(p, s);
-  }
+  if (nb == 4) return launch_t<256, 2, 4, EPI, OP, CVT>(p, s);
   if (EPI == EPI_SWIGLU_16) return hipErrorInvalidValue;
   if (nb == 3) return launch_t<192, 4, 2, EPI, OP, CVT>(p, s);
   if (nb == 2) return launch_t<128, 4, 2, EPI, OP, CVT>(p, s);
