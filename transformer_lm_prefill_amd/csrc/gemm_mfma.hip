@@ -47,10 +47,14 @@
 // workgroup, by the thread whose load brought them (after its own wait, before the barrier
 // that publishes the stage); 0: always per fragment, by every wave after its read; 1: in LDS
 // for tiles whose B fragments are read by four or more waves, per fragment otherwise.
-// 0 measured best (the in-LDS pass adds a read and a write of the B tile to the LDS traffic
-// that bounds the kernel: QKV 5% slower with 1)
+// 3: tiles whose B fragments four or more waves read (QKV) stage B through registers (global
+// load, one conversion per element, LDS store), per fragment otherwise. Measured at the 8B
+// shape: 3 is best (QKV 8% faster than 0, same bits); 1 and 2 add a read and a write of the B
+// tile to the LDS traffic that bounds the kernel (QKV 5% slower than 0); staging the
+// two-wave-shared tiles of o-proj / down too gains at most 1%, and the gate/up kernel has no
+// registers for it.
 #ifndef Q3_GEMM_CVT_LDS
-#define Q3_GEMM_CVT_LDS 0
+#define Q3_GEMM_CVT_LDS 3
 #endif
 // 1: for fp32 outputs (with residual), the direct-to-LDS kernel computes C^T blocks (weight
 // fragment as the MFMA A operand), so each lane ends up with runs of 4 consecutive output
@@ -528,6 +532,10 @@ void gemm_d2l_kernel(const GemmParams p) {
     }
   }
 
+  // STAGE_B: B tiles come through registers (one 16-byte load per slot), are converted once
+  // and stored to LDS by the same thread before the barrier that publishes the stage
+  constexpr bool STAGE_B = CVT && Q3_GEMM_CVT_LDS == 3 && WM >= 4;
+  u32x4 breg[NS][BJ];
   const int nk = p.K / kBK2;
   const int total = my_tiles * nk;  // K steps of all this workgroup's tiles, in order
   // Requests go out one K step at a time in order: (iss_tile, iss_kt) is the next one; past
@@ -555,7 +563,10 @@ void gemm_d2l_kernel(const GemmParams p) {
 #pragma unroll
       for (int j = 0; j < BJ; ++j) {
         const int blk = wave + j * WAVES;
-        buf2lds(rsrc_b[j], stB(st) + (blk * 64 < BSLOT ? blk : BSLOT / 64) * 64, voff_b[j], 2 * k0);
+        if constexpr (STAGE_B)
+          breg[st][j] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_b[j], voff_b[j], 2 * k0, 0);
+        else
+          buf2lds(rsrc_b[j], stB(st) + (blk * 64 < BSLOT ? blk : BSLOT / 64) * 64, voff_b[j], 2 * k0);
       }
     } else {
 #pragma unroll
@@ -563,7 +574,10 @@ void gemm_d2l_kernel(const GemmParams p) {
 #pragma unroll
       for (int j = 0; j < BJ; ++j) {
         const int blk = wave + j * WAVES;
-        g2lds(b_src[j] + k0, stB(st) + (blk * 64 < BSLOT ? blk : BSLOT / 64) * 64);
+        if constexpr (STAGE_B)
+          breg[st][j] = *reinterpret_cast<const u32x4*>(b_src[j] + k0);
+        else
+          g2lds(b_src[j] + k0, stB(st) + (blk * 64 < BSLOT ? blk : BSLOT / 64) * 64);
       }
     }
   };
@@ -585,9 +599,9 @@ void gemm_d2l_kernel(const GemmParams p) {
     }
   };
   // Where the bf16 -> fp16 weight conversion happens (Q3_GEMM_CVT_LDS): per fragment after the
-  // read, or in LDS once per workgroup.
+  // read, in LDS once per workgroup, or (STAGE_B) once per workgroup on the way into LDS.
   constexpr bool CVT_IN_LDS = CVT && (Q3_GEMM_CVT_LDS == 1 ? WM >= 4 : Q3_GEMM_CVT_LDS == 2);
-  constexpr bool CVT_FRAG = CVT && !CVT_IN_LDS;
+  constexpr bool CVT_FRAG = CVT && !CVT_IN_LDS && !STAGE_B;
   auto mfmas = [&](int set) {
     u32x4 bv[NI];
 #pragma unroll
@@ -608,6 +622,18 @@ void gemm_d2l_kernel(const GemmParams p) {
   // In-LDS conversion of the B slots this thread loaded into stage st (its own loads of that
   // stage must have landed).
   auto convert_own = [&](int st) {
+    if constexpr (STAGE_B) {
+#pragma unroll
+      for (int j = 0; j < BJ; ++j) {
+        const int blk = wave + j * WAVES;
+        if (blk * 64 < BSLOT) {
+          u32x4 v = breg[st][j];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = bf16x2_to_f16x2(v[e]);
+          stB(st)[blk * 64 + lane] = v;
+        }
+      }
+    }
     if (CVT_IN_LDS) {
 #pragma unroll
       for (int j = 0; j < BJ; ++j) {
