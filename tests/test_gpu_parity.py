@@ -53,6 +53,10 @@ def test_rms_norm_rows(wdt, ydt, rows, hidden):
     ("f16", "bf16", 128, (24, 20, 20), 5e6, 77, 64, 8, False),
     ("f32", "f32", 64, (12, 10, 10), 1e6, 45, 4, 2, False),
     ("f32", "f32", 128, (24, 20, 20), 5e6, 70, 3, 1, True),
+    # one token at the 8B head layout (two passes of rows, one workgroup each) and a few
+    # tokens with three passes per token
+    ("f16", "bf16", 128, (24, 20, 20), 5e6, 1, 32, 8, False),
+    ("bf16", "bf16", 128, (24, 20, 20), 5e6, 3, 64, 8, False),
 ])
 def test_qk_norm_mrope(dtype, ndt, hd, sec, theta, s, nh, nkv, image):
     q = _normal(3, (s, nh, hd), dtype=dtype if dtype != "f16" else "f32") * 2

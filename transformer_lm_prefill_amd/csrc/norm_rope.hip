@@ -183,6 +183,9 @@ hipError_t launch_deepstack_add(float* y, const int32_t* rows, const void* ds, i
 constexpr int kRopeTokens = 4;
 // rotation pairs per lane: 8 (16-byte accesses for 16-bit rows; 6% faster than 4 at the 8B shape)
 constexpr int kRopePairs = 8;
+// below this many token blocks (fewer than the CUs) the launch splits each token's head rows
+// over workgroups instead
+constexpr int kRopeSplitBelow = 256;
 struct RopeFreqs {
   double inv[64];
 };
@@ -279,9 +282,14 @@ __global__ __launch_bounds__(256) void qk_norm_mrope_kernel(const RopeParams p, 
     kb[e] = load_elem(p.k_norm, i + HALF, p.norm_dt);
   }
 
-  // head rows of the TPW tokens in token order: row index hh = token * (nh + nkv) + head
+  // head rows of the TPW tokens in token order: row index hh = token * (nh + nkv) + head.
+  // With gridDim.y > 1 the q/k workgroups of a token block take every qk_groups-th pass of
+  // rows, and with a cache to fill the last workgroup appends the v rows alone.
   const int nrows = p.nh + p.nkv;
-  for (int hh = sub; hh < TPW * nrows; hh += ROWS_PER_PASS) {
+  const int gy = static_cast<int>(gridDim.y), by = static_cast<int>(blockIdx.y);
+  const int qk_groups = (p.kc && gy > 1) ? gy - 1 : gy;
+  const int stride = ROWS_PER_PASS * qk_groups;
+  for (int hh = by < qk_groups ? sub + by * ROWS_PER_PASS : TPW * nrows; hh < TPW * nrows; hh += stride) {
     const int tt = TPW == 1 ? 0 : hh / nrows;
     const int h = TPW == 1 ? hh : hh - tt * nrows;
     const int s = s0 + tt;
@@ -332,7 +340,7 @@ __global__ __launch_bounds__(256) void qk_norm_mrope_kernel(const RopeParams p, 
     }
   }
   // cache append of the tokens' v rows (same lane layout, no arithmetic)
-  if (p.kc) {
+  if (p.kc && (gy == 1 || by == gy - 1)) {
     for (int hh = sub; hh < TPW * p.nkv; hh += ROWS_PER_PASS) {
       const int tt = TPW == 1 ? 0 : hh / p.nkv;
       const int g = hh - tt * p.nkv;
@@ -351,13 +359,9 @@ __global__ __launch_bounds__(256) void qk_norm_mrope_kernel(const RopeParams p, 
   }
 }
 
-template <int HD>
-static hipError_t rope_launch(const RopeParams& p, int dt, hipStream_t s) {
-  constexpr int TPW = kRopeTokens;
-  dim3 grid((p.S + TPW - 1) / TPW), block(256);
-  // theta^(-2i/hd) for i < hd/2, in double on the host, passed with the launch
-  RopeFreqs f;
-  for (int i = 0; i < HD / 2; ++i) f.inv[i] = std::exp2(-(2.0 * i / HD) * p.log2_theta);
+template <int HD, int TPW>
+static hipError_t rope_launch_t(const RopeParams& p, int dt, dim3 grid, const RopeFreqs& f, hipStream_t s) {
+  const dim3 block(256);
   switch (dt) {
     case DT_F32: qk_norm_mrope_kernel<DT_F32, HD, TPW, kRopePairs><<<grid, block, 0, s>>>(p, f); break;
     case DT_BF16: qk_norm_mrope_kernel<DT_BF16, HD, TPW, kRopePairs><<<grid, block, 0, s>>>(p, f); break;
@@ -365,6 +369,22 @@ static hipError_t rope_launch(const RopeParams& p, int dt, hipStream_t s) {
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int HD>
+static hipError_t rope_launch(const RopeParams& p, int dt, hipStream_t s) {
+  // theta^(-2i/hd) for i < hd/2, in double on the host, passed with the launch
+  RopeFreqs f;
+  for (int i = 0; i < HD / 2; ++i) f.inv[i] = std::exp2(-(2.0 * i / HD) * p.log2_theta);
+  constexpr int TPW = kRopeTokens;
+  const int blocks = (p.S + TPW - 1) / TPW;
+  if (blocks >= kRopeSplitBelow) return rope_launch_t<HD, TPW>(p, dt, dim3(blocks), f, s);
+  // few tokens (decode, short prompts): one token per workgroup and its head rows split over
+  // workgroups, one pass of rows each, so that no workgroup runs passes one after another
+  constexpr int LPR = HD / 2 / kRopePairs;
+  constexpr int ROWS_PER_PASS = 4 * (64 / LPR);
+  const int passes = (p.nh + p.nkv + ROWS_PER_PASS - 1) / ROWS_PER_PASS;
+  return rope_launch_t<HD, 1>(p, dt, dim3(p.S, passes + (p.kc ? 1 : 0)), f, s);
 }
 
 hipError_t launch_qk_norm_mrope(const RopeParams& p, int head_dim, int data_dt, hipStream_t s) {
