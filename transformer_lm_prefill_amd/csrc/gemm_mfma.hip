@@ -26,8 +26,6 @@
 //   sharing A rows and B columns in its own L2;
 //   for fp32 outputs the accumulators hold C^T blocks, so the residual epilogue moves 16-byte
 //   runs of one row.
-// A register-staged kernel (gemm_mfma_kernel: K step 64, double-buffered LDS) serves K that
-// is not a multiple of 32.
 #include <algorithm>
 #include <cstdlib>
 #include <type_traits>
@@ -35,9 +33,6 @@
 #include "common.h"
 #include "kernels.h"
 
-#ifndef Q3_GEMM_D2L
-#define Q3_GEMM_D2L 1
-#endif
 // LDS ring depth of the direct-to-LDS kernel (stages of 32-wide K steps; tiles that would not
 // fit in 160 KiB use 4)
 #ifndef Q3_GEMM_STAGES
@@ -80,9 +75,7 @@
 namespace q3 {
 
 constexpr int kBM = 256;
-constexpr int kBK = 64;
-
-__device__ __forceinline__ int swz8(int row) { return (row ^ (row >> 3)) & 7; }
+constexpr int kBK = 64;  // K must be a multiple of this
 
 // Workgroup id -> (tile row, tile column). Hardware dispatches ids round-robin over the 8
 // XCDs; ids are first regrouped so that XCD x gets a contiguous range of logical ids, then
@@ -253,123 +246,6 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p,
     if (tm * kBM + kBM <= p.M) store_all(std::false_type{});
     else store_all(std::true_type{});
   }
-}
-
-// BN: tile width; WM x WN waves (two or four along each side), each owning a wave tile of
-// (256/WM) x (BN/WN) = MI x NI MFMA blocks of 32 x 32.
-template <int BN, int WM, int WN, int EPI, int OP, bool CVT>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * WM * WN, 64 * WM * WN),
-                          amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4)))
-void gemm_mfma_kernel(const GemmParams p) {
-  using F = Fmt<OP>;
-  constexpr int THREADS = 64 * WM * WN;
-  constexpr int MI = kBM / WM / 32;            // MFMA blocks per wave along M
-  constexpr int NI = BN / WN / 32;             // MFMA blocks per wave along N
-  constexpr int RSTEP = THREADS / 8;           // tile rows covered by one pass of the loaders
-  constexpr int ACH = kBM / RSTEP;             // 16-byte chunks per thread, A tile
-  constexpr int BCH = BN / RSTEP;              // 16-byte chunks per thread, B tile
-  static_assert(MI >= 1 && NI >= 1 && BN % RSTEP == 0, "tile shape");
-  __shared__ u32x4 As[2][kBM * 8];
-  __shared__ u32x4 Bs[2][BN * 8];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave / WN;
-  const int wn = wave % WN;
-  const int tiles_m = (p.M + kBM - 1) / kBM;
-  const int tiles_n = p.N / BN;
-  int tm, tn;
-  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
-
-  const int lrow = tid >> 3;
-  const int lch = tid & 7;    // 16-byte chunk within a 64-wide K step
-
-  // A rows: element offsets from A (rows past M are clamped: read, never stored)
-  uint32_t a_off[ACH];
-#pragma unroll
-  for (int j = 0; j < ACH; ++j) {
-    const int r = min(tm * kBM + lrow + RSTEP * j, p.M - 1);
-    a_off[j] = static_cast<uint32_t>(r) * static_cast<uint32_t>(p.lda) + lch * 8;
-  }
-  const uint16_t* b_src[BCH];
-#pragma unroll
-  for (int j = 0; j < BCH; ++j) b_src[j] = b_row<BN, WN, EPI>(p, tn, lrow + RSTEP * j) + lch * 8;
-
-  const int fr = lane & 31;
-  const int fh = lane >> 5;
-
-  u32x4 ra[ACH], rb[BCH];
-  f32x16 acc[MI][NI];
-#pragma unroll
-  for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.f;
-
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int j = 0; j < ACH; ++j) ra[j] = *reinterpret_cast<const u32x4*>(p.A + a_off[j] + k0);
-#pragma unroll
-    for (int j = 0; j < BCH; ++j) rb[j] = *reinterpret_cast<const u32x4*>(b_src[j] + k0);
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < ACH; ++j) {
-      const int row = lrow + RSTEP * j;
-      As[buf][row * 8 + (lch ^ swz8(row))] = ra[j];
-    }
-#pragma unroll
-    for (int j = 0; j < BCH; ++j) {
-      u32x4 v = rb[j];
-      if (CVT) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = bf16x2_to_f16x2(v[e]);
-      }
-      const int row = lrow + RSTEP * j;
-      Bs[buf][row * 8 + (lch ^ swz8(row))] = v;
-    }
-  };
-  auto fread = [&](int buf, int ks, u32x4 (&fa)[MI], u32x4 (&fb)[NI]) {
-    const int ch = ks * 2 + fh;
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-      const int row = wm * (32 * MI) + mi * 32 + fr;
-      fa[mi] = As[buf][row * 8 + (ch ^ swz8(row))];
-    }
-#pragma unroll
-    for (int ni = 0; ni < NI; ++ni) {
-      const int row = wn * (32 * NI) + ni * 32 + fr;
-      fb[ni] = Bs[buf][row * 8 + (ch ^ swz8(row))];
-    }
-  };
-
-  const int nk = p.K / kBK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    // next K step's tile (the last step re-reads its own tile: same addresses, no branch)
-    gload(kt + 1 < nk ? (kt + 1) * kBK : kt * kBK);
-    u32x4 fa[2][MI], fb[2][NI];
-    fread(buf, 0, fa[0], fb[0]);
-#pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      if (ks + 1 < kBK / 16) fread(buf, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
-          acc[mi][ni] = F::mfma(fa[ks & 1][mi], fb[ks & 1][ni], acc[mi][ni]);
-    }
-    lstore(buf ^ 1);
-    __syncthreads();
-  }
-
-  gemm_epilogue<BN, WM, WN, EPI, OP>(p, acc, tm, tn, wm, wn, lane);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -817,22 +693,19 @@ static hipError_t launch_t(const GemmParams& p, hipStream_t s) {
   const int tiles = ((p.M + kBM - 1) / kBM) * (p.N / BN);
   constexpr int NS = (Q3_GEMM_STAGES * (kBM + BN) * 64 + (BN % 128 ? 1024 : 0) <= 160 * 1024)
                          ? Q3_GEMM_STAGES : 4;
-  if (Q3_GEMM_D2L && p.K % kBK2 == 0) {
-    // SwiGLU outputs with whole groups of NS K steps per tile: one workgroup per CU walks
-    // several tiles (grid a multiple of 8, so a workgroup keeps the XCD its tiles map to). The
-    // 16-bit store epilogue inside the loop pushed the QKV tiles past 256 registers (spills), so
-    // those stay one tile per workgroup.
-    int grid = tiles;
-    if (EPI == EPI_SWIGLU_16 && (p.K / kBK2) % NS == 0 && Q3_GEMM_PERSIST) {
-      const int cus = gemm_cu_count();
-      if (cus >= 8 && tiles > cus) grid = cus & ~7;
-    }
-    if (gemm_buffer_ok(p, EPI))
-      gemm_d2l_kernel<BN, WM, WN, EPI, OP, CVT, NS, true><<<grid, 64 * WM * WN, 0, s>>>(p);
-    else
-      gemm_d2l_kernel<BN, WM, WN, EPI, OP, CVT, NS, false><<<grid, 64 * WM * WN, 0, s>>>(p);
+  // SwiGLU outputs with whole groups of NS K steps per tile: one workgroup per CU walks
+  // several tiles (grid a multiple of 8, so a workgroup keeps the XCD its tiles map to). The
+  // 16-bit store epilogue inside the loop pushed the QKV tiles past 256 registers (spills), so
+  // those stay one tile per workgroup.
+  int grid = tiles;
+  if (EPI == EPI_SWIGLU_16 && (p.K / kBK2) % NS == 0 && Q3_GEMM_PERSIST) {
+    const int cus = gemm_cu_count();
+    if (cus >= 8 && tiles > cus) grid = cus & ~7;
   }
-  else gemm_mfma_kernel<BN, WM, WN, EPI, OP, CVT><<<tiles, 64 * WM * WN, 0, s>>>(p);
+  if (gemm_buffer_ok(p, EPI))
+    gemm_d2l_kernel<BN, WM, WN, EPI, OP, CVT, NS, true><<<grid, 64 * WM * WN, 0, s>>>(p);
+  else
+    gemm_d2l_kernel<BN, WM, WN, EPI, OP, CVT, NS, false><<<grid, 64 * WM * WN, 0, s>>>(p);
   return hipGetLastError();
 }
 
