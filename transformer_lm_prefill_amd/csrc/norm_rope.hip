@@ -252,14 +252,54 @@ __global__ __launch_bounds__(256) void qk_norm_mrope_kernel(const RopeParams p, 
   const int i0 = PPL * (lane % LPR);
   const int sub = (threadIdx.x >> 6) * ROWS_PER_WAVE + lane / LPR;
 
+  // head rows of the TPW tokens in token order: row index hh = token * (nh + nkv) + head.
+  // With gridDim.y > 1 the q/k workgroups of a token block take every qk_groups-th pass of
+  // rows, and with a cache to fill the last workgroup appends the v rows alone.
+  const int nrows = p.nh + p.nkv;
+  const int gy = static_cast<int>(gridDim.y), by = static_cast<int>(blockIdx.y);
+  const int qk_groups = (p.kc && gy > 1) ? gy - 1 : gy;
+  const int stride = ROWS_PER_PASS * qk_groups;
+  auto valid_row = [&](int hh) { return hh < TPW * nrows && s0 + (TPW == 1 ? 0 : hh / nrows) < p.S; };
+  auto row_at = [&](int hh, int& tt, int& h) -> void* {
+    tt = TPW == 1 ? 0 : hh / nrows;
+    h = TPW == 1 ? hh : hh - tt * nrows;
+    const int64_t s = s0 + tt;
+    return h < p.nh ? static_cast<void*>(static_cast<char*>(p.q) +
+                                         (s * p.q_stride + static_cast<int64_t>(h) * HD) * (DT == DT_F32 ? 4 : 2))
+                    : static_cast<void*>(static_cast<char*>(p.k) +
+                                         (s * p.k_stride + static_cast<int64_t>(h - p.nh) * HD) * (DT == DT_F32 ? 4 : 2));
+  };
+  // the first row's loads and the lane's norm weights (entries i0.. and i0+hd/2.. of each,
+  // one vector load per run, the dtype resolved once) go out before the angles are formed
+  int hh = by < qk_groups ? sub + by * ROWS_PER_PASS : TPW * nrows;
+  bool ok = valid_row(hh);
+  int tt = 0, h = 0;
+  // (a lane group without rows loads row 0 of token s0, which every launched workgroup has,
+  // and never uses it: the loads stay unconditional)
+  void* row = row_at(ok ? hh : 0, tt, h);
+  float a[PPL], b[PPL];
+  ld_run<DT, PPL>(row, i0, a);
+  ld_run<DT, PPL>(row, i0 + HALF, b);
+  float qa[PPL], qb[PPL], ka[PPL], kb[PPL];
+  auto load_norms = [&](auto dt) {
+    constexpr int ND = decltype(dt)::value;
+    ld_run<ND, PPL>(p.q_norm, i0, qa);
+    ld_run<ND, PPL>(p.q_norm, i0 + HALF, qb);
+    ld_run<ND, PPL>(p.k_norm, i0, ka);
+    ld_run<ND, PPL>(p.k_norm, i0 + HALF, kb);
+  };
+  if (p.norm_dt == DT_BF16) load_norms(std::integral_constant<int, DT_BF16>{});
+  else if (p.norm_dt == DT_F16) load_norms(std::integral_constant<int, DT_F16>{});
+  else load_norms(std::integral_constant<int, DT_F32>{});
+
   // the hd/2 angles of each of the workgroup's TPW tokens, each formed once (thread
   // t*hd/2 + i forms angle i of token s0 + t) and shared through LDS
   __shared__ __attribute__((aligned(16))) float s_cs[TPW][HALF];
   __shared__ __attribute__((aligned(16))) float s_sn[TPW][HALF];
   if (threadIdx.x < TPW * HALF) {
-    const int tt = threadIdx.x / HALF;
+    const int ta = threadIdx.x / HALF;
     const int i = threadIdx.x % HALF;
-    const int s = s0 + tt;
+    const int s = s0 + ta;
     if (s < p.S) {
       int axis = 0;
       if (i % 3 == 1 && i < 3 * p.sec_h) axis = 1;
@@ -268,43 +308,24 @@ __global__ __launch_bounds__(256) void qk_norm_mrope_kernel(const RopeParams p, 
       const double phi = pos * inv_freq[i];
       const double two_pi = 6.283185307179586476925286766559;
       const double red = fma(-two_pi, rint(phi * (1.0 / two_pi)), phi);
-      sincosf(static_cast<float>(red), &s_sn[tt][i], &s_cs[tt][i]);
+      sincosf(static_cast<float>(red), &s_sn[ta][i], &s_cs[ta][i]);
     }
   }
   __syncthreads();
-  float qa[PPL], qb[PPL], ka[PPL], kb[PPL];
-#pragma unroll
-  for (int e = 0; e < PPL; ++e) {
-    const int i = i0 + e;
-    qa[e] = load_elem(p.q_norm, i, p.norm_dt);
-    qb[e] = load_elem(p.q_norm, i + HALF, p.norm_dt);
-    ka[e] = load_elem(p.k_norm, i, p.norm_dt);
-    kb[e] = load_elem(p.k_norm, i + HALF, p.norm_dt);
-  }
 
-  // head rows of the TPW tokens in token order: row index hh = token * (nh + nkv) + head.
-  // With gridDim.y > 1 the q/k workgroups of a token block take every qk_groups-th pass of
-  // rows, and with a cache to fill the last workgroup appends the v rows alone.
-  const int nrows = p.nh + p.nkv;
-  const int gy = static_cast<int>(gridDim.y), by = static_cast<int>(blockIdx.y);
-  const int qk_groups = (p.kc && gy > 1) ? gy - 1 : gy;
-  const int stride = ROWS_PER_PASS * qk_groups;
-  for (int hh = by < qk_groups ? sub + by * ROWS_PER_PASS : TPW * nrows; hh < TPW * nrows; hh += stride) {
-    const int tt = TPW == 1 ? 0 : hh / nrows;
-    const int h = TPW == 1 ? hh : hh - tt * nrows;
+  // Each row's successor (same lane group, the next pass) is loaded before the row is
+  // written back, so its load overlaps this row's arithmetic and stores; past the last row the
+  // current row is loaded again and never used.
+  while (ok) {
+    const int hn = hh + stride;
+    const bool okn = valid_row(hn);
+    int ttn = tt, hnh = h;
+    void* rown = okn ? row_at(hn, ttn, hnh) : row;
+    float na[PPL], nb[PPL];
+    ld_run<DT, PPL>(rown, i0, na);
+    ld_run<DT, PPL>(rown, i0 + HALF, nb);
     const int s = s0 + tt;
-    if (s >= p.S) break;
     const bool is_q = h < p.nh;
-    void* row = is_q ? static_cast<void*>(static_cast<char*>(p.q) +
-                                          (static_cast<int64_t>(s) * p.q_stride + static_cast<int64_t>(h) * HD) *
-                                              (DT == DT_F32 ? 4 : 2))
-                     : static_cast<void*>(static_cast<char*>(p.k) +
-                                          (static_cast<int64_t>(s) * p.k_stride +
-                                           static_cast<int64_t>(h - p.nh) * HD) *
-                                              (DT == DT_F32 ? 4 : 2));
-    float a[PPL], b[PPL];
-    ld_run<DT, PPL>(row, i0, a);
-    ld_run<DT, PPL>(row, i0 + HALF, b);
     float cs[PPL], sn[PPL];
 #pragma unroll
     for (int e4 = 0; e4 < PPL; e4 += 4) {
@@ -338,13 +359,23 @@ __global__ __launch_bounds__(256) void qk_norm_mrope_kernel(const RopeParams p, 
       st_run_dt<PPL>(crow, i0, ra, p.cache_dt);
       st_run_dt<PPL>(crow, i0 + HALF, rb, p.cache_dt);
     }
+    hh = hn;
+    ok = okn;
+    tt = ttn;
+    h = hnh;
+    row = rown;
+#pragma unroll
+    for (int e = 0; e < PPL; ++e) {
+      a[e] = na[e];
+      b[e] = nb[e];
+    }
   }
   // cache append of the tokens' v rows (same lane layout, no arithmetic)
   if (p.kc && (gy == 1 || by == gy - 1)) {
-    for (int hh = sub; hh < TPW * p.nkv; hh += ROWS_PER_PASS) {
-      const int tt = TPW == 1 ? 0 : hh / p.nkv;
-      const int g = hh - tt * p.nkv;
-      const int s = s0 + tt;
+    for (int hv = sub; hv < TPW * p.nkv; hv += ROWS_PER_PASS) {
+      const int tv = TPW == 1 ? 0 : hv / p.nkv;
+      const int g = hv - tv * p.nkv;
+      const int s = s0 + tv;
       if (s >= p.S) break;
       const void* vrow = static_cast<const char*>(p.v) +
                          (static_cast<int64_t>(s) * p.v_stride + static_cast<int64_t>(g) * HD) * (DT == DT_F32 ? 4 : 2);
