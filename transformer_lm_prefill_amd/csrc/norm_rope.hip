@@ -44,8 +44,10 @@ __device__ __forceinline__ void store4(void* p, int64_t c, f32x4 v) {
 
 // Streaming form: a fixed grid of workgroups walks the rows (row r, r + grid, ...), loading the
 // next row into registers while the current one is reduced and written, so reads and writes
-// overlap instead of alternating in bursts. NV float4 per thread per row.
-template <int W_DT, int Y_DT, int NV>
+// overlap instead of alternating in bursts. NV float4 per thread per row; FULL: hidden is
+// exactly 4 * NV * kNormThreads, so no chunk needs a bounds check and every load is issued
+// unconditionally.
+template <int W_DT, int Y_DT, int NV, bool FULL>
 __global__ __launch_bounds__(kNormThreads) void rmsnorm_stream_kernel(const float* __restrict__ x,
                                                                       const void* __restrict__ w,
                                                                       void* __restrict__ y, int rows,
@@ -55,27 +57,29 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_stream_kernel(const floa
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int c = threadIdx.x + i * kNormThreads;
-    if (c < nv) g[i] = load4<W_DT>(w, c);
+    if (FULL || c < nv) g[i] = load4<W_DT>(w, c);
   }
   auto load_row = [&](f32x4 (&v)[NV], int row) {
     const f32x4* xr = reinterpret_cast<const f32x4*>(x + static_cast<int64_t>(row) * hidden);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int c = threadIdx.x + i * kNormThreads;
-      if (c < nv) v[i] = xr[c];
+      if (FULL || c < nv) v[i] = xr[c];
     }
   };
   __shared__ float red[2][kNormThreads / 64];
+  // the grid never exceeds the rows, so every workgroup has a first row; past its last row a
+  // workgroup loads its current row again (cached, never used)
   int row = blockIdx.x;
-  if (row < rows) load_row(cur, row);
+  load_row(cur, row);
   for (int it = 0; row < rows; row += gridDim.x, ++it) {
     const int rn = row + gridDim.x;
-    if (rn < rows) load_row(nxt, rn);
+    load_row(nxt, rn < rows ? rn : row);
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int c = threadIdx.x + i * kNormThreads;
-      if (c < nv) ss += cur[i][0] * cur[i][0] + cur[i][1] * cur[i][1] + cur[i][2] * cur[i][2] + cur[i][3] * cur[i][3];
+      if (FULL || c < nv) ss += cur[i][0] * cur[i][0] + cur[i][1] * cur[i][1] + cur[i][2] * cur[i][2] + cur[i][3] * cur[i][3];
     }
     ss = wave_sum(ss);
     // two reduction slots by row parity: a slot is rewritten two rows later, after every thread
@@ -89,7 +93,7 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_stream_kernel(const floa
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int c = threadIdx.x + i * kNormThreads;
-      if (c < nv) {
+      if (FULL || c < nv) {
         const f32x4 o = {cur[i][0] * r * g[i][0], cur[i][1] * r * g[i][1], cur[i][2] * r * g[i][2],
                          cur[i][3] * r * g[i][3]};
         store4<Y_DT>(y, static_cast<int64_t>(row) * nv + c, o);
@@ -104,13 +108,16 @@ template <int W_DT, int Y_DT>
 static void rms_launch_k(const float* x, const void* w, void* y, int rows, int hidden, float eps,
                          hipStream_t s) {
   const int grid = rows < kNormGrid ? rows : kNormGrid;
-  if (hidden <= 4 * kNormThreads * 4) {
-    rmsnorm_stream_kernel<W_DT, Y_DT, 4><<<grid, kNormThreads, 0, s>>>(x, w, y, rows, hidden, eps);
-  } else if (hidden <= 4 * kNormThreads * 8) {
-    rmsnorm_stream_kernel<W_DT, Y_DT, 8><<<grid, kNormThreads, 0, s>>>(x, w, y, rows, hidden, eps);
-  } else {
-    rmsnorm_stream_kernel<W_DT, Y_DT, 16><<<grid, kNormThreads, 0, s>>>(x, w, y, rows, hidden, eps);
-  }
+  auto go = [&](auto nv) {
+    constexpr int NV = decltype(nv)::value;
+    if (hidden == 4 * kNormThreads * NV)
+      rmsnorm_stream_kernel<W_DT, Y_DT, NV, true><<<grid, kNormThreads, 0, s>>>(x, w, y, rows, hidden, eps);
+    else
+      rmsnorm_stream_kernel<W_DT, Y_DT, NV, false><<<grid, kNormThreads, 0, s>>>(x, w, y, rows, hidden, eps);
+  };
+  if (hidden <= 4 * kNormThreads * 4) go(std::integral_constant<int, 4>{});
+  else if (hidden <= 4 * kNormThreads * 8) go(std::integral_constant<int, 8>{});
+  else go(std::integral_constant<int, 16>{});
 }
 
 template <int W_DT>
