@@ -420,7 +420,7 @@ def main():
     x0 = to(x_host, "f32")
     pos = torch.from_numpy(pos_host).to(dev)
     rows_h, ds_h = synth.make_deepstack(cfg)
-    rows = None if rows_h is None else torch.from_numpy(rows_h).to(dev)
+    rows = rows_h  # host row list (checked by the library before any launch)
     ds = None if ds_h is None else to(ds_h, cfg.dtype)
     h = torch.empty_like(x0)
     ws = torch.empty(q3.layer_workspace_bytes(spec, S), dtype=torch.uint8, device=dev)

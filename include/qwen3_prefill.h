@@ -68,7 +68,7 @@ typedef enum {
  *               (16-bit operands); any divisor for f32.
  *   n_kv_heads  KV heads nkv (GQA: query head h reads KV head h / (nh / nkv), cortiq-engine
  *               qwen3te.rs, `attention_gemm`).
- *   head_dim    hd: 128 for 16-bit operands; 64 or 128 for f32.
+ *   head_dim    hd: 64 or 128 (16-bit operands and f32 alike).
  *   ffn         F, the SwiGLU width; multiple of 128.
  *   rms_eps     eps added to the mean of squares inside the square root (`rms_norm_into`).
  *   rope_theta  RoPE base: pair i < hd/2 turns at theta^(-2i/hd) per position (`norm_rope`).
@@ -83,9 +83,18 @@ typedef enum {
  *                            for |w| in [2^-17, 65504]);
  *                 QWEN3_BF16 bf16 operands (bf16 weights only);
  *                 QWEN3_F32  fp32 end to end (requires wdtype QWEN3_F32).
- *               fp16 and bf16 run at the same MFMA rate; fp16 keeps 3 more mantissa bits,
- *               which the 8B/32B-shaped layers need to stay within 2e-2 of an exact
- *               reference, but it holds magnitudes only up to 65504.
+ *               fp16 and bf16 run at the same MFMA rate; fp16 keeps 3 more mantissa bits
+ *               but holds magnitudes only up to 65504 (an activation beyond that, such as a
+ *               SwiGLU outlier of a real checkpoint, becomes infinite: such a model needs
+ *               QWEN3_BF16). Measured agreement of the layer output with an exact (float64)
+ *               reference, max |error| / RMS over the output, on synthetic N(0, 0.02)
+ *               weights:
+ *                 QWEN3_F16   2e-3 .. 5e-3 at every shape measured (2048-hidden layers at
+ *                             1024/2048 tokens, the 4096-hidden 4-layer stack at 4096
+ *                             tokens, the 5120-hidden layer at 8192 tokens);
+ *                 QWEN3_BF16  about 1.2e-2 on the 2048-hidden layers; 1.8e-2 .. 3.4e-2 on the
+ *                             4096- and 5120-hidden layers, i.e. ABOVE a 2e-2 bound there: the
+ *                             down projection sums 12k-26k products of bf16-rounded operands.
  *   resid_dtype dtype of the residual stream x_in/x_out; must be QWEN3_F32.
  */
 typedef struct {
@@ -114,7 +123,8 @@ typedef struct {
 
 /* Bytes of device workspace qwen3_layer_prefill needs for `seq_len` tokens (0 if cfg is
  * NULL or seq_len < 1). The workspace holds the normalized activations, q/k/v, the attention
- * output and the SwiGLU activation; its contents on entry do not matter. */
+ * output, the SwiGLU activation and the device copy of the DeepStack row list; its contents
+ * on entry do not matter. */
 size_t qwen3_layer_workspace_bytes(const qwen3_layer_cfg *cfg, int32_t seq_len);
 
 /* One decoder layer over all `seq_len` tokens (the recipe at the top of this file).
@@ -123,15 +133,18 @@ size_t qwen3_layer_workspace_bytes(const qwen3_layer_cfg *cfg, int32_t seq_len);
  *   positions     [3, S] int32: the t row, then the h row, then the w row. A text token has
  *                 t = h = w; an image token has one t per image and h, w on its merged grid
  *                 (inferencelayer vision.rs, `mrope_positions`). Values must be >= 0.
- *   ds_rows, n_ds DeepStack rows: n_ds >= 0 strictly increasing row indices < S, or NULL/0
- *                 (hf2q forward.rs, Phase D: the slab is added on image-token rows only).
- *   ds            [n_ds, H] of cfg.wdtype: ds[i] is added to output row ds_rows[i] after the
- *                 FFN residual; must be NULL when n_ds == 0 and non-NULL otherwise. The row
- *                 values are device data, read by the kernel: an entry outside [0, S) or not
- *                 greater than the entry before it is skipped (nothing is added for it).
+ *   ds_rows, n_ds DeepStack rows: a HOST array of n_ds >= 0 strictly increasing row indices in
+ *                 [0, S), or NULL/0 (hf2q forward.rs, Phase D: the slab is added on image-token
+ *                 rows only; `forward_text_prefill_logits_last` rejects an image-token position
+ *                 outside the sequence). The list is checked on the host and copied into the
+ *                 workspace on `stream` during the call; the caller may reuse it on return.
+ *   ds            device [n_ds, H] of cfg.wdtype: ds[i] is added to output row ds_rows[i]
+ *                 after the FFN residual; must be NULL when n_ds == 0 and non-NULL otherwise.
  *   workspace     at least qwen3_layer_workspace_bytes(cfg, S) bytes, 256-byte aligned.
- * Errors: seq_len < 1, NULL pointers, unsupported shapes, a bad DeepStack row list, or a
- * small workspace return a nonzero status before anything is enqueued. */
+ * Errors: seq_len < 1, NULL pointers, unsupported shapes, a DeepStack row outside [0, S) or
+ * not above its predecessor, a slab without rows (or rows without a slab), or a small
+ * workspace return QWEN3_ERR_INVALID_ARG / _UNSUPPORTED / _WORKSPACE before anything is
+ * enqueued. */
 int qwen3_layer_prefill(const qwen3_layer_cfg *cfg, const qwen3_layer_weights *w,
                         const void *x_in, void *x_out, int32_t seq_len,
                         const int32_t *positions, const int32_t *ds_rows, int32_t n_ds,
@@ -140,7 +153,8 @@ int qwen3_layer_prefill(const qwen3_layer_cfg *cfg, const qwen3_layer_weights *w
 
 /* Per-head RMSNorm then interleaved-MRoPE rotation of q and k, in place
  * (cortiq-engine qwen3te.rs, `norm_rope`).
- *   q [S, n_heads, head_dim], k [S, n_kv_heads, head_dim] of `dtype`, contiguous.
+ *   q [S, n_heads, head_dim], k [S, n_kv_heads, head_dim] of `dtype`, contiguous; n_heads and
+ *   n_kv_heads >= 1, and q, k, q_norm, k_norm all non-NULL.
  *   q_norm, k_norm [head_dim] of `norm_dtype`. Each (token, head) row x is replaced by
  *   r = x / sqrt(mean(x^2) + eps) * norm_w, then for i < hd/2 the pair (r_i, r_{i+hd/2}) is
  *   rotated by phi = positions[axis(i)][s] * theta^(-2i/hd) (axis rule under qwen3_layer_cfg).
@@ -263,9 +277,9 @@ size_t qwen3_model_workspace_bytes(const qwen3_model_cfg* cfg, int32_t seq_len);
  *   tokens     HOST array [seq_len] of ids in [0, vocab), checked on the host before anything is
  *              enqueued and copied into the workspace during the call.
  *   positions  device [3][seq_len] int32 (t, h, w rows), as for qwen3_layer_prefill.
- *   ds_rows, n_ds  device DeepStack rows shared by the first n_deepstack_layers layers (rules as
- *              for qwen3_layer_prefill); ds is a HOST array of n_deepstack_layers device slabs
- *              [n_ds, hidden] (layer.wdtype), or NULL when n_ds == 0.
+ *   ds_rows, n_ds  HOST DeepStack row list shared by the first n_deepstack_layers layers (rules
+ *              and errors as for qwen3_layer_prefill); ds is a HOST array of n_deepstack_layers
+ *              device slabs [n_ds, hidden] (layer.wdtype), or NULL when n_ds == 0.
  *   logits     device [vocab] fp32, written.
  * Every layer uses the same workspace region in turn; the residual stream stays in fp32. */
 int qwen3_model_prefill_logits_last(const qwen3_model_cfg* cfg, const qwen3_model_weights* w,

@@ -70,10 +70,11 @@ def _call_layer(lib, cfg, s=16, ws_bytes=None, n_ds=0, ds=None, ds_rows=None, we
 def test_workspace_size_formula(lib):
     c = _cfg(hidden=4096, n_heads=32, n_kv_heads=8, ffn=12288)
     s = 4096
+    # 16-bit xn | qkv | o | act, then the DeepStack row list (S int32)
     expect = 2 * s * (4096 + (4096 + 2048) + 4096 + 12288)
-    assert lib.qwen3_layer_workspace_bytes(ctypes.byref(c), s) == expect
+    assert lib.qwen3_layer_workspace_bytes(ctypes.byref(c), s) == expect + 4 * s
     c32 = _cfg(hidden=4096, n_heads=32, n_kv_heads=8, ffn=12288, wdtype=0, act_dtype=0)
-    assert lib.qwen3_layer_workspace_bytes(ctypes.byref(c32), s) == 2 * expect
+    assert lib.qwen3_layer_workspace_bytes(ctypes.byref(c32), s) == 2 * expect + 4 * s
     assert lib.qwen3_layer_workspace_bytes(ctypes.byref(c), 0) == 0
     assert lib.qwen3_layer_workspace_bytes(None, 16) == 0
 
@@ -105,13 +106,44 @@ def test_empty_sequence_rejected(lib):
     assert rc == 1 and "empty" in lib.qwen3_last_error().decode()
 
 
+def _rows(*r):
+    return (ctypes.c_int32 * len(r))(*r)
+
+
 def test_deepstack_argument_rules(lib):
+    """The DeepStack row list is a host array checked before anything is enqueued (hf2q
+    forward.rs, `forward_text_prefill_logits_last`: an image-token position outside the
+    sequence is an error, and a slab needs its rows)."""
     c = _cfg()
     assert _call_layer(lib, c, n_ds=0, ds=FAKE) == 1
     assert "n_ds == 0" in lib.qwen3_last_error().decode()
     assert _call_layer(lib, c, n_ds=4, ds=FAKE, ds_rows=None) == 1
-    assert _call_layer(lib, c, n_ds=17, ds=FAKE, ds_rows=FAKE) == 1
+    assert "ds_rows" in lib.qwen3_last_error().decode()
+    assert _call_layer(lib, c, n_ds=17, ds=FAKE, ds_rows=_rows(*range(17))) == 1
     assert _call_layer(lib, c, n_ds=-1) == 1
+    # S = 16: a row at or past S, a negative row, a repeat and a decrease are each rejected
+    for bad, needle in (((3, 16), "outside"), ((-1, 4), "outside"), ((3, 3), "strictly increasing"),
+                        ((5, 9, 7), "strictly increasing")):
+        assert _call_layer(lib, c, n_ds=len(bad), ds=FAKE, ds_rows=_rows(*bad)) == 1, bad
+        assert needle in lib.qwen3_last_error().decode(), bad
+    # rows given but no slab
+    assert _call_layer(lib, c, n_ds=2, ds=None, ds_rows=_rows(1, 2)) == 1
+    # a valid list passes these checks: the call then stops at the (too small) workspace
+    need = lib.qwen3_layer_workspace_bytes(ctypes.byref(c), 16)
+    assert _call_layer(lib, c, n_ds=3, ds=FAKE, ds_rows=_rows(0, 7, 15), ws_bytes=need - 1) == 3
+
+
+def test_qk_norm_mrope_rejects_empty_head_counts(lib):
+    """Both head counts must be >= 1: the kernel reads both norm weight vectors."""
+    sec = (ctypes.c_int32 * 3)(24, 20, 20)
+    for nh, nkv in ((0, 8), (32, 0), (0, 0)):
+        rc = lib.qk_norm_mrope(FAKE, FAKE, 4, nh, nkv, 128, FAKE, FAKE, 1e-6, FAKE, 5e6, sec,
+                               L.QWEN3_F16, L.QWEN3_BF16, None)
+        assert rc == 1 and "must be >= 1" in lib.qwen3_last_error().decode(), (nh, nkv)
+    # a NULL q or k is rejected as well
+    rc = lib.qk_norm_mrope(None, FAKE, 4, 32, 8, 128, FAKE, FAKE, 1e-6, FAKE, 5e6, sec,
+                           L.QWEN3_F16, L.QWEN3_BF16, None)
+    assert rc == 1 and "NULL" in lib.qwen3_last_error().decode()
 
 
 def test_null_weight_and_workspace_rejected(lib):
@@ -212,6 +244,11 @@ def test_model_argument_checks(lib):
     assert _call_model(lib, _model_cfg(vocab=0), [0]) == 1
     assert _call_model(lib, _model_cfg(n_layers=-1), [0]) == 1
     assert _call_model(lib, _model_cfg(n_ds_layers=1), [1, 2], n_ds=1, ds_rows=None) == 1
+    slab = (ctypes.c_void_p * 1)(0x2000)
+    assert _call_model(lib, _model_cfg(n_ds_layers=1), [1, 2], n_ds=1, ds_rows=_rows(2), slabs=slab) == 1
+    assert "outside" in lib.qwen3_last_error().decode()
+    assert _call_model(lib, _model_cfg(n_ds_layers=1), [1, 2, 3], n_ds=2, ds_rows=_rows(1, 1), slabs=slab) == 1
+    assert "strictly increasing" in lib.qwen3_last_error().decode()
     m2 = _model_cfg()
     need = lib.qwen3_model_workspace_bytes(ctypes.byref(m2), 3)
     assert _call_model(lib, m2, [1, 2, 3], ws_bytes=need - 1) == 3

@@ -113,7 +113,7 @@ def test_prefill_kv_writes_the_oracle_cache(name, s0):
     spec = q3.LayerSpec.of(cfg)
     dw = dev_weights(w, cfg.dtype)
     kc, vc = q3.kv_cache_alloc(spec, s0 + 9)
-    args = (dev_i32(rows), dev(slab, cfg.dtype)) if rows is not None else (None, None)
+    args = (rows, dev(slab, cfg.dtype)) if rows is not None else (None, None)
     y_kv = q3.layer_prefill_kv(spec, dw, dev(x), dev_i32(pos), kc, vc, *args)
     y = q3.layer_prefill(spec, dw, dev(x), dev_i32(pos), *args)
     torch.cuda.synchronize()

@@ -32,7 +32,7 @@ def _run(cfg, layers, emb, norm, head, tokens, pos, ds_rows, slabs, act=""):
     out = q3.model_prefill_logits_last(
         spec, [dev_weights(w, d) for w in layers], dev(emb, d), dev(norm, d),
         None if head is None else dev(head, d), tokens.tolist(), dev_i32(pos),
-        None if ds_rows is None else dev_i32(ds_rows),
+        ds_rows,
         None if slabs is None else [dev(s, d) for s in slabs])
     torch.cuda.synchronize()
     return out

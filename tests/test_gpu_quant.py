@@ -85,7 +85,7 @@ def test_layer_prefill_quant_matches_oracle(name, s, formats, act):
         rows, slab = rows[keep], slab[keep]
     spec = q3.LayerSpec.of(cfg, act)
     dn, dp = _dev_layer(cfg, norms, proj)
-    args = (dev_i32(rows), dev(slab, cfg.dtype)) if rows is not None else (None, None)
+    args = (rows, dev(slab, cfg.dtype)) if rows is not None else (None, None)
     got = host(q3.layer_prefill_quant(spec, dn, dp, dev(x), dev_i32(pos), *args))
     ref = oracle.layer_prefill(x, _oracle_weights(cfg, norms, proj), cfg, pos, rows, slab)
     err = rel_err(got, ref)

@@ -141,10 +141,10 @@ void attn_fwd_kernel(const AttnParams p) {
   u32x4 st[4];
   static_assert(KPT <= 4, "head_dim");
   // K / V rows come in through buffer loads when the operand's byte extent fits the 32-bit
-  // range (BUF): a per-thread byte offset within the tile plus the tile's row offset in a
-  // scalar register, rows at or past S reading as zeros through the range check (those keys
-  // are masked), so the loop carries no 64-bit address arithmetic. Otherwise through 64-bit
-  // addresses with the row index clamped to S - 1.
+  // range (BUF), with a per-lane 32-bit byte offset, so the loop carries no 64-bit address
+  // arithmetic; otherwise through 64-bit addresses. Either way a row index at or past S is
+  // clamped to S - 1: such keys are masked (probability 0) and their values are finite data
+  // of the sequence, so nothing past the last row is read and no 0 * Inf/NaN can reach O.
   const int64_t row_elems = k_loader ? p.k_stride : p.v_stride;
   const uint16_t* gbase = (k_loader ? p.k : p.v) + g * HD;
   int trow[4], tcol[4];  // row within the tile and element column of this thread's chunks
@@ -158,16 +158,13 @@ void attn_fwd_kernel(const AttnParams p) {
   const int row_bytes = static_cast<int>(2 * row_elems);  // used only when BUF
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(gbase), static_cast<short>(0), p.S * row_bytes, 0x00020000);
-  int voff[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) voff[i] = trow[i] * row_bytes + 2 * tcol[i];
   auto gload = [&](int tile) {
     if constexpr (BUF) {
-      const int soff = tile * kKT * row_bytes;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if (i < nst) {
-          const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff[i], soff, 0);
+          const int row = min(tile * kKT + trow[i], p.S - 1);
+          const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, row * row_bytes + 2 * tcol[i], 0, 0);
           st[i] = u32x4{v[0], v[1], v[2], v[3]};
         }
       }
@@ -351,11 +348,10 @@ template <int G, int OP, int HD>
 static hipError_t launch_g(const AttnParams& p, hipStream_t s) {
   constexpr int TOK = 32 * kAttnWaves / G;
   const int nblk = (p.S + TOK - 1) / TOK;
-  // Buffer loads address K and V with 32-bit byte offsets from the head's column; the extent
-  // covers the rows a last partial tile reaches past S. Q3_ATTN_ADDR64 (environment) forces
-  // the 64-bit address path, so that it can be tested at small sizes.
-  const int64_t extent =
-      2 * (static_cast<int64_t>(p.S) + kKT) * (p.k_stride > p.v_stride ? p.k_stride : p.v_stride);
+  // Buffer loads address K and V with 32-bit byte offsets from the head's column (rows
+  // clamped to S - 1). Q3_ATTN_ADDR64 (environment) forces the 64-bit address path, so that it
+  // can be tested at small sizes.
+  const int64_t extent = 2 * static_cast<int64_t>(p.S) * (p.k_stride > p.v_stride ? p.k_stride : p.v_stride);
   if (extent <= 0x7fffffff && std::getenv("Q3_ATTN_ADDR64") == nullptr)
     attn_fwd_kernel<G, OP, true, HD><<<nblk * p.nkv, kAttnThreads, 0, s>>>(p);
   else

@@ -131,6 +131,22 @@ int check_sections(const int32_t sec[3], int32_t hd) {
   return QWEN3_OK;
 }
 
+// DeepStack rows: a HOST array of n_ds strictly increasing row indices in [0, S) (hf2q
+// forward.rs, `forward_text_prefill_logits_last`: an image-token position outside the sequence
+// is an error; a slab needs its rows).
+int check_ds_rows(const int32_t* rows, int32_t n_ds, int32_t S) {
+  if (n_ds < 0 || n_ds > S) return fail(QWEN3_ERR_INVALID_ARG, "n_ds (%d) must be in [0, seq_len = %d]", n_ds, S);
+  if (n_ds > 0 && !rows) return fail(QWEN3_ERR_INVALID_ARG, "n_ds = %d needs the host row list ds_rows", n_ds);
+  for (int32_t i = 0; i < n_ds; ++i) {
+    if (rows[i] < 0 || rows[i] >= S)
+      return fail(QWEN3_ERR_INVALID_ARG, "DeepStack row %d (entry %d) is outside [0, seq_len = %d)", rows[i], i, S);
+    if (i > 0 && rows[i] <= rows[i - 1])
+      return fail(QWEN3_ERR_INVALID_ARG, "DeepStack rows must be strictly increasing (entry %d: %d after %d)", i,
+                  rows[i], rows[i - 1]);
+  }
+  return QWEN3_OK;
+}
+
 int check_cfg(const qwen3_layer_cfg* c) {
   if (!c) return fail(QWEN3_ERR_INVALID_ARG, "cfg is NULL");
   int st = check_formats(c->wdtype, c->act_dtype);
@@ -155,7 +171,7 @@ int check_cfg(const qwen3_layer_cfg* c) {
 }
 
 struct Workspace {
-  size_t xn, qkv, o, act, total;
+  size_t xn, qkv, o, act, dsrows, total;
 };
 
 Workspace layout(const qwen3_layer_cfg* c, int32_t S) {
@@ -167,7 +183,8 @@ Workspace layout(const qwen3_layer_cfg* c, int32_t S) {
   w.qkv = w.xn + align256(static_cast<size_t>(S) * c->hidden * e);
   w.o = w.qkv + align256(static_cast<size_t>(S) * (q_dim + 2 * kv_dim) * e);
   w.act = w.o + align256(static_cast<size_t>(S) * q_dim * e);
-  w.total = w.act + align256(static_cast<size_t>(S) * c->ffn * e);
+  w.dsrows = w.act + align256(static_cast<size_t>(S) * c->ffn * e);
+  w.total = w.dsrows + align256(static_cast<size_t>(S) * 4);
   return w;
 }
 
@@ -376,11 +393,9 @@ static int layer_prefill_impl(const qwen3_layer_cfg* cfg, const LayerW& w, const
   if (!positions) return fail(QWEN3_ERR_INVALID_ARG, "positions is NULL");
   if (misaligned16({x_in, x_out, ds}))
     return fail(QWEN3_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
-  if (n_ds < 0 || n_ds > seq_len)
-    return fail(QWEN3_ERR_INVALID_ARG, "n_ds (%d) must be in [0, seq_len = %d]", n_ds, seq_len);
+  if ((st = check_ds_rows(ds_rows, n_ds, seq_len))) return st;
   if (n_ds == 0 && ds) return fail(QWEN3_ERR_INVALID_ARG, "a DeepStack slab was given with n_ds == 0");
-  if (n_ds > 0 && (!ds || !ds_rows))
-    return fail(QWEN3_ERR_INVALID_ARG, "n_ds = %d needs both ds_rows and ds", n_ds);
+  if (n_ds > 0 && !ds) return fail(QWEN3_ERR_INVALID_ARG, "n_ds = %d needs the slab ds", n_ds);
   const Workspace L = layout(cfg, seq_len);
   const size_t need = L.total + (quant ? dequant_bytes(cfg) : 0);
   if (!workspace || workspace_bytes < need)
@@ -473,10 +488,13 @@ static int layer_prefill_impl(const qwen3_layer_cfg* cfg, const LayerW& w, const
     Proj dn{act, F, B[0], nullptr, nullptr, H, H, F, y, H, y, H, S, H, F};
     if ((st = run_gemm("gemm_down_resid", dn, q3::EPI_STORE_F32, bdt, dt, s))) return st;
   }
-  // a10: DeepStack rows
+  // a10: DeepStack rows (the validated host row list goes to the workspace on the stream)
   if (n_ds > 0) {
+    int32_t* drows = reinterpret_cast<int32_t*>(ws + L.dsrows);
+    hipError_t he = hipMemcpyAsync(drows, ds_rows, static_cast<size_t>(n_ds) * 4, hipMemcpyHostToDevice, s);
+    if (he != hipSuccess) return hip_fail(he, "DeepStack row upload");
     KTimer t("deepstack_add", s);
-    hipError_t he = q3::launch_deepstack_add(y, ds_rows, ds, wdt, n_ds, S, H, s);
+    he = q3::launch_deepstack_add(y, drows, ds, wdt, n_ds, S, H, s);
     if (he != hipSuccess) return hip_fail(he, "deepstack_add launch");
   }
   return QWEN3_OK;
@@ -621,10 +639,9 @@ static int model_prefill_impl(const qwen3_model_cfg* cfg, const qwen3_model_weig
   if (misaligned16({w->token_embd, w->output_norm, w->lm_head, logits}))
     return fail(QWEN3_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
   const int nds = cfg->n_deepstack_layers;
-  if (n_ds < 0 || n_ds > seq_len)
-    return fail(QWEN3_ERR_INVALID_ARG, "n_ds (%d) must be in [0, seq_len = %d]", n_ds, seq_len);
+  if ((st = check_ds_rows(ds_rows, n_ds, seq_len))) return st;
   if (n_ds > 0 && nds > 0) {
-    if (!ds_rows || !ds) return fail(QWEN3_ERR_INVALID_ARG, "n_ds = %d needs ds_rows and the slab array", n_ds);
+    if (!ds) return fail(QWEN3_ERR_INVALID_ARG, "n_ds = %d needs the slab array", n_ds);
     for (int l = 0; l < nds; ++l)
       if (!ds[l]) return fail(QWEN3_ERR_INVALID_ARG, "DeepStack slab %d is NULL", l);
   }
@@ -769,13 +786,13 @@ int qk_norm_mrope(void* q, void* k, int32_t seq_len, int32_t n_heads, int32_t n_
   if (!valid_dtype(dtype) || !valid_dtype(norm_dtype))
     return fail(QWEN3_ERR_INVALID_ARG, "dtype (%d, %d) is not a qwen3_dtype", dtype, norm_dtype);
   if (seq_len < 1) return fail(QWEN3_ERR_INVALID_ARG, "seq_len must be >= 1 (got %d)", seq_len);
-  if (n_heads < 0 || n_kv_heads < 0) return fail(QWEN3_ERR_INVALID_ARG, "head counts must be >= 0");
+  if (n_heads < 1 || n_kv_heads < 1)
+    return fail(QWEN3_ERR_INVALID_ARG, "n_heads (%d) and n_kv_heads (%d) must be >= 1", n_heads, n_kv_heads);
   if (head_dim != 64 && head_dim != 128)
     return fail(QWEN3_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", head_dim);
   int st = check_sections(mrope_section, head_dim);
   if (st) return st;
-  if ((n_heads > 0 && (!q || !q_norm)) || (n_kv_heads > 0 && (!k || !k_norm)) || !positions)
-    return fail(QWEN3_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (!q || !q_norm || !k || !k_norm || !positions) return fail(QWEN3_ERR_INVALID_ARG, "NULL tensor pointer");
   if (misaligned16({q, k, q_norm, k_norm}))
     return fail(QWEN3_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
   if (!(eps >= 0.f) || !(theta > 1.f)) return fail(QWEN3_ERR_INVALID_ARG, "eps must be >= 0 and theta > 1");

@@ -17,8 +17,8 @@ hipError_t launch_rmsnorm(const float* x, const void* w, int w_dt, void* y, int 
                           int hidden, float eps, hipStream_t s);
 
 // ---- DeepStack rows add -------------------------------------------------------------------
-// y[rows[i], :] += ds[i, :] for i < n; entries outside [0, S) or not above their predecessor
-// are skipped. y f32 [S, H]; ds [n, H] of ds_dt.
+// y[rows[i], :] += ds[i, :] for i < n; rows is a device copy of a host-checked list (strictly
+// increasing, inside [0, S)). y f32 [S, H]; ds [n, H] of ds_dt.
 hipError_t launch_deepstack_add(float* y, const int32_t* rows, const void* ds, int ds_dt, int n,
                                 int S, int hidden, hipStream_t s);
 

@@ -85,6 +85,22 @@ def _cfg(spec):
     return c
 
 
+def _host_rows(ds_rows):
+    """DeepStack rows as a host int32 array for the C ABI: (ctypes array or None, count).
+    Accepts a sequence of ints, a numpy array or a CPU tensor; a GPU tensor is refused (the
+    library checks the list on the host before it enqueues anything)."""
+    if ds_rows is None:
+        return None, 0
+    if isinstance(ds_rows, torch.Tensor):
+        if ds_rows.device.type != "cpu":
+            raise TypeError("ds_rows must be host data (a sequence, numpy array or CPU tensor)")
+        ds_rows = ds_rows.tolist()
+    vals = [int(r) for r in (ds_rows.tolist() if hasattr(ds_rows, "tolist") else ds_rows)]
+    if not vals:
+        return None, 0
+    return (ctypes.c_int32 * len(vals))(*vals), len(vals)
+
+
 def layer_workspace_bytes(spec, seq_len):
     return int(_lib.load().qwen3_layer_workspace_bytes(ctypes.byref(_cfg(spec)), int(seq_len)))
 
@@ -93,7 +109,8 @@ def layer_prefill(spec, weights, x, positions, ds_rows=None, ds=None, out=None, 
     """qwen3_layer_prefill: one decoder layer over x [S, H] float32; returns out [S, H] float32.
 
     weights: mapping of the eleven weight names to tensors of spec's dtype; positions [3, S]
-    int32; ds_rows [n] int32 and ds [n, H] (spec's dtype) for DeepStack, or None.
+    int32; ds_rows: n host row indices (strictly increasing, < S) and ds [n, H] (spec's dtype)
+    on the GPU for DeepStack, or None.
     out may be x (in place). workspace: a uint8 tensor of layer_workspace_bytes() or None.
     """
     lib = _lib.load()
@@ -105,10 +122,10 @@ def layer_prefill(spec, weights, x, positions, ds_rows=None, ds=None, out=None, 
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     w = _lib.LayerWeights(*[_ptr(weights[n]) for n in WEIGHT_NAMES])
-    n_ds = 0 if ds_rows is None else int(ds_rows.numel())
+    rows, n_ds = _host_rows(ds_rows)
     _lib.check(lib.qwen3_layer_prefill(
         ctypes.byref(cfg), ctypes.byref(w), _ptr(x), _ptr(out), int(s), _ptr(positions),
-        _ptr(ds_rows), n_ds, _ptr(ds), _ptr(workspace), int(workspace.numel()), _stream()))
+        rows, n_ds, _ptr(ds), _ptr(workspace), int(workspace.numel()), _stream()))
     return out
 
 
@@ -147,10 +164,10 @@ def layer_prefill_kv(spec, weights, x, positions, k_cache, v_cache, ds_rows=None
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     w = _lib.LayerWeights(*[_ptr(weights[n]) for n in WEIGHT_NAMES])
-    n_ds = 0 if ds_rows is None else int(ds_rows.numel())
+    rows, n_ds = _host_rows(ds_rows)
     _lib.check(lib.qwen3_layer_prefill_kv(
         ctypes.byref(cfg), ctypes.byref(w), _ptr(x), _ptr(out), int(s), _ptr(positions),
-        _ptr(ds_rows), n_ds, _ptr(ds), _ptr(k_cache), _ptr(v_cache), int(k_cache.shape[1]),
+        rows, n_ds, _ptr(ds), _ptr(k_cache), _ptr(v_cache), int(k_cache.shape[1]),
         _ptr(workspace), int(workspace.numel()), _stream()))
     return out
 
@@ -248,10 +265,10 @@ def layer_prefill_quant(spec, norms, proj, x, positions, ds_rows=None, ds=None, 
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     w = _qweights(norms, proj)
-    n_ds = 0 if ds_rows is None else int(ds_rows.numel())
+    rows, n_ds = _host_rows(ds_rows)
     cap = 0 if k_cache is None else int(k_cache.shape[1])
     _lib.check(lib.qwen3_layer_prefill_quant(
-        ctypes.byref(cfg), ctypes.byref(w), _ptr(x), _ptr(out), int(s), _ptr(positions), _ptr(ds_rows), n_ds,
+        ctypes.byref(cfg), ctypes.byref(w), _ptr(x), _ptr(out), int(s), _ptr(positions), rows, n_ds,
         _ptr(ds), _ptr(k_cache), _ptr(v_cache), cap, _ptr(workspace), int(workspace.numel()), _stream()))
     return out
 
@@ -336,8 +353,8 @@ def model_prefill_logits_last(spec, layers, token_embd, output_norm, lm_head, to
 
     layers: list of weight mappings (one per decoder layer); token_embd [vocab, H],
     output_norm [H], lm_head [vocab, H] or None (tied) on the GPU in spec's dtype; tokens: a
-    host sequence of int token ids; positions [3, S] int32 on the GPU; ds_rows [n] int32 and ds
-    a list of [n, H] slabs (one per DeepStack layer, the first len(ds) layers) or None.
+    host sequence of int token ids; positions [3, S] int32 on the GPU; ds_rows n host row indices
+    (strictly increasing, < S) and ds a list of [n, H] slabs (one per DeepStack layer, the first len(ds) layers) or None.
     caches: None, or [(k, v)] per layer (kv_cache_alloc) to be filled with every layer's k', v
     (qwen3_model_prefill_logits_last_kv).
     """
@@ -361,15 +378,15 @@ def model_prefill_logits_last(spec, layers, token_embd, output_norm, lm_head, to
         slabs = (ctypes.c_void_p * len(ds))(*[t.data_ptr() if t is not None else None for t in ds])
         for t in ds:
             _ptr(t)  # device and contiguity checks
-    n_ds = 0 if ds_rows is None else int(ds_rows.numel())
+    rows, n_ds = _host_rows(ds_rows)
     if caches is None:
         _lib.check(lib.qwen3_model_prefill_logits_last(
-            ctypes.byref(m), ctypes.byref(mw), tok, int(s), _ptr(positions), _ptr(ds_rows), n_ds, slabs,
+            ctypes.byref(m), ctypes.byref(mw), tok, int(s), _ptr(positions), rows, n_ds, slabs,
             _ptr(out), _ptr(workspace), int(workspace.numel()), _stream()))
     else:
         kc, vc = _cache_arrays(caches)
         _lib.check(lib.qwen3_model_prefill_logits_last_kv(
-            ctypes.byref(m), ctypes.byref(mw), tok, int(s), _ptr(positions), _ptr(ds_rows), n_ds, slabs, kc, vc,
+            ctypes.byref(m), ctypes.byref(mw), tok, int(s), _ptr(positions), rows, n_ds, slabs, kc, vc,
             int(caches[0][0].shape[1]) if caches else 0, _ptr(out), _ptr(workspace), int(workspace.numel()),
             _stream()))
     return out
