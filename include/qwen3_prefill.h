@@ -340,6 +340,19 @@ int gqa_decode_attention(const float *q, const void *k_cache, const void *v_cach
 /* Workspace for gqa_decode_attention; also enough for every smaller len. 0 for invalid input. */
 size_t gqa_decode_attention_workspace_bytes(int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, int32_t len);
 
+/* gqa_decode_attention for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same checks, kernels and
+ * results, with the per-split partial results in a fixed array of the library's device code
+ * (QWEN3_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends) instead of a workspace.
+ * Calls whose gqa_decode_attention_workspace_bytes() exceeds that size return
+ * QWEN3_ERR_UNSUPPORTED (the 8B shape, 32 query / 8 KV heads of 128, needs 1 MiB at any length).
+ * Every call on one GPU uses that GPU's one array: calls that overlap on one GPU (several host
+ * threads, or several streams) race and must be ordered by the caller. Allocates nothing. */
+#define QWEN3_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+int gqa_decode_attention_noalloc(const float *q, const void *k_cache, const void *v_cache, int32_t capacity,
+                                 int32_t len, int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, float scale,
+                                 qwen3_dtype cache_dtype, float *out, void *stream);
+
 /* One new token through the layer, reading positions 0 .. len-1 from the caches and appending
  * its own k' and v at row len:
  *   xn = RMSNorm(x); q, k, v = xn W^T; per-head RMSNorm + interleaved MRoPE at `position`;

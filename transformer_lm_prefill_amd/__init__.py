@@ -16,6 +16,7 @@ from .ops import (  # noqa: F401
     gqa_bidirectional_attention,
     gqa_causal_attention,
     gqa_decode_attention,
+    gqa_decode_attention_noalloc,
     kv_cache_alloc,
     kv_cache_write,
     layer_decode,

@@ -17,7 +17,7 @@ EXPORTS = ("qwen3_layer_workspace_bytes", "qwen3_layer_prefill", "qk_norm_mrope"
            "apply_rope_tables", "swiglu_ffn", "swiglu_ffn_workspace_bytes", "rms_norm_rows",
            "qwen3_model_workspace_bytes", "qwen3_model_prefill_logits_last",
            "kv_cache_write", "qwen3_layer_prefill_kv", "gqa_decode_attention",
-           "gqa_decode_attention_workspace_bytes", "qwen3_layer_decode",
+           "gqa_decode_attention_workspace_bytes", "gqa_decode_attention_noalloc", "qwen3_layer_decode",
            "qwen3_layer_decode_workspace_bytes", "dequantize_matrix",
            "qwen3_layer_quant_workspace_bytes", "qwen3_layer_prefill_quant", "qwen3_layer_decode_quant",
            "qwen3_model_prefill_logits_last_kv", "qwen3_model_decode_workspace_bytes", "qwen3_model_decode_logits",
@@ -124,6 +124,8 @@ def load():
     lib.gqa_decode_attention.restype = ctypes.c_int
     lib.gqa_decode_attention_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.gqa_decode_attention_workspace_bytes.restype = sz
+    lib.gqa_decode_attention_noalloc.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, f32, ctypes.c_int, vp, vp]
+    lib.gqa_decode_attention_noalloc.restype = ctypes.c_int
     lib.qwen3_layer_decode.argtypes = [ctypes.POINTER(LayerCfg), ctypes.POINTER(LayerWeights),
                                        vp, vp, vp, vp, vp, i32, i32, vp, sz, vp]
     lib.qwen3_layer_decode.restype = ctypes.c_int

@@ -362,6 +362,11 @@ int group_weights(const MatW* const* m, int n, const int* rows, int cols, qwen3_
 
 }  // namespace
 
+namespace q3 {
+// Sets the thread's error text (for entry points defined in other sources); returns status.
+int set_error(int status, const char* msg) { return fail(status, "%s", msg); }
+}  // namespace q3
+
 extern "C" {
 
 const char* qwen3_last_error(void) { return g_err.c_str(); }

@@ -196,6 +196,22 @@ def gqa_decode_attention(q, k_cache, v_cache, length, scale=None, out=None, work
     return out
 
 
+def gqa_decode_attention_noalloc(q, k_cache, v_cache, length, scale=None, out=None):
+    """gqa_decode_attention_noalloc: gqa_decode_attention with the library's fixed per-GPU
+    scratch array in place of a workspace (nothing is allocated except `out` when None)."""
+    lib = _lib.load()
+    nh, hd = q.shape
+    nkv, cap = k_cache.shape[0], k_cache.shape[1]
+    if scale is None:
+        scale = hd ** -0.5
+    if out is None:
+        out = torch.empty_like(q)
+    _lib.check(lib.gqa_decode_attention_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), int(cap), int(length),
+                                                int(nh), int(nkv), int(hd), float(scale), _dt(k_cache), _ptr(out),
+                                                _stream()))
+    return out
+
+
 def layer_decode_workspace_bytes(spec, capacity):
     return int(_lib.load().qwen3_layer_decode_workspace_bytes(ctypes.byref(_cfg(spec)), int(capacity)))
 
