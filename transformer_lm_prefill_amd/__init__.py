@@ -27,6 +27,7 @@ from .ops import (  # noqa: F401
     layer_prefill_quant,
     layer_quant_workspace_bytes,
     layer_workspace_bytes,
+    mfma_probe,
     model_decode_logits,
     model_decode_workspace_bytes,
     model_prefill_logits_last,

@@ -21,7 +21,7 @@ EXPORTS = ("qwen3_layer_workspace_bytes", "qwen3_layer_prefill", "qk_norm_mrope"
            "qwen3_layer_decode_workspace_bytes", "dequantize_matrix",
            "qwen3_layer_quant_workspace_bytes", "qwen3_layer_prefill_quant", "qwen3_layer_decode_quant",
            "qwen3_model_prefill_logits_last_kv", "qwen3_model_decode_workspace_bytes", "qwen3_model_decode_logits",
-           "qwen3_last_error", "qwen3_timing_enable", "qwen3_timing_collect")
+           "qwen3_last_error", "qwen3_timing_enable", "qwen3_timing_collect", "qwen3_mfma_probe")
 
 
 class LayerCfg(ctypes.Structure):
@@ -126,6 +126,8 @@ def load():
     lib.gqa_decode_attention_workspace_bytes.restype = sz
     lib.gqa_decode_attention_noalloc.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, f32, ctypes.c_int, vp, vp]
     lib.gqa_decode_attention_noalloc.restype = ctypes.c_int
+    lib.qwen3_mfma_probe.argtypes = [i32, i32, vp, vp, vp]
+    lib.qwen3_mfma_probe.restype = ctypes.c_int
     lib.qwen3_layer_decode.argtypes = [ctypes.POINTER(LayerCfg), ctypes.POINTER(LayerWeights),
                                        vp, vp, vp, vp, vp, i32, i32, vp, sz, vp]
     lib.qwen3_layer_decode.restype = ctypes.c_int

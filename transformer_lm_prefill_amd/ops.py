@@ -516,3 +516,21 @@ def timing_collect(max_entries=64):
     n = ctypes.c_int32(0)
     _lib.check(lib.qwen3_timing_collect(arr, max_entries, ctypes.byref(n)))
     return {arr[i].name.decode(): (arr[i].launches, arr[i].total_ms) for i in range(n.value)}
+
+
+def mfma_probe(workgroups, iters):
+    """qwen3_mfma_probe on the current stream: returns (milliseconds, FLOP, shader clock in GHz)
+    of one launch, timed with events around it."""
+    lib = _lib.load()
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    clocks = torch.zeros(2, dtype=torch.int64, device="cuda")
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    _lib.check(lib.qwen3_mfma_probe(int(workgroups), int(iters), _ptr(sink), _ptr(clocks), _stream()))
+    e1.record(s)
+    torch.cuda.synchronize()
+    cyc, ticks = (int(v) for v in clocks.cpu().tolist())
+    ghz = cyc / (ticks / 100e6) / 1e9 if ticks > 0 else float("nan")
+    flop = float(workgroups) * 4 * iters * 8 * 32768.0
+    return e0.elapsed_time(e1), flop, ghz
