@@ -345,7 +345,8 @@ def quant_extra(cfg, x0, pos, n_tokens=16):
     q3.timing_enable(False)
     res = {"workload": f"{cfg.name} layer 1 with Q4_0 projections (18 bytes per 32 weights), seq {S}",
            "prefill": {"ms": round(ms_pre, 4), "tokens_per_s": round(S / (ms_pre * 1e-3), 1),
-                       "dequant_ms": round(kt["dequant"][1], 4),
+                       "dequant_ms": round(kt["dequant"][1], 4) if "dequant" in kt else 0.0,
+                       "q4_0_decoded_in_products": "dequant" not in kt,
                        "kernels_ms": {k: round(v[1], 4) for k, v in kt.items()}}}
     del ws
     dws = torch.empty(q3.layer_decode_workspace_bytes(spec, cap), dtype=torch.uint8, device=dev)

@@ -408,11 +408,14 @@ int qwen3_model_decode_logits(const qwen3_model_cfg* cfg, const qwen3_model_weig
  * cortiq-engine 0.8.21, qwen3te.rs, `q8_exact_matmat`: int8 rows with a per-row scale, weight[o, j]
  * = row_scale[o] * q[o, j], activations not quantized.
  *
- * Projections with quantized weights compute x W^T with the dequantized W. In a prefill each
- * quantized matrix is expanded to the operand type (f16 or bf16, one rounding per weight: d *
- * (code - 8) and row_scale * q are rounded to nearest even) in the workspace just before its
- * product; a decode step reads the quantized bytes directly (Q4_0: the activations are rounded to
- * binary16 for v_dot2 products with fp32 sums; int8 rows: fp32 activations).
+ * Projections with quantized weights compute x W^T with the dequantized W, each weight rounded
+ * once to the operand type (f16 or bf16, round to nearest even: d * (code - 8) and
+ * row_scale * q). In a prefill, a product group whose matrices are all Q4_0 (q|k|v, o, gate|up,
+ * down) reads the blocks inside the MFMA product, decoding them in its weight-tile path, with
+ * the same bits as the product over expanded weights; other quantized groups (int8 rows, or
+ * Q4_0 mixed with int8 rows) are expanded into the workspace just before their product. A decode
+ * step reads the quantized bytes directly (Q4_0: the activations are rounded to binary16 for
+ * v_dot2 products with fp32 sums; int8 rows: fp32 activations).
  * Norm weights stay in cfg.wdtype; dense projections use cfg.wdtype as in qwen3_layer_weights.
  */
 typedef enum { QWEN3_W_DENSE = 0, QWEN3_W_Q4_0 = 1, QWEN3_W_Q8_ROW = 2 } qwen3_wformat;

@@ -153,3 +153,35 @@ def test_quant_8b_prefill_4096_then_decode():
     log_err("layer_decode_quant[8b,S0=4096,q4_0]", err_d)
     print(f"8B Q4_0: prefill rows {err:.3e}, decode {err_d:.3e}")
     assert err <= TOL[cfg.dtype] and err_d <= TOL[cfg.dtype]
+
+
+@pytest.mark.parametrize("act,s", [("f16", 300), ("bf16", 300), ("f16", 1030)])
+def test_q4_0_decoded_in_product_equals_expanded_product(act, s):
+    """A layer whose projections are all Q4_0 decodes the blocks inside the matrix products'
+    weight-tile path. Each weight is the same one rounding of d * (code - 8) that the expansion
+    kernel stores, placed in the same tile layout, so the layer's output equals, bit for bit,
+    the dense layer run on the expanded matrices."""
+    cfg = synth.get_config("qwen3vl_2b_text").with_seq(s)
+    formats = {n: "q4_0" for n in synth.PROJ_NAMES}
+    norms, proj = synth.make_quant_layer_weights(cfg, 0, formats)
+    x, pos = synth.make_x(cfg), synth.make_positions(cfg)
+    spec = q3.LayerSpec.of(cfg, act)
+    dn, dp = _dev_layer(cfg, norms, proj)
+    yq = q3.layer_prefill_quant(spec, dn, dp, dev(x), dev_i32(pos))
+    dense = {n: q3.dequantize_matrix("q4_0", dp[n][1], d.shape[0], d.shape[1] * 32, out_dtype=TDT[act])
+             for n, (_, d, _) in proj.items()}
+    dense.update({n: t.to(TDT[act]) for n, t in dn.items()})
+    spec_d = q3.LayerSpec(**{**spec.__dict__, "dtype": act})
+    yd = q3.layer_prefill(spec_d, dense, dev(x), dev_i32(pos))
+    torch.cuda.synchronize()
+    assert torch.equal(yq, yd)
+    # against the oracle on the weights the products multiply (each rounded once to `act`)
+    w_used = dict(norms)
+    w_used.update({n: host(t) for n, t in dense.items() if n in proj})
+    err = rel_err(host(yq), oracle.layer_prefill(x, w_used, cfg, pos))
+    log_err(f"layer_q4_0_in_product[{act},S{s}]", err)
+    # fp16 operands: the layer bound. bf16 operands carry 8-bit significands through every
+    # product and sit at that bound on these weights (2.0e-2 measured); their pin here is the
+    # equality with the expanded product above, whose own numerics the other tests bound.
+    if act == "f16":
+        assert err <= TOL["bf16"]

@@ -230,15 +230,20 @@ struct Proj {
   int M, N, K;
 };
 
-// wd: weight dtype; ad: operand dtype (A, MFMA, 16-bit outputs).
-int run_gemm(const char* name, const Proj& g, int epi, qwen3_dtype wd, qwen3_dtype ad, hipStream_t s) {
+// wd: weight dtype; ad: operand dtype (A, MFMA, 16-bit outputs); q4: the B matrices are Q4_0
+// blocks decoded inside the product.
+int run_gemm(const char* name, const Proj& g, int epi, qwen3_dtype wd, qwen3_dtype ad, hipStream_t s,
+             bool q4 = false) {
   KTimer t(name, s);
   hipError_t e;
   if (ad != QWEN3_F32) {
     q3::GemmParams p{static_cast<const uint16_t*>(g.A), g.lda, static_cast<const uint16_t*>(g.B0),
                      static_cast<const uint16_t*>(g.B1), static_cast<const uint16_t*>(g.B2),
                      g.nseg0, g.nseg1, g.ldb, g.C, g.ldc, g.R, g.ldr, g.M, g.N, g.K};
-    e = q3::launch_gemm_mfma(p, epi, ad == QWEN3_F16 ? q3::OPH_F16 : q3::OPH_BF16, wd == QWEN3_BF16, 0, s);
+    if (q4)
+      e = q3::launch_gemm_mfma_q4(p, epi, ad == QWEN3_F16 ? q3::OPH_F16 : q3::OPH_BF16, 0, s);
+    else
+      e = q3::launch_gemm_mfma(p, epi, ad == QWEN3_F16 ? q3::OPH_F16 : q3::OPH_BF16, wd == QWEN3_BF16, 0, s);
   } else {
     // f32 SwiGLU: N counts F outputs (the dual kernel multiplies gate and up together)
     q3::GemmF32Params p{static_cast<const float*>(g.A), g.lda, static_cast<const float*>(g.B0),
@@ -340,12 +345,23 @@ size_t dequant_bytes(const qwen3_layer_cfg* c) {
 }
 
 // The matrices of one product group in one storage type: all dense -> as given (wdt); all
+// Q4_0, with the product's A operand (a_elems 16-bit elements) within the 32-bit offsets of the
+// GEMM's buffer loads -> the blocks as given, decoded inside the GEMM (*q4 set); otherwise
 // quantized -> expanded back to back into dq in the operand type.
 int group_weights(const MatW* const* m, int n, const int* rows, int cols, qwen3_dtype wdt, qwen3_dtype act,
-                  char* dq, const void** out, qwen3_dtype* bdt, hipStream_t s) {
+                  char* dq, const void** out, qwen3_dtype* bdt, bool* q4, int64_t a_elems, hipStream_t s) {
+  *q4 = false;
   if (m[0]->fmt == QWEN3_W_DENSE) {
     for (int i = 0; i < n; ++i) out[i] = m[i]->data;
     *bdt = wdt;
+    return QWEN3_OK;
+  }
+  bool all_q4 = 2 * a_elems <= 0x7fffffff;
+  for (int i = 0; i < n; ++i) all_q4 = all_q4 && m[i]->fmt == QWEN3_W_Q4_0;
+  if (all_q4) {
+    for (int i = 0; i < n; ++i) out[i] = m[i]->data;
+    *bdt = act;
+    *q4 = true;
     return QWEN3_OK;
   }
   KTimer t("dequant", s);
@@ -432,6 +448,7 @@ static int layer_prefill_impl(const qwen3_layer_cfg* cfg, const LayerW& w, const
   float* y = static_cast<float*>(x_out);
   const void* B[3];
   qwen3_dtype bdt;
+  bool q4 = false;
 
   // a1: input RMSNorm
   if ((st = run_rmsnorm(x, w.attn_norm, wdt, xn, dt, S, H, cfg->rms_eps, s))) return st;
@@ -439,9 +456,9 @@ static int layer_prefill_impl(const qwen3_layer_cfg* cfg, const LayerW& w, const
   {
     const MatW* g[3] = {&w.wq, &w.wk, &w.wv};
     const int rows[3] = {q_dim, kv_dim, kv_dim};
-    if ((st = group_weights(g, 3, rows, H, wdt, dt, dq, B, &bdt, s))) return st;
+    if ((st = group_weights(g, 3, rows, H, wdt, dt, dq, B, &bdt, &q4, int64_t(S) * H, s))) return st;
     Proj p{xn, H, B[0], B[1], B[2], q_dim, q_dim + kv_dim, H, qkv, qkv_dim, nullptr, 0, S, qkv_dim, H};
-    if ((st = run_gemm("gemm_qkv", p, dt == QWEN3_F32 ? q3::EPI_STORE_F32 : q3::EPI_STORE_16, bdt, dt, s)))
+    if ((st = run_gemm("gemm_qkv", p, dt == QWEN3_F32 ? q3::EPI_STORE_F32 : q3::EPI_STORE_16, bdt, dt, s, q4)))
       return st;
   }
   // a3+a4: per-head RMSNorm and interleaved MRoPE on q and k, in place; with caches, the same
@@ -471,9 +488,9 @@ static int layer_prefill_impl(const qwen3_layer_cfg* cfg, const LayerW& w, const
   {
     const MatW* g[1] = {&w.wo};
     const int rows[1] = {H};
-    if ((st = group_weights(g, 1, rows, q_dim, wdt, dt, dq, B, &bdt, s))) return st;
+    if ((st = group_weights(g, 1, rows, q_dim, wdt, dt, dq, B, &bdt, &q4, int64_t(S) * q_dim, s))) return st;
     Proj p{o, q_dim, B[0], nullptr, nullptr, H, H, q_dim, y, H, x, H, S, H, q_dim};
-    if ((st = run_gemm("gemm_o_resid", p, q3::EPI_STORE_F32, bdt, dt, s))) return st;
+    if ((st = run_gemm("gemm_o_resid", p, q3::EPI_STORE_F32, bdt, dt, s, q4))) return st;
   }
   // a7: yn = RMSNorm(y1, ffn_norm) (reuses the xn buffer)
   if ((st = run_rmsnorm(y, w.ffn_norm, wdt, xn, dt, S, H, cfg->rms_eps, s))) return st;
@@ -481,17 +498,17 @@ static int layer_prefill_impl(const qwen3_layer_cfg* cfg, const LayerW& w, const
   {
     const MatW* g[2] = {&w.wg, &w.wu};
     const int rows[2] = {F, F};
-    if ((st = group_weights(g, 2, rows, H, wdt, dt, dq, B, &bdt, s))) return st;
+    if ((st = group_weights(g, 2, rows, H, wdt, dt, dq, B, &bdt, &q4, int64_t(S) * H, s))) return st;
     Proj gu{xn, H, B[0], B[1], nullptr, 0, 0, H, act, F, nullptr, 0, S, 2 * F, H};
-    if ((st = run_gemm("gemm_gate_up_swiglu", gu, q3::EPI_SWIGLU_16, bdt, dt, s))) return st;
+    if ((st = run_gemm("gemm_gate_up_swiglu", gu, q3::EPI_SWIGLU_16, bdt, dt, s, q4))) return st;
   }
   // a9: y2 = y1 + a Wd^T
   {
     const MatW* g[1] = {&w.wd};
     const int rows[1] = {H};
-    if ((st = group_weights(g, 1, rows, F, wdt, dt, dq, B, &bdt, s))) return st;
+    if ((st = group_weights(g, 1, rows, F, wdt, dt, dq, B, &bdt, &q4, int64_t(S) * F, s))) return st;
     Proj dn{act, F, B[0], nullptr, nullptr, H, H, F, y, H, y, H, S, H, F};
-    if ((st = run_gemm("gemm_down_resid", dn, q3::EPI_STORE_F32, bdt, dt, s))) return st;
+    if ((st = run_gemm("gemm_down_resid", dn, q3::EPI_STORE_F32, bdt, dt, s, q4))) return st;
   }
   // a10: DeepStack rows (the validated host row list goes to the workspace on the stream)
   if (n_ds > 0) {

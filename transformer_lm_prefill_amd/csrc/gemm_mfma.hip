@@ -74,6 +74,15 @@
 
 namespace q3 {
 
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>), in order
+template <int N, int I = 0, class Fn>
+__device__ __forceinline__ void static_for(Fn&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
 constexpr int kBM = 256;
 constexpr int kBK = 64;  // K must be a multiple of this
 
@@ -275,7 +284,70 @@ __device__ __forceinline__ void buf2lds(__amdgpu_buffer_rsrc_t r, void* l, uint3
 #define Q3_WAIT_VMCNT(N) \
   __builtin_amdgcn_s_waitcnt(((N) & 0xF) | (0x7 << 4) | (0xF << 8) | (((N) >> 4) << 14))
 
-template <int BN, int WM, int WN, int EPI, int OP, bool CVT, int NS, bool BUF>
+// Q4_0 weight tiles (GGML's block: a binary16 scale d, then 16 bytes holding the codes of
+// weights j (low nibble) and j + 16 (high nibble) of 32 consecutive weights of a row; weight =
+// d * (code - 8)). One 32-wide K step of a weight row is exactly one 18-byte block, and two
+// consecutive blocks (36 bytes) start at a 4-byte boundary when K is a multiple of 64. One
+// thread per weight row loads the pair on even K steps and decodes block 0 of it on the even
+// step, block 1 on the odd one. Each weight is d * (code - 8) rounded once to the operand type,
+// as the separate expansion kernel does: the code becomes the binary16 1024 + code by inserting
+// its byte under a 0x64 exponent byte, 1032 is subtracted exactly, and one multiplication by d
+// rounds.
+typedef uint32_t u32x4a4_g __attribute__((ext_vector_type(4), aligned(4)));
+struct Q4Pair {
+  u32x4 a, b;   // bytes 0-15, 16-31 of the pair
+  uint32_t c;   // bytes 32-35
+};
+// The 4 chunks of 8 weights (chunk i: weights 8i .. 8i+7) of block `second` of the pair.
+template <int OP>
+__device__ __forceinline__ void q4_decode_block(const Q4Pair& q, bool second, u32x4 (&chunk)[4]) {
+  // block 0: d in bytes 0-1, codes in bytes 2-17; block 1: d in bytes 18-19, codes 20-35
+  const uint32_t w[9] = {q.a[0], q.a[1], q.a[2], q.a[3], q.b[0], q.b[1], q.b[2], q.b[3], q.c};
+  uint32_t code[4];
+  uint32_t dbits;
+  if (second) {
+    dbits = w[4] >> 16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) code[i] = w[5 + i];
+  } else {
+    dbits = w[0] & 0xFFFFu;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) code[i] = __builtin_amdgcn_alignbyte(w[i + 1], w[i], 2u);
+  }
+  // code[i] holds code bytes 4i .. 4i+3: low nibbles = weights 4i..4i+3 (chunk i / 2), high
+  // nibbles = weights 16 + 4i .. (chunk 2 + i / 2)
+  if constexpr (OP == OP_F16) {
+    typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+    const h2_t dd = __builtin_bit_cast(h2_t, dbits | (dbits << 16));
+    const h2_t off = __builtin_bit_cast(h2_t, 0xE408E408u);  // (-1032, -1032)
+    auto pair = [&](uint32_t nib, uint32_t sel) {
+      const h2_t v = __builtin_bit_cast(h2_t, __builtin_amdgcn_perm(0x64646464u, nib, sel)) + off;
+      return __builtin_bit_cast(uint32_t, v * dd);
+    };
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = code[i] & 0x0F0F0F0Fu, hi = (code[i] >> 4) & 0x0F0F0F0Fu;
+      chunk[i >> 1][2 * (i & 1)] = pair(lo, 0x04010400u);
+      chunk[i >> 1][2 * (i & 1) + 1] = pair(lo, 0x04030402u);
+      chunk[2 + (i >> 1)][2 * (i & 1)] = pair(hi, 0x04010400u);
+      chunk[2 + (i >> 1)][2 * (i & 1) + 1] = pair(hi, 0x04030402u);
+    }
+  } else {
+    const float d = h2f(static_cast<uint16_t>(dbits));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const uint32_t b0 = (code[i] >> (16 * k)) & 0xFFu, b1 = (code[i] >> (16 * k + 8)) & 0xFFu;
+        chunk[i >> 1][2 * (i & 1) + k] = pack2bf(d * static_cast<float>(static_cast<int>(b0 & 15u) - 8),
+                                                 d * static_cast<float>(static_cast<int>(b1 & 15u) - 8));
+        chunk[2 + (i >> 1)][2 * (i & 1) + k] = pack2bf(d * static_cast<float>(static_cast<int>(b0 >> 4) - 8),
+                                                       d * static_cast<float>(static_cast<int>(b1 >> 4) - 8));
+      }
+  }
+}
+
+template <int BN, int WM, int WN, int EPI, int OP, bool CVT, int NS, bool BUF, bool BQ = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WM * WN, 64 * WM * WN),
                           amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4)))
 void gemm_d2l_kernel(const GemmParams p) {
@@ -288,7 +360,12 @@ void gemm_d2l_kernel(const GemmParams p) {
   constexpr int WAVES = THREADS / 64;
   constexpr int AJ = ASLOT / THREADS;         // loads per thread per stage, A
   constexpr int BJ = (BSLOT + THREADS - 1) / THREADS;  // loads per thread per stage, B
-  constexpr int LPS = AJ + BJ;                // loads per thread per stage (equal in every wave)
+  constexpr int LPS = AJ + (BQ ? 0 : BJ);     // loads per thread per stage (equal in every wave)
+  // BQ: Q4_0 block pairs are requested with the stages of even K steps, 3 loads each
+  constexpr int QL = 3;
+  static_assert(!BQ || (!CVT && NS % 2 == 0 && BN <= THREADS), "Q4_0 weight tiles");
+  // loads this thread issues for stage st (the K step of stage st has the parity of st)
+  auto lps = [](int st) constexpr { return LPS + ((BQ && st % 2 == 0) ? QL : 0); };
   constexpr bool SINK = (BSLOT % THREADS) != 0;
   constexpr bool TRANS = Q3_GEMM_TRANS && EPI == EPI_STORE_F32;  // accumulators hold C^T blocks
   static_assert(ASLOT % THREADS == 0 && BSLOT % 64 == 0, "tile shape");
@@ -341,7 +418,19 @@ void gemm_d2l_kernel(const GemmParams p) {
   if constexpr (BUF)
     rsrc_a = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.A), static_cast<short>(0),
                                                static_cast<int>(2 * static_cast<int64_t>(p.M) * p.lda), 0x00020000);
+  // BQ: this thread's weight row (one thread per row; threads past BN load row BN - 1 and store
+  // nothing)
+  const int q_r = min(tid, BN - 1);
+  const bool q_active = tid < BN;
+  const int64_t q_row_bytes = static_cast<int64_t>(p.K / 32) * 18;
+  const uint8_t* q_rowp = nullptr;
   auto set_issue_tile = [&](int itm, int itn) {
+    if constexpr (BQ) {
+      const uint16_t* base;
+      int idx, rows;
+      b_seg<BN, WN, EPI>(p, itn, q_r, base, idx, rows);
+      q_rowp = reinterpret_cast<const uint8_t*>(base) + idx * q_row_bytes;
+    }
 #pragma unroll
     for (int j = 0; j < AJ; ++j) {
       const int slot = (wave + j * WAVES) * 64 + lane;
@@ -412,6 +501,7 @@ void gemm_d2l_kernel(const GemmParams p) {
   // and stored to LDS by the same thread before the barrier that publishes the stage
   constexpr bool STAGE_B = CVT && Q3_GEMM_CVT_LDS == 3 && WM >= 4;
   u32x4 breg[NS][BJ];
+  Q4Pair qraw[NS / 2];   // BQ: the block pair of stages 2i (block 0) and 2i + 1 (block 1)
   const int nk = p.K / kBK2;
   const int total = my_tiles * nk;  // K steps of all this workgroup's tiles, in order
   // Requests go out one K step at a time in order: (iss_tile, iss_kt) is the next one; past
@@ -432,10 +522,22 @@ void gemm_d2l_kernel(const GemmParams p) {
     } else {
       k0 = (nk - 1) * kBK2;
     }
+    if constexpr (BQ) {
+      if (st % 2 == 0) {   // even K step: its block and the next one, 36 bytes from a 4-byte boundary
+        const uint8_t* src = q_rowp + (k0 / 64) * 36;
+        const u32x4a4_g v0 = *reinterpret_cast<const u32x4a4_g*>(src);
+        const u32x4a4_g v1 = *reinterpret_cast<const u32x4a4_g*>(src + 16);
+        Q4Pair& q = qraw[st / 2];
+        q.a = u32x4{v0[0], v0[1], v0[2], v0[3]};
+        q.b = u32x4{v1[0], v1[1], v1[2], v1[3]};
+        q.c = *reinterpret_cast<const uint32_t*>(src + 32);
+      }
+    }
     if constexpr (BUF) {
 #pragma unroll
       for (int j = 0; j < AJ; ++j)
         buf2lds(rsrc_a, stA(st) + (wave + j * WAVES) * 64, voff_a[j], 2 * k0);
+      if constexpr (!BQ)
 #pragma unroll
       for (int j = 0; j < BJ; ++j) {
         const int blk = wave + j * WAVES;
@@ -447,6 +549,7 @@ void gemm_d2l_kernel(const GemmParams p) {
     } else {
 #pragma unroll
       for (int j = 0; j < AJ; ++j) g2lds(a_src[j] + k0, stA(st) + (wave + j * WAVES) * 64);
+      if constexpr (!BQ)
 #pragma unroll
       for (int j = 0; j < BJ; ++j) {
         const int blk = wave + j * WAVES;
@@ -498,6 +601,15 @@ void gemm_d2l_kernel(const GemmParams p) {
   // In-LDS conversion of the B slots this thread loaded into stage st (its own loads of that
   // stage must have landed).
   auto convert_own = [&](int st) {
+    if constexpr (BQ) {
+      // the K step held by stage st has the parity of st (NS and the K steps per tile are even)
+      if (q_active) {
+        u32x4 chunk[4];
+        q4_decode_block<OP>(qraw[st / 2], (st & 1) != 0, chunk);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) stB(st)[q_r * 4 + (c ^ swz4(q_r))] = chunk[c];
+      }
+    }
     if constexpr (STAGE_B) {
 #pragma unroll
       for (int j = 0; j < BJ; ++j) {
@@ -540,7 +652,13 @@ void gemm_d2l_kernel(const GemmParams p) {
 
 #pragma unroll
   for (int st = 0; st < NS - 1; ++st) issue(st, st);
-  wait_vm(std::integral_constant<int, (NS - 2) * LPS>{});  // own loads of stage 0 landed
+  // own loads of stage 0 landed (those of stages 1 .. NS-2 may still be in flight)
+  constexpr int W0 = [&]() constexpr {
+    int n = 0;
+    for (int st = 1; st < NS - 1; ++st) n += lps(st);
+    return n;
+  }();
+  wait_vm(std::integral_constant<int, W0>{});
   convert_own(0);
   barrier();  // stage 0 complete (and converted) everywhere
   fread(0, 0, 0);
@@ -549,8 +667,15 @@ void gemm_d2l_kernel(const GemmParams p) {
   // its reads of stage kt-1), refill stage kt-1's buffer with step kt+NS-1, then the two
   // 16-wide sub-steps; the second one reads sub-step 0 of step kt+1, so the MFMAs after the
   // next barrier start on operands already in registers.
-  auto step = [&](int u, int g) {
-    wait_vm(std::integral_constant<int, (NS - 3) * LPS>{});
+  auto step = [&](auto u_c, int g) __attribute__((always_inline)) {
+    constexpr int u = decltype(u_c)::value;
+    // own loads of stage u+1 landed (stages u+2 .. u+NS-2 may still be in flight)
+    constexpr int WN1 = [&]() constexpr {
+      int n = 0;
+      for (int k = 2; k <= NS - 2; ++k) n += lps((u + k) % NS);
+      return n;
+    }();
+    wait_vm(std::integral_constant<int, WN1>{});
     convert_own((u + 1) % NS);
     barrier();
     issue((u + NS - 1) % NS, g + NS - 1);
@@ -567,8 +692,7 @@ void gemm_d2l_kernel(const GemmParams p) {
   int g = 0;
   int done = 0, cur = 0;
   for (; g + NS <= total; g += NS) {
-#pragma unroll
-    for (int u = 0; u < NS; ++u) step(u, g + u);
+    static_for<NS>([&](auto u_c) __attribute__((always_inline)) { step(u_c, g + decltype(u_c)::value); });
     if constexpr (EPI == EPI_SWIGLU_16) {
       const bool tile_end = my_tiles > 1 && done + NS == nk;
       if (my_tiles > 1) done += NS;
@@ -588,9 +712,9 @@ void gemm_d2l_kernel(const GemmParams p) {
       }
     }
   }
-#pragma unroll
-  for (int u = 0; u < NS - 1; ++u)
-    if (g + u < total) step(u, g + u);
+  static_for<NS - 1>([&](auto u_c) __attribute__((always_inline)) {
+    if (g + decltype(u_c)::value < total) step(u_c, g + decltype(u_c)::value);
+  });
 
   // the trailing reloads of the last tile must land before this workgroup's LDS is released
   Q3_WAIT_VMCNT(0);
@@ -707,6 +831,52 @@ static hipError_t launch_t(const GemmParams& p, hipStream_t s) {
   else
     gemm_d2l_kernel<BN, WM, WN, EPI, OP, CVT, NS, false><<<grid, 64 * WM * WN, 0, s>>>(p);
   return hipGetLastError();
+}
+
+// Q4_0 weights decoded in the weight-tile path (A through buffer loads: the caller checks
+// that its byte extent fits 32-bit offsets).
+template <int BN, int WM, int WN, int EPI, int OP>
+static hipError_t launch_q4(const GemmParams& p, hipStream_t s) {
+  const int tiles = ((p.M + kBM - 1) / kBM) * (p.N / BN);
+  constexpr int NS = 4;
+  int grid = tiles;
+  if (EPI == EPI_SWIGLU_16 && (p.K / kBK2) % NS == 0 && Q3_GEMM_PERSIST) {
+    const int cus = gemm_cu_count();
+    if (cus >= 8 && tiles > cus) grid = cus & ~7;
+  }
+  gemm_d2l_kernel<BN, WM, WN, EPI, OP, false, NS, true, true><<<grid, 64 * WM * WN, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+template <int EPI, int OP>
+static hipError_t launch_q4_nb(const GemmParams& p, int nb, hipStream_t s) {
+  if (nb == 4) return launch_q4<256, 2, 4, EPI, OP>(p, s);
+  if (EPI == EPI_SWIGLU_16) return hipErrorInvalidValue;
+  if (nb == 3) return launch_q4<192, 4, 2, EPI, OP>(p, s);
+  if (nb == 2) return launch_q4<128, 4, 2, EPI, OP>(p, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_mfma_q4(const GemmParams& p, int epi, int op, int nb, hipStream_t s) {
+  if (p.M <= 0) return hipSuccess;
+  if (nb == 0) nb = gemm_pick_nb(p.M, p.N, epi);
+  if (nb < 2 || nb > 4 || p.N % (64 * nb) != 0 || p.K % kBK != 0 || p.K <= 0) return hipErrorInvalidValue;
+  if (2 * static_cast<int64_t>(p.M) * p.lda > 0x7fffffff) return hipErrorInvalidValue;
+  if (epi != EPI_SWIGLU_16 && (p.nseg0 % 16 != 0 || p.nseg1 % 16 != 0)) return hipErrorInvalidValue;
+  if (op == OP_F16) {
+    switch (epi) {
+      case EPI_STORE_16: return launch_q4_nb<EPI_STORE_16, OP_F16>(p, nb, s);
+      case EPI_STORE_F32: return launch_q4_nb<EPI_STORE_F32, OP_F16>(p, nb, s);
+      case EPI_SWIGLU_16: return launch_q4_nb<EPI_SWIGLU_16, OP_F16>(p, nb, s);
+    }
+  } else if (op == OP_BF16) {
+    switch (epi) {
+      case EPI_STORE_16: return launch_q4_nb<EPI_STORE_16, OP_BF16>(p, nb, s);
+      case EPI_STORE_F32: return launch_q4_nb<EPI_STORE_F32, OP_BF16>(p, nb, s);
+      case EPI_SWIGLU_16: return launch_q4_nb<EPI_SWIGLU_16, OP_BF16>(p, nb, s);
+    }
+  }
+  return hipErrorInvalidValue;
 }
 
 // nb selects the tile width 64*nb: 256 (8 waves, 2 x 4), 192 (8 waves, 4 x 2), 128 (8 waves, 4 x 2)

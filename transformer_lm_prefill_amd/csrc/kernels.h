@@ -152,6 +152,11 @@ struct GemmParams {
 // stored as bf16 (converted to fp16 on the way to LDS when op is fp16); otherwise B is in op's
 // format. nb: 32-column MFMA blocks per wave along N (tile width 64*nb); 0 picks one.
 hipError_t launch_gemm_mfma(const GemmParams& p, int epi, int op, bool b_bf16, int nb, hipStream_t s);
+// The same product with B0..B2 holding Q4_0 blocks (18 bytes per 32 weights of a row, rows back
+// to back, 4-byte aligned; ldb unused) decoded in the weight-tile path into op's format. Needs
+// K % 64 == 0, the A operand's byte extent within 32-bit offsets and segment bounds (QKV) at
+// multiples of 16 rows; returns hipErrorInvalidValue otherwise.
+hipError_t launch_gemm_mfma_q4(const GemmParams& p, int epi, int op, int nb, hipStream_t s);
 int gemm_pick_nb(int M, int N, int epi);
 
 // ---- 16-bit GQA flash attention (causal or bidirectional), head_dim 64 or 128 ---------------
