@@ -2,9 +2,10 @@
 
 One step = the whole hot path (RMSNorm, QKV, q/k norm + MRoPE, causal GQA attention, o-proj +
 residual, RMSNorm, SwiGLU FFN + residual) for all 4 layers over one 4096-token sequence, with
-seeded synthetic bf16 weight values (stored once as fp16 at load: the same numbers in the
-products' operand format) and inputs already resident in HBM. The same stack with the bf16
-weights as given, the measured MFMA and copy peaks, the streaming kernels' HBM rates on
+seeded synthetic bf16 weight values (stored once at load as fp16 with the projection matrices
+in 16x32 tiles: the same numbers in the products' operand format, read as whole 1 KiB blocks)
+and inputs already resident in HBM. The same stack with the bf16 weights as given and with
+row-major fp16 weights, the measured MFMA and copy peaks, the streaming kernels' HBM rates on
 rotated inputs and the wider paths (whole model, bidirectional attention, decode, Q4_0) are
 extra fields. Prints ONE JSON line.
 
@@ -63,7 +64,7 @@ def copy_calibration():
 
 def kernel_sources_digest():
     """Digest of the GEMM kernel source, to tell whether stored counter data is still current."""
-    p = os.path.join(ROOT, "transformer_lm_prefill_amd", "csrc", "gemm_mfma.hip")
+    p = os.path.join(ROOT, "transformer_lm_prefill_amd", "csrc", "gemm_mfma.h")
     with open(p, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
@@ -590,18 +591,20 @@ def main():
     rows = rows_h  # host row list (checked by the library before any launch)
 
     # The weights are generated as bf16 values (the workload's format). Loading stores them once
-    # as fp16, the format of the matrix products: every such bf16 value with magnitude in
-    # [2^-17, 65504] is an fp16 value, so this re-encodes the same numbers; the kernels then
-    # read operand-format weights instead of converting each bf16 tile in their inner loop.
+    # as fp16, the format of the matrix products, with the projection matrices in the tiled
+    # layout (qwen3_tile_weights: 16-row x 32-column tiles of 1 KiB): every such bf16 value of
+    # magnitude in [2^-14, 65504] is an fp16 value, so this re-encodes the same numbers; the
+    # kernels then read operand-format weights as whole 1 KiB blocks instead of converting each
+    # bf16 tile in their inner loop.
     prepared, spec_run = layers, spec
     prep_ms = None
     if cfg.dtype == "bf16":
         torch.cuda.synchronize()
         t = time.perf_counter()
-        prepared = [{n: t_.to(torch.float16) for n, t_ in lw.items()} for lw in layers]
+        prepared = [q3.tile_layer_weights(lw) for lw in layers]
         torch.cuda.synchronize()
         prep_ms = (time.perf_counter() - t) * 1e3
-        spec_run = q3.LayerSpec(**{**spec.__dict__, "dtype": "f16"})
+        spec_run = q3.LayerSpec(**{**spec.__dict__, "dtype": "f16t"})
     ds = None if ds_h is None else to(ds_h, cfg.dtype).to(torch.float16 if cfg.dtype == "bf16" else torch.float32)
 
     r = run_stack(q3, spec_run, prepared, x0, pos, rows, ds, S, L, args.steps, args.warmup)
@@ -635,7 +638,16 @@ def main():
         out["what"] = "the same stack with the bf16 weights as given (each weight tile converted to fp16 in the GEMM loop)"
         return out
 
+    def row_major_f16():
+        plain = [{n: t_.to(torch.float16) for n, t_ in lw.items()} for lw in layers]
+        rp = run_stack(q3, q3.LayerSpec(**{**spec.__dict__, "dtype": "f16"}), plain, x0, pos, rows, ds, S, L,
+                       args.steps, args.warmup)
+        out = stack_summary(rp, cfg, S, L, args.steps)
+        out["what"] = "the same stack with the fp16 weights row-major (not tiled)"
+        return out
+
     bf16_in_kernel = extra(cfg.dtype != "bf16", as_given)
+    f16_row_major = extra(cfg.dtype != "bf16", row_major_f16)
     del prepared
     peaks = extra(False, measured_peaks)
     streaming = extra(False, streaming_rotated, cfg)
@@ -660,8 +672,9 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f16",
-        "weights_dtype": ("bf16 values, stored once as fp16 at load (exact re-encoding; "
-                          f"{prep_ms:.1f} ms for the 4 layers, outside the timed region)"
+        "weights_dtype": ("bf16 values, stored once at load as fp16 with the projection matrices in "
+                          "16x32 tiles (qwen3_tile_weights; exact re-encoding; "
+                          f"{prep_ms:.1f} ms for the {L} layers, outside the timed region)"
                           if prep_ms is not None else cfg.dtype),
         "data": "synthetic (seeded N(0,1) inputs, N(0,0.02) weights, 1+N(0,0.1) norms; random-init)",
         "config": {"workload": f"{cfg.name}: {L} decoder layers, hidden {cfg.hidden}, "
@@ -680,6 +693,7 @@ def main():
         "measured_peaks": peaks,
         "streaming_kernels_rotated_inputs": streaming,
         "bf16_weights_in_kernel": bf16_in_kernel,
+        "f16_row_major_weights": f16_row_major,
         "model_prefill_logits_last": model,
         "bidirectional_attention": bidir,
         "decode": decode,

@@ -52,7 +52,9 @@
 extern "C" {
 #endif
 
-typedef enum { QWEN3_F32 = 0, QWEN3_BF16 = 1, QWEN3_F16 = 2 } qwen3_dtype;
+/* Element types. QWEN3_F16_TILED is a weight storage format only (cfg.wdtype): fp16 values
+ * with each projection matrix in the tiled layout that qwen3_tile_weights writes. */
+typedef enum { QWEN3_F32 = 0, QWEN3_BF16 = 1, QWEN3_F16 = 2, QWEN3_F16_TILED = 3 } qwen3_dtype;
 
 typedef enum {
   QWEN3_OK = 0,
@@ -75,7 +77,13 @@ typedef enum {
  *   mrope_section  (t, h, w) pair counts: sum == hd/2, 3*h <= hd/2 and 3*w <= hd/2. Pair i
  *               follows the h axis when i % 3 == 1 and i < 3*h, the w axis when i % 3 == 2 and
  *               i < 3*w, and the t axis otherwise (Qwen3-VL interleaved MRoPE, `norm_rope`).
- *   wdtype      dtype of the weights: QWEN3_BF16, QWEN3_F16 or QWEN3_F32.
+ *   wdtype      dtype of the weights: QWEN3_BF16, QWEN3_F16 or QWEN3_F32; or QWEN3_F16_TILED:
+ *               fp16 weights whose seven projection matrices (wq, wk, wv, wo, w_gate, w_up,
+ *               w_down) are stored in the tiled layout (qwen3_tile_weights) while the norm
+ *               vectors, DeepStack slabs, embeddings and LM head stay plain row-major fp16.
+ *               Same values and same results as QWEN3_F16; each 32-wide K step of 16 weight
+ *               rows is then one contiguous 1 KiB block, which the products load faster
+ *               (requires act_dtype QWEN3_F16).
  *   act_dtype   dtype of the intermediate matrix-product operands (normalized activations,
  *               q, k, v, attention probabilities and output, the SwiGLU activation):
  *                 QWEN3_F16  fp16 operands, fp32 accumulation and softmax (with bf16 weights,
@@ -106,7 +114,8 @@ typedef struct {
   qwen3_dtype resid_dtype;
 } qwen3_layer_cfg;
 
-/* Device pointers to one layer's weights, all of dtype cfg.wdtype, layout [out, in]. */
+/* Device pointers to one layer's weights, all of dtype cfg.wdtype, layout [out, in]
+ * (QWEN3_F16_TILED: the seven matrices in the tiled layout, the four vectors plain fp16). */
 typedef struct {
   const void *attn_norm;   /* [H]                 input RMSNorm weight                    */
   const void *wq;          /* [nh*hd, H]                                                  */
@@ -124,7 +133,9 @@ typedef struct {
 /* Bytes of device workspace qwen3_layer_prefill needs for `seq_len` tokens (0 if cfg is
  * NULL or seq_len < 1). The workspace holds the normalized activations, q/k/v, the attention
  * output, the SwiGLU activation and the device copy of the DeepStack row list; its contents
- * on entry do not matter. */
+ * on entry do not matter. The normalized activations, attention output and SwiGLU activation
+ * (the A operands of the products) take seq_len rounded up to a multiple of 16 rows: with
+ * 16-bit operands they are kept in the tiled layout. */
 size_t qwen3_layer_workspace_bytes(const qwen3_layer_cfg *cfg, int32_t seq_len);
 
 /* One decoder layer over all `seq_len` tokens (the recipe at the top of this file).
@@ -138,7 +149,8 @@ size_t qwen3_layer_workspace_bytes(const qwen3_layer_cfg *cfg, int32_t seq_len);
  *                 rows only; `forward_text_prefill_logits_last` rejects an image-token position
  *                 outside the sequence). The list is checked on the host and copied into the
  *                 workspace on `stream` during the call; the caller may reuse it on return.
- *   ds            device [n_ds, H] of cfg.wdtype: ds[i] is added to output row ds_rows[i]
+ *   ds            device [n_ds, H] of cfg.wdtype (plain fp16 for QWEN3_F16_TILED): ds[i] is
+ *                 added to output row ds_rows[i]
  *                 after the FFN residual; must be NULL when n_ds == 0 and non-NULL otherwise.
  *   workspace     at least qwen3_layer_workspace_bytes(cfg, S) bytes, 256-byte aligned.
  * Errors: seq_len < 1, NULL pointers, unsupported shapes, a DeepStack row outside [0, S) or
@@ -215,12 +227,28 @@ int apply_rope_tables(void *x, int32_t n, int32_t heads, int32_t head_dim, int64
  *   `x_dtype`, which is also the product operand format (the (wdtype, x_dtype) pairs allowed
  *   are those of (wdtype, act_dtype) in qwen3_layer_cfg). residual [S, hidden] f32 or NULL.
  *   out [S, hidden] of `out_dtype`: f32, or x_dtype when residual is NULL; out may equal
- *   residual. workspace holds the [S, ffn] activation: swiglu_ffn_workspace_bytes() bytes. */
+ *   residual. wdtype QWEN3_F16_TILED: the three matrices in the tiled layout. workspace holds
+ *   the [S, ffn] activation: swiglu_ffn_workspace_bytes() bytes. */
 int swiglu_ffn(const void *x_normed, const void *w_gate, const void *w_up, const void *w_down,
                const void *residual, void *out, int32_t seq_len, int32_t hidden, int32_t ffn,
                qwen3_dtype wdtype, qwen3_dtype x_dtype, qwen3_dtype out_dtype, void *workspace,
                size_t workspace_bytes, void *stream);
 size_t swiglu_ffn_workspace_bytes(int32_t seq_len, int32_t ffn, qwen3_dtype x_dtype);
+
+/* Weight preparation for QWEN3_F16_TILED (for callers that load weights once and run many
+ * prefills; the layer computes the same products either way).
+ *   src   device [rows, cols] row-major of src_dtype (QWEN3_F32, QWEN3_BF16 or QWEN3_F16).
+ *   dst   device rows * cols fp16 values (2 * rows * cols bytes, 16-byte aligned), written
+ *         in the tiled layout: 16-row x 32-column tiles of 1 KiB, row-major inside a tile,
+ *         tiles ordered by row group and then by column, i.e. element (r, c) at
+ *         ((r / 16) * (cols / 32) + c / 32) * 512 + (r % 16) * 32 + c % 32.
+ *   Each value is rounded to the nearest fp16 (ties to even): exact for bf16 and f32 values
+ *   representable in fp16 (bf16 values of magnitude in [2^-14, 65504]); magnitudes beyond
+ *   65504 become infinite, as in any fp16 conversion. rows must be a positive multiple of 16,
+ *   cols of 32; dst must not overlap src. Errors (QWEN3_ERR_INVALID_ARG /
+ *   QWEN3_ERR_UNSUPPORTED) are returned before anything is enqueued. */
+int qwen3_tile_weights(const void *src, qwen3_dtype src_dtype, int32_t rows, int32_t cols, void *dst,
+                       void *stream);
 
 /* Row RMSNorm with a plain weight (cortiq-engine qwen3te.rs, `rms_norm_into`):
  *   y[s] = x[s] / sqrt(mean_j x[s,j]^2 + eps) * w.
@@ -274,7 +302,7 @@ typedef struct {
   const qwen3_layer_weights* layers;   /* HOST array of n_layers entries (device pointers)      */
   const void* output_norm;             /* device [hidden], layer.wdtype                         */
   const void* lm_head;                 /* device [vocab, hidden], layer.wdtype; NULL = tied      */
-} qwen3_model_weights;
+} qwen3_model_weights;                 /* (QWEN3_F16_TILED: these three plain row-major fp16)   */
 
 /* Workspace for qwen3_model_prefill_logits_last: the token ids, the fp32 residual stream
  * [S, hidden], the last row's normalized state and one layer's workspace. 0 for invalid input. */

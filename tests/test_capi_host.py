@@ -77,6 +77,13 @@ def test_workspace_size_formula(lib):
     assert lib.qwen3_layer_workspace_bytes(ctypes.byref(c32), s) == 2 * expect + 4 * s
     assert lib.qwen3_layer_workspace_bytes(ctypes.byref(c), 0) == 0
     assert lib.qwen3_layer_workspace_bytes(None, 16) == 0
+    # a ragged length: xn, o and act (the product A operands, tiled for 16-bit operands) take
+    # whole 16-row groups; qkv and the row list take S rows
+    a256 = lambda b: (b + 255) // 256 * 256
+    s, s16 = 77, 80
+    expect = (a256(2 * s16 * 4096) + a256(2 * s * 6144) + a256(2 * s16 * 4096) + a256(2 * s16 * 12288)
+              + a256(4 * s))
+    assert lib.qwen3_layer_workspace_bytes(ctypes.byref(c), s) == expect
 
 
 @pytest.mark.parametrize("kw,status,needle", [
@@ -397,3 +404,30 @@ def test_model_decode_argument_checks(lib):
                                                   kc, vc, 15, FAKE, ws, mws, None) == 1
     assert lib.qwen3_model_prefill_logits_last_kv(ctypes.byref(m), ctypes.byref(mw), tok, 16, FAKE, None, 0, None,
                                                   None, None, 16, FAKE, ws, mws, None) == 1
+
+
+def test_tiled_weight_format_rules(lib):
+    """QWEN3_F16_TILED (3) is a weight format for fp16 operands only, never an operand type."""
+    assert _call_layer(lib, _cfg(wdtype=3, act_dtype=1)) == 2     # with bf16 operands
+    assert _call_layer(lib, _cfg(wdtype=3, act_dtype=0)) == 2     # with f32 operands
+    assert _call_layer(lib, _cfg(wdtype=2, act_dtype=3)) == 1     # as an operand type
+    assert _call_layer(lib, _cfg(wdtype=3, act_dtype=2), ws_bytes=16) == 3   # accepted: stops at the workspace
+
+
+def test_tile_weights_checks(lib):
+    """Every rejection happens before anything is enqueued (fake pointers, never dereferenced)."""
+    src = ctypes.c_void_p(0x200000)
+    dst = ctypes.c_void_p(0x800000)
+    t = lib.qwen3_tile_weights
+    assert t(None, 1, 64, 128, dst, None) == 1                      # NULL source
+    assert t(src, 1, 64, 128, None, None) == 1                      # NULL destination
+    assert t(src, 3, 64, 128, dst, None) == 1                       # the tiled format is no source type
+    assert t(src, 7, 64, 128, dst, None) == 1                       # not a dtype
+    assert t(ctypes.c_void_p(0x200008), 1, 64, 128, dst, None) == 1  # misaligned
+    assert t(src, 1, 60, 128, dst, None) == 2                       # rows not a multiple of 16
+    assert t(src, 1, 64, 112, dst, None) == 2                       # cols not a multiple of 32
+    assert t(src, 1, 0, 128, dst, None) == 2
+    # bf16 [64, 128] spans 16 KiB from src: a destination starting inside it overlaps
+    assert t(src, 1, 64, 128, ctypes.c_void_p(0x200000 + 0x3000), None) == 1
+    assert t(src, 0, 64, 128, ctypes.c_void_p(0x200000 - 0x3000), None) == 1   # dst (16 KiB) runs into src
+    assert b"overlap" in lib.qwen3_last_error()

@@ -35,6 +35,8 @@ from .ops import (  # noqa: F401
     qk_norm_mrope,
     rms_norm_rows,
     swiglu_ffn,
+    tile_layer_weights,
+    tile_weights,
     timing_collect,
     timing_enable,
     vision_rope_tables,

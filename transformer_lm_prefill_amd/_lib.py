@@ -8,6 +8,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqwen3_pr
 QWEN3_F32 = 0
 QWEN3_BF16 = 1
 QWEN3_F16 = 2
+QWEN3_F16_TILED = 3
 STATUS = {0: "QWEN3_OK", 1: "QWEN3_ERR_INVALID_ARG", 2: "QWEN3_ERR_UNSUPPORTED",
           3: "QWEN3_ERR_WORKSPACE", 4: "QWEN3_ERR_HIP"}
 
@@ -21,7 +22,8 @@ EXPORTS = ("qwen3_layer_workspace_bytes", "qwen3_layer_prefill", "qk_norm_mrope"
            "qwen3_layer_decode_workspace_bytes", "dequantize_matrix",
            "qwen3_layer_quant_workspace_bytes", "qwen3_layer_prefill_quant", "qwen3_layer_decode_quant",
            "qwen3_model_prefill_logits_last_kv", "qwen3_model_decode_workspace_bytes", "qwen3_model_decode_logits",
-           "qwen3_last_error", "qwen3_timing_enable", "qwen3_timing_collect", "qwen3_mfma_probe")
+           "qwen3_last_error", "qwen3_timing_enable", "qwen3_timing_collect", "qwen3_mfma_probe",
+           "qwen3_tile_weights")
 
 
 class LayerCfg(ctypes.Structure):
@@ -128,6 +130,8 @@ def load():
     lib.gqa_decode_attention_noalloc.restype = ctypes.c_int
     lib.qwen3_mfma_probe.argtypes = [i32, i32, vp, vp, vp]
     lib.qwen3_mfma_probe.restype = ctypes.c_int
+    lib.qwen3_tile_weights.argtypes = [vp, ctypes.c_int, i32, i32, vp, vp]
+    lib.qwen3_tile_weights.restype = ctypes.c_int
     lib.qwen3_layer_decode.argtypes = [ctypes.POINTER(LayerCfg), ctypes.POINTER(LayerWeights),
                                        vp, vp, vp, vp, vp, i32, i32, vp, sz, vp]
     lib.qwen3_layer_decode.restype = ctypes.c_int

@@ -16,9 +16,11 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqwen3_prefill.so")
-SOURCES = ["capi.hip", "norm_rope.hip", "gemm_mfma.hip", "attention_mfma.hip", "fp32_path.hip",
+# longest compiles first (the product kernels), so the parallel build ends sooner
+SOURCES = ["gemm_part_f16.hip", "gemm_part_q4.hip", "gemm_part_f16_cvt.hip", "gemm_part_bf16.hip",
+           "capi.hip", "norm_rope.hip", "gemm_mfma.hip", "attention_mfma.hip", "fp32_path.hip",
            "model_head.hip", "vision_rope.hip", "decode.hip",
-           "quant.hip", "noalloc.hip", "measure.hip"]
+           "quant.hip", "noalloc.hip", "measure.hip", "tiles.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

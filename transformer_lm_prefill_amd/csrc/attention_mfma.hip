@@ -330,16 +330,21 @@ void attn_fwd_kernel(const AttnParams p) {
   const float l_run = l_part + __shfl_xor(l_part, 32);
   if (my_t < p.S) {
     const float inv = 1.0f / l_run;
-    uint16_t* op = p.o + static_cast<int64_t>(my_t) * p.o_stride + hq * HD;
+    // row-major: column hq*HD + 32d + j at row offset + hq*HD + 32d + j; tiled (16-row groups of
+    // 32-column tiles): the row's offset inside its group, + 512 per 32 columns
+    const int64_t o_row = p.o_tiled ? static_cast<int64_t>(my_t >> 4) * 16 * p.o_stride + (my_t & 15) * 32
+                                    : static_cast<int64_t>(my_t) * p.o_stride;
+    const int d_ks = p.o_tiled ? 512 : 32;
+    uint16_t* op = p.o + o_row + (hq * HD / 32) * d_ks;
 #pragma unroll
     for (int d = 0; d < ND; ++d)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const int hd0 = d * 32 + 8 * q4 + 4 * hi;
+        const int j = 8 * q4 + 4 * hi;
         u32x2 w;
         w[0] = F::pack2(o[d][4 * q4 + 0] * inv, o[d][4 * q4 + 1] * inv);
         w[1] = F::pack2(o[d][4 * q4 + 2] * inv, o[d][4 * q4 + 3] * inv);
-        *reinterpret_cast<u32x2*>(op + hd0) = w;
+        *reinterpret_cast<u32x2*>(op + d * d_ks + j) = w;
       }
   }
 }
@@ -373,6 +378,7 @@ static hipError_t launch_op(const AttnParams& p, hipStream_t s) {
 hipError_t launch_attention_mfma(const AttnParams& p, int op, hipStream_t s) {
   if (p.S <= 0) return hipSuccess;
   if (p.nkv <= 0 || p.nh % p.nkv != 0) return hipErrorInvalidValue;
+  if (p.o_tiled && p.o_stride != static_cast<int64_t>(p.nh) * p.head_dim) return hipErrorInvalidValue;
   if (p.head_dim == 128) {
     if (op == OP_BF16) return launch_op<OP_BF16, 128>(p, s);
     if (op == OP_F16) return launch_op<OP_F16, 128>(p, s);

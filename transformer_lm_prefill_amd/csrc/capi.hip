@@ -81,17 +81,24 @@ struct KTimer {
 
 // ---- checks ---------------------------------------------------------------------------------
 bool valid_dtype(int d) { return d == QWEN3_F32 || d == QWEN3_BF16 || d == QWEN3_F16; }
+// Weight storage formats: the element types, plus fp16 with tiled projection matrices.
+bool valid_wdtype(int d) { return valid_dtype(d) || d == QWEN3_F16_TILED; }
+// Element type of the weight vectors (norms), embeddings and DeepStack slabs under wdtype w.
+qwen3_dtype plain_w(qwen3_dtype w) { return w == QWEN3_F16_TILED ? QWEN3_F16 : w; }
+size_t round16(int32_t n) { return (static_cast<size_t>(n) + 15) & ~static_cast<size_t>(15); }
 size_t dsize(qwen3_dtype d) { return d == QWEN3_F32 ? 4 : 2; }
 
 // (weights, product operands) pairs the kernels run: f32/f32, bf16/bf16, bf16/f16, f16/f16.
 int check_formats(qwen3_dtype w, qwen3_dtype a) {
-  if (!valid_dtype(w) || !valid_dtype(a))
+  if (!valid_wdtype(w) || !valid_dtype(a))
     return fail(QWEN3_ERR_INVALID_ARG, "dtype (%d, %d) is not a qwen3_dtype", w, a);
   const bool ok = (w == QWEN3_F32 && a == QWEN3_F32) || (w == QWEN3_BF16 && a == QWEN3_BF16) ||
-                  (w == QWEN3_BF16 && a == QWEN3_F16) || (w == QWEN3_F16 && a == QWEN3_F16);
+                  (w == QWEN3_BF16 && a == QWEN3_F16) || (w == QWEN3_F16 && a == QWEN3_F16) ||
+                  (w == QWEN3_F16_TILED && a == QWEN3_F16);
   if (!ok)
     return fail(QWEN3_ERR_UNSUPPORTED,
-                "weights %d with operands %d: supported pairs are f32/f32, bf16/bf16, bf16/f16, f16/f16", w, a);
+                "weights %d with operands %d: supported pairs are f32/f32, bf16/bf16, bf16/f16, f16/f16, "
+                "f16-tiled/f16", w, a);
   return QWEN3_OK;
 }
 size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
@@ -174,25 +181,28 @@ struct Workspace {
   size_t xn, qkv, o, act, dsrows, total;
 };
 
+// xn, o and act are the A operands of the products: in the tiled layout for 16-bit operands,
+// over whole 16-row groups (S rounded up to a multiple of 16).
 Workspace layout(const qwen3_layer_cfg* c, int32_t S) {
   const size_t e = dsize(c->act_dtype);
   const size_t q_dim = static_cast<size_t>(c->n_heads) * c->head_dim;
   const size_t kv_dim = static_cast<size_t>(c->n_kv_heads) * c->head_dim;
+  const size_t S16 = round16(S);
   Workspace w;
   w.xn = 0;
-  w.qkv = w.xn + align256(static_cast<size_t>(S) * c->hidden * e);
+  w.qkv = w.xn + align256(S16 * c->hidden * e);
   w.o = w.qkv + align256(static_cast<size_t>(S) * (q_dim + 2 * kv_dim) * e);
-  w.act = w.o + align256(static_cast<size_t>(S) * q_dim * e);
-  w.dsrows = w.act + align256(static_cast<size_t>(S) * c->ffn * e);
+  w.act = w.o + align256(S16 * q_dim * e);
+  w.dsrows = w.act + align256(S16 * c->ffn * e);
   w.total = w.dsrows + align256(static_cast<size_t>(S) * 4);
   return w;
 }
 
 // ---- building blocks shared by the layer and the sub-op entry points ------------------------
 int run_rmsnorm(const float* x, const void* w, qwen3_dtype wd, void* y, qwen3_dtype yd, int rows,
-                int hidden, float eps, hipStream_t s) {
+                int hidden, float eps, hipStream_t s, bool y_tiled = false) {
   KTimer t("rmsnorm", s);
-  hipError_t e = q3::launch_rmsnorm(x, w, wd, y, yd, rows, hidden, eps, s);
+  hipError_t e = q3::launch_rmsnorm(x, w, wd, y, yd, rows, hidden, eps, s, y_tiled);
   return e == hipSuccess ? QWEN3_OK : hip_fail(e, "rmsnorm launch");
 }
 
@@ -204,13 +214,13 @@ int run_qk_norm_mrope(const q3::RopeParams& p, int hd, qwen3_dtype dt, hipStream
 
 int run_attention(const void* q, const void* k, const void* v, void* o, int64_t qs, int64_t ks,
                   int64_t vs, int64_t os, int S, int nh, int nkv, int hd, float scale, qwen3_dtype dt,
-                  int causal, hipStream_t s) {
+                  int causal, hipStream_t s, bool o_tiled = false) {
   KTimer t(causal ? "attention" : "attention_bidirectional", s);
   hipError_t e;
   if (dt != QWEN3_F32) {
     q3::AttnParams p{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), qs, ks, vs, os,
-                     S, nh, nkv, scale * 1.4426950408889634f, hd, causal};
+                     S, nh, nkv, scale * 1.4426950408889634f, hd, causal, o_tiled ? 1 : 0};
     e = q3::launch_attention_mfma(p, dt == QWEN3_F16 ? q3::OPH_F16 : q3::OPH_BF16, s);
   } else {
     q3::AttnF32Params p{static_cast<const float*>(q), static_cast<const float*>(k),
@@ -228,6 +238,7 @@ struct Proj {
   void* C; int64_t ldc;
   const float* R; int64_t ldr;
   int M, N, K;
+  int a_t = 0, b_t = 0, c_t = 0;   // A, B, the SwiGLU output in the tiled layout (16-bit only)
 };
 
 // wd: weight dtype; ad: operand dtype (A, MFMA, 16-bit outputs); q4: the B matrices are Q4_0
@@ -239,7 +250,7 @@ int run_gemm(const char* name, const Proj& g, int epi, qwen3_dtype wd, qwen3_dty
   if (ad != QWEN3_F32) {
     q3::GemmParams p{static_cast<const uint16_t*>(g.A), g.lda, static_cast<const uint16_t*>(g.B0),
                      static_cast<const uint16_t*>(g.B1), static_cast<const uint16_t*>(g.B2),
-                     g.nseg0, g.nseg1, g.ldb, g.C, g.ldc, g.R, g.ldr, g.M, g.N, g.K};
+                     g.nseg0, g.nseg1, g.ldb, g.C, g.ldc, g.R, g.ldr, g.M, g.N, g.K, g.a_t, g.b_t, g.c_t};
     if (q4)
       e = q3::launch_gemm_mfma_q4(p, epi, ad == QWEN3_F16 ? q3::OPH_F16 : q3::OPH_BF16, 0, s);
     else
@@ -257,13 +268,16 @@ int run_gemm(const char* name, const Proj& g, int epi, qwen3_dtype wd, qwen3_dty
 }
 
 // a = silu(x Wg^T) * (x Wu^T) into act [S, F]; then out = [R +] a Wd^T.
+// wdt may be QWEN3_F16_TILED (tiled weight matrices); x, act and out are row-major.
 int run_ffn(const void* x, const void* wg, const void* wu, const void* wd, const float* R, void* out,
             qwen3_dtype out_dt, void* act, int S, int H, int F, qwen3_dtype wdt, qwen3_dtype adt,
             hipStream_t s) {
-  Proj gu{x, H, wg, wu, nullptr, 0, 0, H, act, F, nullptr, 0, S, 2 * F, H};
+  const int wt = wdt == QWEN3_F16_TILED;
+  wdt = plain_w(wdt);
+  Proj gu{x, H, wg, wu, nullptr, 0, 0, H, act, F, nullptr, 0, S, 2 * F, H, 0, wt, 0};
   int st = run_gemm("gemm_gate_up_swiglu", gu, q3::EPI_SWIGLU_16, wdt, adt, s);
   if (st) return st;
-  Proj dn{act, F, wd, nullptr, nullptr, H, H, F, out, H, R, H, S, H, F};
+  Proj dn{act, F, wd, nullptr, nullptr, H, H, F, out, H, R, H, S, H, F, 0, wt, 0};
   const int epi = out_dt == QWEN3_F32 ? q3::EPI_STORE_F32 : q3::EPI_STORE_16;
   return run_gemm(R ? "gemm_down_resid" : "gemm_down", dn, epi, wdt, adt, s);
 }
@@ -344,16 +358,20 @@ size_t dequant_bytes(const qwen3_layer_cfg* c) {
   return align256(m * e);
 }
 
-// The matrices of one product group in one storage type: all dense -> as given (wdt); all
+// The matrices of one product group in one storage type: all dense -> as given (wdt; tiled
+// matrices set *b_tiled); all
 // Q4_0, with the product's A operand (a_elems 16-bit elements) within the 32-bit offsets of the
 // GEMM's buffer loads -> the blocks as given, decoded inside the GEMM (*q4 set); otherwise
 // quantized -> expanded back to back into dq in the operand type.
 int group_weights(const MatW* const* m, int n, const int* rows, int cols, qwen3_dtype wdt, qwen3_dtype act,
-                  char* dq, const void** out, qwen3_dtype* bdt, bool* q4, int64_t a_elems, hipStream_t s) {
+                  char* dq, const void** out, qwen3_dtype* bdt, bool* q4, int64_t a_elems, hipStream_t s,
+                  int* b_tiled) {
   *q4 = false;
+  *b_tiled = 0;
   if (m[0]->fmt == QWEN3_W_DENSE) {
     for (int i = 0; i < n; ++i) out[i] = m[i]->data;
-    *bdt = wdt;
+    *bdt = plain_w(wdt);
+    *b_tiled = wdt == QWEN3_F16_TILED;
     return QWEN3_OK;
   }
   bool all_q4 = 2 * a_elems <= 0x7fffffff;
@@ -433,10 +451,14 @@ static int layer_prefill_impl(const qwen3_layer_cfg* cfg, const LayerW& w, const
   }
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const qwen3_dtype wdt = cfg->wdtype, dt = cfg->act_dtype;
+  const qwen3_dtype wdt = plain_w(cfg->wdtype), dt = cfg->act_dtype;
   const int S = seq_len, H = cfg->hidden, nh = cfg->n_heads, nkv = cfg->n_kv_heads, hd = cfg->head_dim;
   const int F = cfg->ffn;
   const int q_dim = nh * hd, kv_dim = nkv * hd, qkv_dim = q_dim + 2 * kv_dim;
+  // 16-bit operands: xn / yn, o and act go through the workspace in the tiled layout
+  const int at = dt != QWEN3_F32;
+  const int64_t S16 = static_cast<int64_t>(round16(S));
+  int bt = 0;
   const size_t e = dsize(dt);
   char* ws = static_cast<char*>(workspace);
   void* xn = ws + L.xn;
@@ -451,13 +473,13 @@ static int layer_prefill_impl(const qwen3_layer_cfg* cfg, const LayerW& w, const
   bool q4 = false;
 
   // a1: input RMSNorm
-  if ((st = run_rmsnorm(x, w.attn_norm, wdt, xn, dt, S, H, cfg->rms_eps, s))) return st;
+  if ((st = run_rmsnorm(x, w.attn_norm, wdt, xn, dt, S, H, cfg->rms_eps, s, at))) return st;
   // a2: q | k | v = xn [Wq; Wk; Wv]^T in one product, token-major [S, q_dim + 2 kv_dim]
   {
     const MatW* g[3] = {&w.wq, &w.wk, &w.wv};
     const int rows[3] = {q_dim, kv_dim, kv_dim};
-    if ((st = group_weights(g, 3, rows, H, wdt, dt, dq, B, &bdt, &q4, int64_t(S) * H, s))) return st;
-    Proj p{xn, H, B[0], B[1], B[2], q_dim, q_dim + kv_dim, H, qkv, qkv_dim, nullptr, 0, S, qkv_dim, H};
+    if ((st = group_weights(g, 3, rows, H, cfg->wdtype, dt, dq, B, &bdt, &q4, S16 * H, s, &bt))) return st;
+    Proj p{xn, H, B[0], B[1], B[2], q_dim, q_dim + kv_dim, H, qkv, qkv_dim, nullptr, 0, S, qkv_dim, H, at, bt, 0};
     if ((st = run_gemm("gemm_qkv", p, dt == QWEN3_F32 ? q3::EPI_STORE_F32 : q3::EPI_STORE_16, bdt, dt, s, q4)))
       return st;
   }
@@ -482,32 +504,32 @@ static int layer_prefill_impl(const qwen3_layer_cfg* cfg, const LayerW& w, const
   // a5: causal GQA attention -> o [S, q_dim]
   if ((st = run_attention(qkv, qkv + static_cast<size_t>(q_dim) * e, qkv + static_cast<size_t>(q_dim + kv_dim) * e,
                           o, qkv_dim, qkv_dim, qkv_dim, q_dim, S, nh, nkv, hd,
-                          1.0f / std::sqrt(static_cast<float>(hd)), dt, 1, s)))
+                          1.0f / std::sqrt(static_cast<float>(hd)), dt, 1, s, at)))
     return st;
   // a6: y1 = x + o Wo^T (fp32, into x_out)
   {
     const MatW* g[1] = {&w.wo};
     const int rows[1] = {H};
-    if ((st = group_weights(g, 1, rows, q_dim, wdt, dt, dq, B, &bdt, &q4, int64_t(S) * q_dim, s))) return st;
-    Proj p{o, q_dim, B[0], nullptr, nullptr, H, H, q_dim, y, H, x, H, S, H, q_dim};
+    if ((st = group_weights(g, 1, rows, q_dim, cfg->wdtype, dt, dq, B, &bdt, &q4, S16 * q_dim, s, &bt))) return st;
+    Proj p{o, q_dim, B[0], nullptr, nullptr, H, H, q_dim, y, H, x, H, S, H, q_dim, at, bt, 0};
     if ((st = run_gemm("gemm_o_resid", p, q3::EPI_STORE_F32, bdt, dt, s, q4))) return st;
   }
   // a7: yn = RMSNorm(y1, ffn_norm) (reuses the xn buffer)
-  if ((st = run_rmsnorm(y, w.ffn_norm, wdt, xn, dt, S, H, cfg->rms_eps, s))) return st;
+  if ((st = run_rmsnorm(y, w.ffn_norm, wdt, xn, dt, S, H, cfg->rms_eps, s, at))) return st;
   // a8: a = silu(yn Wg^T) * (yn Wu^T)
   {
     const MatW* g[2] = {&w.wg, &w.wu};
     const int rows[2] = {F, F};
-    if ((st = group_weights(g, 2, rows, H, wdt, dt, dq, B, &bdt, &q4, int64_t(S) * H, s))) return st;
-    Proj gu{xn, H, B[0], B[1], nullptr, 0, 0, H, act, F, nullptr, 0, S, 2 * F, H};
+    if ((st = group_weights(g, 2, rows, H, cfg->wdtype, dt, dq, B, &bdt, &q4, S16 * H, s, &bt))) return st;
+    Proj gu{xn, H, B[0], B[1], nullptr, 0, 0, H, act, F, nullptr, 0, S, 2 * F, H, at, bt, at};
     if ((st = run_gemm("gemm_gate_up_swiglu", gu, q3::EPI_SWIGLU_16, bdt, dt, s, q4))) return st;
   }
   // a9: y2 = y1 + a Wd^T
   {
     const MatW* g[1] = {&w.wd};
     const int rows[1] = {H};
-    if ((st = group_weights(g, 1, rows, F, wdt, dt, dq, B, &bdt, &q4, int64_t(S) * F, s))) return st;
-    Proj dn{act, F, B[0], nullptr, nullptr, H, H, F, y, H, y, H, S, H, F};
+    if ((st = group_weights(g, 1, rows, F, cfg->wdtype, dt, dq, B, &bdt, &q4, S16 * F, s, &bt))) return st;
+    Proj dn{act, F, B[0], nullptr, nullptr, H, H, F, y, H, y, H, S, H, F, at, bt, 0};
     if ((st = run_gemm("gemm_down_resid", dn, q3::EPI_STORE_F32, bdt, dt, s, q4))) return st;
   }
   // a10: DeepStack rows (the validated host row list goes to the workspace on the stream)
@@ -680,7 +702,7 @@ static int model_prefill_impl(const qwen3_model_cfg* cfg, const qwen3_model_weig
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int S = seq_len, H = cfg->layer.hidden;
-  const qwen3_dtype wdt = cfg->layer.wdtype;
+  const qwen3_dtype wdt = plain_w(cfg->layer.wdtype);
   char* ws = static_cast<char*>(workspace);
   int32_t* tok = reinterpret_cast<int32_t*>(ws + L.tokens);
   float* x = reinterpret_cast<float*>(ws + L.x);
@@ -777,7 +799,7 @@ int qwen3_model_decode_logits(const qwen3_model_cfg* cfg, const qwen3_model_weig
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int H = cfg->layer.hidden;
-  const qwen3_dtype wdt = cfg->layer.wdtype;
+  const qwen3_dtype wdt = plain_w(cfg->layer.wdtype);
   char* ws = static_cast<char*>(workspace);
   float* x = reinterpret_cast<float*>(ws + L.x);
   float* xlast = reinterpret_cast<float*>(ws + L.xlast);
@@ -916,6 +938,24 @@ int swiglu_ffn(const void* x_normed, const void* w_gate, const void* w_up, const
     return fail(QWEN3_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
   return run_ffn(x_normed, w_gate, w_up, w_down, static_cast<const float*>(residual), out, out_dtype,
                  workspace, seq_len, hidden, ffn, wdtype, x_dtype, static_cast<hipStream_t>(stream));
+}
+
+int qwen3_tile_weights(const void* src, qwen3_dtype src_dtype, int32_t rows, int32_t cols, void* dst, void* stream) {
+  if (!valid_dtype(src_dtype)) return fail(QWEN3_ERR_INVALID_ARG, "src_dtype %d is not an element type", src_dtype);
+  if (!src || !dst) return fail(QWEN3_ERR_INVALID_ARG, "src / dst is NULL");
+  if (misaligned16({src, dst})) return fail(QWEN3_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  if (rows < 16 || rows % 16 != 0 || cols < 32 || cols % 32 != 0)
+    return fail(QWEN3_ERR_UNSUPPORTED, "rows (%d) must be a positive multiple of 16 and cols (%d) of 32", rows, cols);
+  {
+    const size_t n = static_cast<size_t>(rows) * cols;
+    const char* a = static_cast<const char*>(src);
+    const char* b = static_cast<const char*>(dst);
+    if (a < b + 2 * n && b < a + n * dsize(src_dtype)) return fail(QWEN3_ERR_INVALID_ARG, "dst overlaps src");
+  }
+  KTimer t("tile_weights", static_cast<hipStream_t>(stream));
+  const hipError_t e = q3::launch_tile_matrix(src, src_dtype, rows, cols, static_cast<uint16_t*>(dst),
+                                              static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? QWEN3_OK : hip_fail(e, "tile_weights launch");
 }
 
 int rms_norm_rows(const float* x, const void* w, void* y, int32_t rows, int32_t hidden, float eps,
@@ -1138,7 +1178,8 @@ static int layer_decode_impl(const qwen3_layer_cfg* cfg, const LayerW& w, const 
     return fail(QWEN3_ERR_WORKSPACE, "workspace must be 256-byte aligned");
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const qwen3_dtype wdt = cfg->wdtype, cdt = cfg->act_dtype;
+  const qwen3_dtype wdt = plain_w(cfg->wdtype), cdt = cfg->act_dtype;
+  const int wt = cfg->wdtype == QWEN3_F16_TILED;   // dense matrices tiled (quantized ones never are)
   const int H = cfg->hidden, nh = cfg->n_heads, nkv = cfg->n_kv_heads, hd = cfg->head_dim, F = cfg->ffn;
   const int q_dim = nh * hd, kv_dim = nkv * hd, qkv_dim = q_dim + 2 * kv_dim;
   char* ws = static_cast<char*>(workspace);
@@ -1156,6 +1197,7 @@ static int layer_decode_impl(const qwen3_layer_cfg* cfg, const LayerW& w, const 
     const MatW* g[3] = {&w.wq, &w.wk, &w.wv};
     q3::GemvParams p{nullptr, nullptr, nullptr, q_dim, q_dim + kv_dim, fold_norm ? x_in : xn, qkv, nullptr,
                      qkv_dim, H};
+    p.w_tiled = wt;
     if (fold_norm) {
       p.norm_w = w.attn_norm;
       p.norm_dt = wdt;
@@ -1186,12 +1228,14 @@ static int layer_decode_impl(const qwen3_layer_cfg* cfg, const LayerW& w, const 
   {
     const MatW* g[1] = {&w.wo};
     q3::GemvParams p{nullptr, nullptr, nullptr, H, H, o, x_out, x_in, H, q_dim};
+    p.w_tiled = wt;
     if ((st = run_gemv("gemv_o_resid", g, 1, p, q3::GV_RESID, wdt, s))) return st;
   }
   if (!fold_norm && (st = run_rmsnorm(x_out, w.ffn_norm, wdt, xn, QWEN3_F32, 1, H, cfg->rms_eps, s))) return st;
   {
     const MatW* g[2] = {&w.wg, &w.wu};
     q3::GemvParams p{nullptr, nullptr, nullptr, F, F, fold_norm ? x_out : xn, act, nullptr, F, H};
+    p.w_tiled = wt;
     if (fold_norm) {
       p.norm_w = w.ffn_norm;
       p.norm_dt = wdt;
@@ -1202,6 +1246,7 @@ static int layer_decode_impl(const qwen3_layer_cfg* cfg, const LayerW& w, const 
   {
     const MatW* g[1] = {&w.wd};
     q3::GemvParams p{nullptr, nullptr, nullptr, H, H, act, x_out, x_out, H, F};
+    p.w_tiled = wt;
     if ((st = run_gemv("gemv_down_resid", g, 1, p, q3::GV_RESID, wdt, s))) return st;
   }
   return QWEN3_OK;

@@ -358,17 +358,23 @@ __global__ __launch_bounds__(256) void gemv_epi_kernel(GemvParams p) {
   // the workgroup's four waves share the same rows and split K: wave w takes the 8-element
   // chunks w*64 + lane, (w + 4)*64 + lane, ...
   const int r0 = blockIdx.x * kGvRows;
+  // byte offset of row rr: row-major rr * K, or tiled (16-row groups of 32-column tiles): the
+  // group's base plus 32 elements per row inside it; element i of a row then sits at i
+  // (row-major) or (i / 32) * 512 + i % 32 (tiled) from there
+  auto row_off = [&](int rr) -> int64_t {
+    return (p.w_tiled ? static_cast<int64_t>(rr >> 4) * 16 * p.K + (rr & 15) * 32 : static_cast<int64_t>(rr) * p.K) * ES;
+  };
   const char* rowp[NR];
 #pragma unroll
   for (int j = 0; j < kGvRows; ++j) {
     const int r = min(r0 + j, p.rows - 1);  // rows past the end repeat the last (never stored)
     if (EPI == GV_SWIGLU) {
-      rowp[j] = static_cast<const char*>(p.W0) + static_cast<int64_t>(r) * p.K * ES;
-      rowp[kGvRows + j] = static_cast<const char*>(p.W1) + static_cast<int64_t>(r) * p.K * ES;
+      rowp[j] = static_cast<const char*>(p.W0) + row_off(r);
+      rowp[kGvRows + j] = static_cast<const char*>(p.W1) + row_off(r);
     } else {
       const void* W = r < p.nseg0 ? p.W0 : r < p.nseg1 ? p.W1 : p.W2;
       const int rr = r < p.nseg0 ? r : r < p.nseg1 ? r - p.nseg0 : r - p.nseg1;
-      rowp[j] = static_cast<const char*>(W) + static_cast<int64_t>(rr) * p.K * ES;
+      rowp[j] = static_cast<const char*>(W) + row_off(rr);
     }
   }
   float acc[NR];
@@ -385,8 +391,9 @@ __global__ __launch_bounds__(256) void gemv_epi_kernel(GemvParams p) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int i = min(i0 + u * STEP, p.K - 8);   // chunks past the end repeat the last, weighted 0
+      const int wi = p.w_tiled ? ((i >> 5) << 9) + (i & 31) : i;
 #pragma unroll
-      for (int j = 0; j < NR; ++j) w[u][j] = load_raw8<DT>(rowp[j], i);
+      for (int j = 0; j < NR; ++j) w[u][j] = load_raw8<DT>(rowp[j], wi);
       load8<DT_F32>(p.x, i, xv[u]);
       if (i0 + u * STEP >= p.K) {
 #pragma unroll
@@ -457,6 +464,9 @@ static hipError_t gemv_dt(const GemvParams& p, int dt, unsigned blocks, hipStrea
 hipError_t launch_gemv(const GemvParams& p, int epi, int wdt, hipStream_t s) {
   if (p.rows <= 0) return hipSuccess;
   if (p.K % 8 != 0 || p.K <= 0) return hipErrorInvalidValue;
+  // tiled weights: 16-bit, K a multiple of 32, every segment a whole number of row groups
+  if (p.w_tiled && (wdt == DT_F32 || p.K % 32 != 0 || p.nseg0 % 16 != 0 || p.nseg1 % 16 != 0 || p.rows % 16 != 0))
+    return hipErrorInvalidValue;
   const unsigned blocks = static_cast<unsigned>((p.rows + kGvRows - 1) / kGvRows);
   if (epi == GV_STORE) return gemv_dt<GV_STORE>(p, wdt, blocks, s);
   if (epi == GV_RESID) return gemv_dt<GV_RESID>(p, wdt, blocks, s);

@@ -11,10 +11,21 @@ namespace q3 {
 // Element storage types; the values match qwen3_dtype in the public header.
 enum DType : int { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
 
+// Tiled 16-bit matrix layout: a [R, C] matrix (R a multiple of 16, C of 32) as 16-row x
+// 32-column tiles of 1 KiB each, row-major inside a tile, tiles ordered by row group and then
+// by column: element (r, c) sits at ((r / 16) * (C / 32) + c / 32) * 512 + (r % 16) * 32 + c % 32.
+// One 32-wide K step of 16 operand rows is then a single contiguous 1 KiB block.
+__host__ __device__ constexpr int64_t tiled_index(int64_t r, int64_t c, int64_t C) {
+  return ((r >> 4) * (C >> 5) + (c >> 5)) * 512 + (r & 15) * 32 + (c & 31);
+}
+// src [rows, cols] row-major (src_dt) -> dst fp16 in the tiled layout, rounded to nearest even.
+hipError_t launch_tile_matrix(const void* src, int src_dt, int rows, int cols, uint16_t* dst, hipStream_t s);
+
 // ---- RMSNorm (a row per workgroup) -------------------------------------------------------
-// y[r] = x[r] * rsqrt(mean(x[r]^2) + eps) * w; x f32 [rows, H]; w and y of the given types.
+// y[r] = x[r] * rsqrt(mean(x[r]^2) + eps) * w; x f32 [rows, H]; w and y of the given types;
+// y_tiled: y (16-bit) in the tiled layout over ceil(rows / 16) * 16 rows (padding rows untouched).
 hipError_t launch_rmsnorm(const float* x, const void* w, int w_dt, void* y, int y_dt, int rows,
-                          int hidden, float eps, hipStream_t s);
+                          int hidden, float eps, hipStream_t s, bool y_tiled = false);
 
 // ---- DeepStack rows add -------------------------------------------------------------------
 // y[rows[i], :] += ds[i, :] for i < n; rows is a device copy of a host-checked list (strictly
@@ -85,6 +96,7 @@ struct GemvParams {
   const void* norm_w = nullptr;
   int norm_dt = 0;
   float eps = 0.f;
+  int w_tiled = 0;     // dense 16-bit weights in the tiled layout (rows and K as given)
 };
 hipError_t launch_gemv(const GemvParams& p, int epi, int wdt, hipStream_t s);
 
@@ -147,6 +159,10 @@ struct GemmParams {
   const float* R;      // EPI_STORE_F32 only: residual added to the product, or nullptr
   int64_t ldr;
   int M, N, K;         // N: product columns (for SwiGLU, 2F: gate and up together)
+  // Tiled operands (16-bit, the tiled layout; ld must equal the row length): a_tiled: A over
+  // ceil(M / 16) * 16 rows, lda == K (rows past M are read and their products discarded);
+  // b_tiled: every B segment, ldb == K; c_tiled: the EPI_SWIGLU_16 output, ldc == N / 2.
+  int a_tiled = 0, b_tiled = 0, c_tiled = 0;
 };
 // op: OPH_BF16 or OPH_F16, the format of A, of the MFMA and of 16-bit outputs. b_bf16: B is
 // stored as bf16 (converted to fp16 on the way to LDS when op is fp16); otherwise B is in op's
@@ -167,6 +183,7 @@ struct AttnParams {
   float scale_log2;    // softmax scale * log2(e)
   int head_dim;        // 64 or 128
   int causal;          // 1: key j <= query s; 0: every key (bidirectional)
+  int o_tiled = 0;     // o in the tiled layout over o_stride columns (rows padded to 16)
 };
 hipError_t launch_attention_mfma(const AttnParams& p, int op, hipStream_t s);
 

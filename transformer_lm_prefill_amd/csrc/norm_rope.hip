@@ -51,8 +51,11 @@ template <int W_DT, int Y_DT, int NV, bool FULL>
 __global__ __launch_bounds__(kNormThreads) void rmsnorm_stream_kernel(const float* __restrict__ x,
                                                                       const void* __restrict__ w,
                                                                       void* __restrict__ y, int rows,
-                                                                      int hidden, float eps) {
+                                                                      int hidden, float eps, int tiled) {
   const int nv = hidden >> 2;
+  // output index of float4 c of a row (4-element units): row-major row * nv + c; tiled (16-bit
+  // y): the row's base inside its 16-row group plus 128 per 32 columns
+  const int c_ks = tiled ? 128 : 8;
   f32x4 g[NV], cur[NV], nxt[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
@@ -90,13 +93,15 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_stream_kernel(const floa
 #pragma unroll
     for (int i = 0; i < kNormThreads / 64; ++i) tot += red[it & 1][i];
     const float r = 1.0f / sqrtf(tot / static_cast<float>(hidden) + eps);
+    const int64_t y_row = tiled ? static_cast<int64_t>(row >> 4) * 4 * hidden + (row & 15) * 8
+                                : static_cast<int64_t>(row) * nv;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int c = threadIdx.x + i * kNormThreads;
       if (FULL || c < nv) {
         const f32x4 o = {cur[i][0] * r * g[i][0], cur[i][1] * r * g[i][1], cur[i][2] * r * g[i][2],
                          cur[i][3] * r * g[i][3]};
-        store4<Y_DT>(y, static_cast<int64_t>(row) * nv + c, o);
+        store4<Y_DT>(y, y_row + (c >> 3) * c_ks + (c & 7), o);
       }
     }
 #pragma unroll
@@ -106,14 +111,14 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_stream_kernel(const floa
 
 template <int W_DT, int Y_DT>
 static void rms_launch_k(const float* x, const void* w, void* y, int rows, int hidden, float eps,
-                         hipStream_t s) {
+                         int tiled, hipStream_t s) {
   const int grid = rows < kNormGrid ? rows : kNormGrid;
   auto go = [&](auto nv) {
     constexpr int NV = decltype(nv)::value;
     if (hidden == 4 * kNormThreads * NV)
-      rmsnorm_stream_kernel<W_DT, Y_DT, NV, true><<<grid, kNormThreads, 0, s>>>(x, w, y, rows, hidden, eps);
+      rmsnorm_stream_kernel<W_DT, Y_DT, NV, true><<<grid, kNormThreads, 0, s>>>(x, w, y, rows, hidden, eps, tiled);
     else
-      rmsnorm_stream_kernel<W_DT, Y_DT, NV, false><<<grid, kNormThreads, 0, s>>>(x, w, y, rows, hidden, eps);
+      rmsnorm_stream_kernel<W_DT, Y_DT, NV, false><<<grid, kNormThreads, 0, s>>>(x, w, y, rows, hidden, eps, tiled);
   };
   if (hidden <= 4 * kNormThreads * 4) go(std::integral_constant<int, 4>{});
   else if (hidden <= 4 * kNormThreads * 8) go(std::integral_constant<int, 8>{});
@@ -122,24 +127,26 @@ static void rms_launch_k(const float* x, const void* w, void* y, int rows, int h
 
 template <int W_DT>
 static hipError_t rms_launch_y(const float* x, const void* w, void* y, int y_dt, int rows, int hidden,
-                               float eps, hipStream_t s) {
+                               float eps, int tiled, hipStream_t s) {
   switch (y_dt) {
-    case DT_F32: rms_launch_k<W_DT, DT_F32>(x, w, y, rows, hidden, eps, s); break;
-    case DT_BF16: rms_launch_k<W_DT, DT_BF16>(x, w, y, rows, hidden, eps, s); break;
-    case DT_F16: rms_launch_k<W_DT, DT_F16>(x, w, y, rows, hidden, eps, s); break;
+    case DT_F32: rms_launch_k<W_DT, DT_F32>(x, w, y, rows, hidden, eps, 0, s); break;
+    case DT_BF16: rms_launch_k<W_DT, DT_BF16>(x, w, y, rows, hidden, eps, tiled, s); break;
+    case DT_F16: rms_launch_k<W_DT, DT_F16>(x, w, y, rows, hidden, eps, tiled, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_rmsnorm(const float* x, const void* w, int w_dt, void* y, int y_dt, int rows,
-                          int hidden, float eps, hipStream_t s) {
+                          int hidden, float eps, hipStream_t s, bool y_tiled) {
   if (rows <= 0) return hipSuccess;
   if (hidden % 4 != 0 || hidden > 4 * kNormThreads * kNormMaxVec) return hipErrorInvalidValue;
+  if (y_tiled && (y_dt == DT_F32 || hidden % 32 != 0)) return hipErrorInvalidValue;
+  const int t = y_tiled ? 1 : 0;
   switch (w_dt) {
-    case DT_F32: return rms_launch_y<DT_F32>(x, w, y, y_dt, rows, hidden, eps, s);
-    case DT_BF16: return rms_launch_y<DT_BF16>(x, w, y, y_dt, rows, hidden, eps, s);
-    case DT_F16: return rms_launch_y<DT_F16>(x, w, y, y_dt, rows, hidden, eps, s);
+    case DT_F32: return rms_launch_y<DT_F32>(x, w, y, y_dt, rows, hidden, eps, t, s);
+    case DT_BF16: return rms_launch_y<DT_BF16>(x, w, y, y_dt, rows, hidden, eps, t, s);
+    case DT_F16: return rms_launch_y<DT_F16>(x, w, y, y_dt, rows, hidden, eps, t, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -28,7 +28,8 @@ class LayerSpec:
     eps: float = 1e-6
     theta: float = 5e6
     sections: tuple = (24, 20, 20)
-    dtype: str = "bf16"      # weights: "bf16", "f16" or "f32"
+    dtype: str = "bf16"      # weights: "bf16", "f16", "f32", or "f16t": fp16 with the seven
+                             # projection matrices in the tiled layout (tile_weights)
     act: str = ""            # matrix-product operands: "f16", "bf16" or "f32"; "" = f16 for
                              # 16-bit weights, f32 for f32 weights
 
@@ -45,8 +46,11 @@ class LayerSpec:
         return "f32" if self.dtype == "f32" else "f16"
 
 
-_CODES = {"f32": _lib.QWEN3_F32, "bf16": _lib.QWEN3_BF16, "f16": _lib.QWEN3_F16}
-TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+_CODES = {"f32": _lib.QWEN3_F32, "bf16": _lib.QWEN3_BF16, "f16": _lib.QWEN3_F16,
+          "f16t": _lib.QWEN3_F16_TILED}
+TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16, "f16t": torch.float16}
+# the seven projection matrices (tiled under "f16t"; the vectors stay plain)
+MATRIX_NAMES = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
 
 
 def _dt(t):
@@ -477,8 +481,9 @@ def apply_rope_tables(x, cos, sin, pairing="split"):
 
 
 def swiglu_ffn(x_normed, w_gate, w_up, w_down, residual=None, out_dtype=torch.float32, out=None,
-               workspace=None):
-    """out [S, H] = [residual +] (silu(x Wg^T) * (x Wu^T)) Wd^T."""
+               workspace=None, weights_tiled=False):
+    """out [S, H] = [residual +] (silu(x Wg^T) * (x Wu^T)) Wd^T. weights_tiled: the three
+    matrices come from tile_weights (wdtype QWEN3_F16_TILED)."""
     lib = _lib.load()
     s, h = x_normed.shape
     f = w_gate.shape[0]
@@ -488,10 +493,32 @@ def swiglu_ffn(x_normed, w_gate, w_up, w_down, residual=None, out_dtype=torch.fl
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x_normed.device)
     _lib.check(lib.swiglu_ffn(_ptr(x_normed), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
-                              _ptr(residual), _ptr(out), int(s), int(h), int(f), _dt(w_gate),
+                              _ptr(residual), _ptr(out), int(s), int(h), int(f),
+                              _lib.QWEN3_F16_TILED if weights_tiled else _dt(w_gate),
                               _dt(x_normed), _dt(out), _ptr(workspace), int(workspace.numel()),
                               _stream()))
     return out
+
+
+def tile_weights(w, out=None):
+    """qwen3_tile_weights: a [rows, cols] matrix (f32, bf16 or f16 on the GPU) as fp16 in the
+    tiled layout (16-row x 32-column tiles of 1 KiB; element (r, c) at ((r // 16) * (cols // 32)
+    + c // 32) * 512 + (r % 16) * 32 + c % 32). The result is a float16 tensor of the same
+    shape whose memory holds that order: pass it only where a tiled matrix is expected."""
+    if w.dim() != 2:
+        raise ValueError("tile_weights takes a 2-D matrix")
+    rows, cols = w.shape
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.float16, device=w.device)
+    _lib.check(_lib.load().qwen3_tile_weights(_ptr(w), _dt(w), int(rows), int(cols), _ptr(out), _stream()))
+    return out
+
+
+def tile_layer_weights(weights):
+    """The eleven weights of a layer prepared for dtype "f16t": projection matrices tiled,
+    vectors converted to plain fp16."""
+    return {n: tile_weights(t) if n in MATRIX_NAMES else t.to(torch.float16).contiguous()
+            for n, t in weights.items()}
 
 
 def rms_norm_rows(x, w, eps, out_dtype=torch.bfloat16, out=None):
