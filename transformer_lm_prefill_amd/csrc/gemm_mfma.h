@@ -215,21 +215,30 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p,
   const int col_in_blk = lane & 31;
   const int row_base = tm * kBM + wm * (32 * MI) + 4 * (lane >> 5);
   if (EPI == EPI_SWIGLU_16) {
-    uint16_t* C = static_cast<uint16_t*>(p.C);
+    // Row row_base + mi*32 + 8*(e/4) + e%4 (row_base % 16 is 0 or 4, so no offset below
+    // carries into the next 16-row group) and column f0 + ni*32 (f0 % 32 = the lane's column):
+    // the element offset is a per-lane base plus a constant multiple of ldc plus a constant.
+    static_assert((32 * MI) % 16 == 0, "row groups");
+    const int f0 = tn * (BN / 2) + wn * (16 * NI) + col_in_blk;
+    uint16_t* C = static_cast<uint16_t*>(p.C) + c_row(row_base) + c_col(f0);
+    auto off = [&](int mi, int ni, int e) -> int64_t {
+      if (CT)
+        return static_cast<int64_t>(2 * mi + (e >> 3)) * 16 * p.ldc + (8 * ((e >> 2) & 1) + (e & 3)) * 32 + ni * 512;
+      return static_cast<int64_t>(mi * 32 + 8 * (e >> 2) + (e & 3)) * p.ldc + ni * 32;
+    };
     // tiles wholly inside M (all but a ragged last row of tiles) store without per-row checks
     auto store_all = [&](auto check) {
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
         for (int ni = 0; ni < NI / 2; ++ni) {
-          const int f = tn * (BN / 2) + wn * (16 * NI) + ni * 32 + col_in_blk;
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const int m = row_base + mi * 32 + 8 * (e >> 2) + (e & 3);
             if (!check.value || m < p.M) {
               const float g = acc[mi][ni][e];
               const float u = acc[mi][ni + NI / 2][e];
-              C[c_row(m) + c_col(f)] = F::from_f32(silu_f(g) * u);
+              C[off(mi, ni, e)] = F::from_f32(silu_f(g) * u);
             }
           }
         }
@@ -463,13 +472,16 @@ void gemm_d2l_kernel(const GemmParams p) {
     }
 #pragma unroll
     for (int j = 0; j < BJ; ++j) {
-      int slot = (wave + j * WAVES) * 64 + lane;
+      const int blk = wave + j * WAVES;
+      int slot = blk * 64 + lane;
       if (slot >= BSLOT) slot = lane;  // sink load: a valid row
       const int row = slot >> 2;
-      const int row0 = slot & ~63;     // first tile row of this load's 16, times 4
+      // first tile row of this load's 16, from wave-uniform values only: the segment base
+      // then is provably uniform and its buffer descriptor needs no per-lane loop
+      const int row0 = blk * 64 < BSLOT ? blk * 16 : 0;
       const uint16_t* base;
       int idx0, rows;
-      b_seg<BN, WN, EPI>(p, itn, row0 >> 2, base, idx0, rows);
+      b_seg<BN, WN, EPI>(p, itn, row0, base, idx0, rows);
       // tiled B: a load's 16 rows are one row group of one segment (the host checks that
       // segment bounds are multiples of 16)
       b_src[j] = TB ? base + static_cast<int64_t>(idx0 >> 4) * 16 * p.K + tile_pos(lane) * 8
