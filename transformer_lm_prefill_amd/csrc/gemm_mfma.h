@@ -246,19 +246,22 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p,
     if (tm * kBM + kBM <= p.M) store_all(std::false_type{});
     else store_all(std::true_type{});
   } else {
+    // as above: a per-lane base (row row_base, column n0) plus constant multiples of ldc
+    const int n0 = tn * BN + wn * 32 * NI + col_in_blk;
+    uint16_t* C16 = static_cast<uint16_t*>(p.C) + static_cast<int64_t>(row_base) * p.ldc + n0;
     auto store_all = [&](auto check) {
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) {
-          const int n = tn * BN + wn * 32 * NI + ni * 32 + col_in_blk;
+          const int n = n0 + ni * 32;
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const int m = row_base + mi * 32 + 8 * (e >> 2) + (e & 3);
             if (!check.value || m < p.M) {
               const float v = acc[mi][ni][e];
               if (EPI == EPI_STORE_16) {
-                static_cast<uint16_t*>(p.C)[static_cast<int64_t>(m) * p.ldc + n] = F::from_f32(v);
+                C16[static_cast<int64_t>(mi * 32 + 8 * (e >> 2) + (e & 3)) * p.ldc + ni * 32] = F::from_f32(v);
               } else {
                 float r = 0.f;
                 if (p.R) r = p.R[static_cast<int64_t>(m) * p.ldr + n];
