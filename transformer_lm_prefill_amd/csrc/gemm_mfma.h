@@ -73,6 +73,10 @@
 #ifndef Q3_GEMM_LDS_EPI
 #define Q3_GEMM_LDS_EPI 1
 #endif
+// 1: one-tile fp32-residual products take the residual in chunks during their first K steps
+#ifndef Q3_GEMM_RSTREAM
+#define Q3_GEMM_RSTREAM 1
+#endif
 
 namespace q3 {
 
@@ -514,7 +518,28 @@ void gemm_d2l_kernel(const GemmParams p) {
   // here, behind the ring's first tile loads, so the epilogue only stores; rows past M load a
   // clamped valid row and are never stored
   const bool rin = TRANS && p.R != nullptr;
-  if (rin) {
+  // RS: a one-tile workgroup with enough K steps takes the residual in MI * NI chunks (one
+  // 32 x 32 accumulator block each) during its first groups of K steps instead of before them,
+  // so a launch's residual reads (all workgroups at once) spread over the K loop instead of
+  // stalling the first MFMA; the sum is the same up to the order of fp32 additions
+  // (instantiated for the layer's products only: buffer loads, tiled activations)
+  constexpr bool RS_OK = Q3_GEMM_RSTREAM && TRANS && EPI == EPI_STORE_F32 && BUF && TA;
+  constexpr int RS_GAP = 2;  // groups of NS steps from one chunk to the next
+  const bool rs = RS_OK && rin && my_tiles == 1 && p.K / kBK2 >= NS * RS_GAP * MI * NI;
+  // C^T layout of the residual: lane l, elements 4q..4q+3 of block (mi, ni) = R[row l%32 of
+  // block mi][4 columns 8q + 4*(l/32) ..]; rows past M read a clamped valid row (never stored)
+  auto r_load = [&](int mi, int ni, f32x16& dst) __attribute__((always_inline)) {
+    const int c4 = 4 * (lane >> 5);
+    const int row = min(tm * kBM + wm * (32 * MI) + mi * 32 + (lane & 31), p.M - 1);
+    const float* rr = p.R + static_cast<int64_t>(row) * p.ldr;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 r = *reinterpret_cast<const f32x4*>(rr + tn * BN + wn * 32 * NI + ni * 32 + 8 * q + c4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[4 * q + e] = r[e];
+    }
+  };
+  if (rin && !rs) {
     const int c4 = 4 * (lane >> 5);
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
@@ -702,23 +727,36 @@ void gemm_d2l_kernel(const GemmParams p) {
   // its reads of stage kt-1), refill stage kt-1's buffer with step kt+NS-1, then the two
   // 16-wide sub-steps; the second one reads sub-step 0 of step kt+1, so the MFMAs after the
   // next barrier start on operands already in registers.
-  auto step = [&](auto u_c, int g) __attribute__((always_inline)) {
+  // RS chunk in flight: loaded at step u = 0 of a group (after its tile requests), 4 loads per
+  // lane; steps 1 and 2 of the group let them stay outstanding, step 3 waits for them (they
+  // are older than the stage it waits for) and adds them
+  f32x16 rtmp;
+  constexpr int RL = 4;
+  static_assert(NS == 4, "residual streaming assumes a 4-stage ring");
+  auto step = [&](auto u_c, int g, auto rc_c) __attribute__((always_inline)) {
     constexpr int u = decltype(u_c)::value;
+    constexpr int rc = decltype(rc_c)::value;  // residual block mi * NI + ni of this group, or -1
     // own loads of stage u+1 landed (stages u+2 .. u+NS-2 may still be in flight)
     constexpr int WN1 = [&]() constexpr {
       int n = 0;
       for (int k = 2; k <= NS - 2; ++k) n += lps((u + k) % NS);
       return n;
-    }();
+    }() + ((rc >= 0 && (u == 1 || u == 2)) ? RL : 0);
     wait_vm(std::integral_constant<int, WN1>{});
+    if constexpr (rc >= 0 && u == NS - 1) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[rc / NI][rc % NI][e] += rtmp[e];
+    }
     convert_own((u + 1) % NS);
     barrier();
     issue((u + NS - 1) % NS, g + NS - 1);
+    if constexpr (rc >= 0 && u == 0) r_load(rc / NI, rc % NI, rtmp);
     fread(u, 1, 1);
     mfmas(0);
     fread((u + 1) % NS, 0, 0);
     mfmas(1);
   };
+  using NoR = std::integral_constant<int, -1>;
   // Whole groups of NS steps without any branch (stage indices are constants after unrolling),
   // then the remaining steps (one-tile launches whose K steps are not a multiple of NS). With
   // several tiles per workgroup (NS divides a tile's K steps, so every tile ends with a group),
@@ -726,8 +764,19 @@ void gemm_d2l_kernel(const GemmParams p) {
   // fragments are already in registers and its first stages are on their way.
   int g = 0;
   int done = 0, cur = 0;
+  if constexpr (RS_OK) {
+    if (rs) {
+      // chunk c in group c * RS_GAP, plain groups in between
+      static_for<MI * NI>([&](auto c_c) __attribute__((always_inline)) {
+        static_for<NS>([&](auto u_c) __attribute__((always_inline)) { step(u_c, g + decltype(u_c)::value, c_c); });
+        g += NS;
+        for (int k = 1; k < RS_GAP; ++k, g += NS)
+          static_for<NS>([&](auto u_c) __attribute__((always_inline)) { step(u_c, g + decltype(u_c)::value, NoR{}); });
+      });
+    }
+  }
   for (; g + NS <= total; g += NS) {
-    static_for<NS>([&](auto u_c) __attribute__((always_inline)) { step(u_c, g + decltype(u_c)::value); });
+    static_for<NS>([&](auto u_c) __attribute__((always_inline)) { step(u_c, g + decltype(u_c)::value, NoR{}); });
     if constexpr (EPI == EPI_SWIGLU_16) {
       const bool tile_end = my_tiles > 1 && done + NS == nk;
       if (my_tiles > 1) done += NS;
@@ -748,7 +797,7 @@ void gemm_d2l_kernel(const GemmParams p) {
     }
   }
   static_for<NS - 1>([&](auto u_c) __attribute__((always_inline)) {
-    if (g + decltype(u_c)::value < total) step(u_c, g + decltype(u_c)::value);
+    if (g + decltype(u_c)::value < total) step(u_c, g + decltype(u_c)::value, NoR{});
   });
 
   // the trailing reloads of the last tile must land before this workgroup's LDS is released
