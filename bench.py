@@ -104,22 +104,23 @@ def cpu_baseline(cfg, w0, x, pos, n_tok, min_s=10.0, max_reps=8):
                       f"(float64 numpy oracle, {dt:.1f} s)"}
 
 
-def model_prefill_extra(cfg, layers, pos, stream, vocab):
+def model_prefill_extra(cfg, layers, pos, stream, vocab, spec=None):
     """The whole-model path on the same layers: embedding lookup, the layer stack, final
     RMSNorm and an untied LM head over `vocab` rows, for the last position's logits. Weights of
-    the embedding table and head are seeded random (torch generator) of the layer dtype."""
+    the embedding table and head are seeded random (torch generator) in the layers' element
+    type (fp16 for tiled layers)."""
     import torch
 
     import transformer_lm_prefill_amd as q3
     dev = torch.device("cuda:0")
     g = torch.Generator(device=dev)
     g.manual_seed(1234)
-    wdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    spec = spec or q3.LayerSpec.of(cfg)
+    wdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f16t": torch.float16, "f32": torch.float32}[spec.dtype]
     emb = (torch.randn(vocab, cfg.hidden, device=dev, generator=g) * 0.02).to(wdt)
     head = (torch.randn(vocab, cfg.hidden, device=dev, generator=g) * 0.02).to(wdt)
     norm = (1 + 0.1 * torch.randn(cfg.hidden, device=dev, generator=g)).to(wdt)
     tokens = torch.randint(0, vocab, (cfg.seq_len,), generator=torch.Generator().manual_seed(5)).tolist()
-    spec = q3.LayerSpec.of(cfg)
     ws = torch.empty(q3.model_workspace_bytes(spec, len(layers), vocab, cfg.seq_len), dtype=torch.uint8,
                      device=dev)
     out = torch.empty(vocab, dtype=torch.float32, device=dev)
@@ -141,7 +142,7 @@ def model_prefill_extra(cfg, layers, pos, stream, vocab):
     kt = q3.timing_collect()
     q3.timing_enable(False)
     head_ms = kt["lm_head"][1] / kt["lm_head"][0]
-    head_bytes = vocab * cfg.hidden * (2 if wdt == torch.bfloat16 else 4)
+    head_bytes = vocab * cfg.hidden * (4 if wdt == torch.float32 else 2)
     emb_ms = kt["embed_gather"][1] / kt["embed_gather"][0]
 
     # generation after the prompt: the prefill leaves every layer's cache, then single tokens
@@ -165,6 +166,7 @@ def model_prefill_extra(cfg, layers, pos, stream, vocab):
     torch.cuda.synchronize()
     dec_ms = (time.perf_counter() - t) * 1e3 / n_dec
     return {"workload": f"{cfg.name}: {len(layers)} layers, seq {cfg.seq_len}, vocab {vocab} untied head",
+            "weights": spec.dtype,
             "ms": round(ms, 4), "tokens_per_s": round(cfg.seq_len / (ms * 1e-3), 1),
             "lm_head": {"avg_ms": round(head_ms, 4), "bound": "hbm",
                         "GB_per_s": round(head_bytes / (head_ms * 1e-3) / 1e9, 1),
@@ -319,7 +321,8 @@ def quant_extra(cfg, x0, pos, n_tokens=16):
     dev = torch.device("cuda:0")
     S = cfg.seq_len
     norms, proj = synth.make_quant_layer_weights(cfg, 0)
-    wdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    spec = spec or q3.LayerSpec.of(cfg)
+    wdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f16t": torch.float16, "f32": torch.float32}[spec.dtype]
     dn = {n: torch.from_numpy(a).to(dev).to(wdt) for n, a in norms.items()}
     dp = {n: (f, torch.from_numpy(np.ascontiguousarray(d)).to(dev), None) for n, (f, d, _) in proj.items()}
     qbytes = {n: d.numel() for n, (_, d, _) in dp.items()}
@@ -648,10 +651,11 @@ def main():
 
     bf16_in_kernel = extra(cfg.dtype != "bf16", as_given)
     f16_row_major = extra(cfg.dtype != "bf16", row_major_f16)
+    # the whole model on the headline's weights (tiled layers; its decode steps read them too)
+    model = extra(args.no_model, model_prefill_extra, cfg, prepared, pos, None, args.vocab, spec_run)
     del prepared
     peaks = extra(False, measured_peaks)
     streaming = extra(False, streaming_rotated, cfg)
-    model = extra(args.no_model, model_prefill_extra, cfg, layers, pos, None, args.vocab)
     bidir = extra(args.no_bidirectional, bidirectional_extra)
     decode = extra(args.no_decode, decode_extra, cfg, layers, x0, pos)
     quant = extra(args.no_quant, quant_extra, cfg, x0, pos)

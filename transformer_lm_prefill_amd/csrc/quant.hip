@@ -29,15 +29,18 @@ typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
 
 // ---- expansion to the operand format -----------------------------------------------------------
 // Workgroup = 256 consecutive blocks: their 4608 bytes come in with coalesced dword loads into
-// LDS, thread t expands block t into an LDS tile of 16-bit weights, and the 16 KB tile leaves
-// with coalesced 16-byte stores. (Blocks are 18 bytes, so a thread reading its own block from
+// LDS, thread t expands block t into an LDS tile of 16-bit weights (rows padded against bank
+// conflicts), and the 16 KB of weights leave with coalesced 16-byte stores. (Blocks are 18 bytes, so a thread reading its own block from
 // global memory would issue nine 2-byte loads at an 18-byte lane stride.)
 constexpr int kDqBlocks = 256;
 
 template <int ODT>
 __global__ __launch_bounds__(256) void dequant_q4_0_kernel(const uint8_t* blocks, int64_t nblocks, void* out) {
+  // tile rows padded from 64 to 80 bytes: 8 consecutive threads' 16-byte stores then start 20
+  // words apart, on distinct LDS banks
+  constexpr int kRow = 40;  // halfwords per padded tile row
   __shared__ __align__(16) uint32_t raw[kDqBlocks * 18 / 4];
-  __shared__ __align__(16) uint16_t tile[kDqBlocks * 32];
+  __shared__ __align__(16) uint16_t tile[kDqBlocks * kRow];
   const int tid = threadIdx.x;
   const int64_t b0 = static_cast<int64_t>(blockIdx.x) * kDqBlocks;
   const int nb = static_cast<int>(min<int64_t>(kDqBlocks, nblocks - b0));
@@ -62,7 +65,7 @@ __global__ __launch_bounds__(256) void dequant_q4_0_kernel(const uint8_t* blocks
         hi[2 * i + k] = d * static_cast<float>(static_cast<int>(byte >> 4) - 8);
       }
     }
-    uint16_t* t = tile + tid * 32;
+    uint16_t* t = tile + tid * kRow;
     store8<ODT>(t, 0, *reinterpret_cast<const float(*)[8]>(lo));
     store8<ODT>(t, 8, *reinterpret_cast<const float(*)[8]>(lo + 8));
     store8<ODT>(t, 16, *reinterpret_cast<const float(*)[8]>(hi));
@@ -71,7 +74,7 @@ __global__ __launch_bounds__(256) void dequant_q4_0_kernel(const uint8_t* blocks
   __syncthreads();
   u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + b0 * 32);
   const u32x4* from = reinterpret_cast<const u32x4*>(tile);
-  for (int i = tid; i < nb * 4; i += 256) dst[i] = from[i];
+  for (int i = tid; i < nb * 4; i += 256) dst[i] = from[(i >> 2) * (kRow / 8) + (i & 3)];
 }
 
 // Thread = 16 consecutive weights of one row (cols % 16 == 0).
