@@ -73,6 +73,10 @@
 #ifndef Q3_GEMM_LDS_EPI
 #define Q3_GEMM_LDS_EPI 1
 #endif
+// 1: each K step's fragment reads and MFMAs in fixed scheduling groups (see the step)
+#ifndef Q3_GEMM_SGG
+#define Q3_GEMM_SGG 1
+#endif
 // 1: one-tile fp32-residual products take the residual in chunks during their first K steps
 #ifndef Q3_GEMM_RSTREAM
 #define Q3_GEMM_RSTREAM 1
@@ -703,12 +707,20 @@ void gemm_d2l_kernel(const GemmParams p) {
                                ((decltype(n_vm)::value >> 4) << 14));
     asm volatile("" ::: "memory");
   };
-  auto barrier = [&]() {
+  // Workgroup barrier. With wait_lds, this thread's LDS accesses complete first (lgkmcnt(0)):
+  // needed where threads write LDS before it (converted or decoded weight tiles, the LDS
+  // epilogue). The ring's direct-to-LDS loads are covered by the vmcnt waits, and the fragment
+  // reads still in flight at a step's barrier are of stages no load will overwrite before the
+  // next barrier (their MFMAs wait for them), so the step barrier of a pure direct-to-LDS ring
+  // does not wait for them.
+  auto barrier = [&](auto wait_lds) {
     asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt((0x7 << 4) | 0xF | (0x3 << 14));  // lgkmcnt(0)
+    if constexpr (decltype(wait_lds)::value) __builtin_amdgcn_s_waitcnt((0x7 << 4) | 0xF | (0x3 << 14));  // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
+  constexpr bool LDS_W = STAGE_B || CVT_IN_LDS || BQ;  // threads write ring stages themselves
+  using WaitLds = std::integral_constant<bool, LDS_W>;
 
 #pragma unroll
   for (int st = 0; st < NS - 1; ++st) issue(st, st);
@@ -720,7 +732,7 @@ void gemm_d2l_kernel(const GemmParams p) {
   }();
   wait_vm(std::integral_constant<int, W0>{});
   convert_own(0);
-  barrier();  // stage 0 complete (and converted) everywhere
+  barrier(WaitLds{});  // stage 0 complete (and converted) everywhere
   fread(0, 0, 0);
   // Step kt (stage kt % NS): wait for this thread's loads of stage kt+1 (later stages may still
   // be in flight) and convert them, barrier (stage kt+1 complete everywhere; every wave is past
@@ -748,13 +760,22 @@ void gemm_d2l_kernel(const GemmParams p) {
       for (int e = 0; e < 16; ++e) acc[rc / NI][rc % NI][e] += rtmp[e];
     }
     convert_own((u + 1) % NS);
-    barrier();
+    barrier(WaitLds{});
     issue((u + NS - 1) % NS, g + NS - 1);
     if constexpr (rc >= 0 && u == 0) r_load(rc / NI, rc % NI, rtmp);
     fread(u, 1, 1);
     mfmas(0);
     fread((u + 1) % NS, 0, 0);
     mfmas(1);
+#if Q3_GEMM_SGG
+    // scheduling groups in source order: each sub-step's fragment reads are issued before the
+    // MFMAs of the other sub-step (the compiler otherwise moved them among those MFMAs, so the
+    // MFMAs right after them waited for LDS): QKV, o-proj and down ~2% faster
+    __builtin_amdgcn_sched_group_barrier(0x100, MI + NI, 0);   // DS reads
+    __builtin_amdgcn_sched_group_barrier(0x008, MI * NI, 0);   // MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, MI + NI, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, MI * NI, 0);
+#endif
   };
   using NoR = std::integral_constant<int, -1>;
   // Whole groups of NS steps without any branch (stage indices are constants after unrolling),
@@ -808,7 +829,7 @@ void gemm_d2l_kernel(const GemmParams p) {
     // fp32 output (residual already in the accumulators) through LDS: each wave owns one 16 KiB
     // ring array and stages half of its 128 x 64 block at a time (chunk of 4 columns XOR-permuted
     // by row), then writes whole 256-byte row segments (16 lanes per row)
-    barrier();  // every wave is past its last fragment reads of the ring
+    barrier(std::true_type{});  // every wave is past its last fragment reads of the ring
     u32x4* buf = wave == 0 ? sA0 : wave == 1 ? sA1 : wave == 2 ? sA2 : wave == 3 ? sA3
                : wave == 4 ? sB0 : wave == 5 ? sB1 : wave == 6 ? sB2 : sB3;
     float* C = static_cast<float*>(p.C);
