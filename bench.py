@@ -321,8 +321,7 @@ def quant_extra(cfg, x0, pos, n_tokens=16):
     dev = torch.device("cuda:0")
     S = cfg.seq_len
     norms, proj = synth.make_quant_layer_weights(cfg, 0)
-    spec = spec or q3.LayerSpec.of(cfg)
-    wdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f16t": torch.float16, "f32": torch.float32}[spec.dtype]
+    wdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     dn = {n: torch.from_numpy(a).to(dev).to(wdt) for n, a in norms.items()}
     dp = {n: (f, torch.from_numpy(np.ascontiguousarray(d)).to(dev), None) for n, (f, d, _) in proj.items()}
     qbytes = {n: d.numel() for n, (_, d, _) in dp.items()}

@@ -41,9 +41,10 @@
 //                             granules are stored in the order 0,2,1,3,4,6,5,7, so the two
 //                             granules an MFMA lane needs (4-key groups i and i+2 of the S^T
 //                             accumulator order) are adjacent: one 16-byte read.
-// Waves 0-3 stage K tiles, waves 4-7 V tiles (transposed on the way into LDS); the global
-// loads of tile t+1 (K) and t (V) are issued at the top of iteration t and written to LDS at
-// its end, into slots last read in iteration t-1.
+// Waves 0-3 stage K tiles, waves 4-7 V tiles (transposed on the way into LDS). Iteration t
+// writes K(t+1) and V(t) to LDS at its end, into slots last read in iteration t-1; their global
+// loads were issued one iteration earlier (K(t+2) and V(t+1) are requested at the top of
+// iteration t), into two register sets that alternate, so a load has a whole iteration to land.
 #include <cstdlib>
 #include <type_traits>
 
@@ -138,7 +139,10 @@ void attn_fwd_kernel(const AttnParams p) {
   const int vg = tv & 15, vc = tv >> 4;
   const bool v_active = vc < NCH;  // with HD = 64 waves 6 and 7 stage nothing (wave-uniform)
   const int vpos = vt_pos(vg);
-  u32x4 st[4];
+  // staging registers of the global loads, two sets: K(j) goes to set j % 2 and V(j) to set
+  // (j + 1) % 2 (so both roles request into, and store from, the same set in an iteration), and
+  // each is written to LDS one iteration after it was requested
+  u32x4 st0[4], st1[4];
   static_assert(KPT <= 4, "head_dim");
   // K / V rows come in through buffer loads when the operand's byte extent fits the 32-bit
   // range (BUF), with a per-lane 32-bit byte offset, so the loop carries no 64-bit address
@@ -158,7 +162,7 @@ void attn_fwd_kernel(const AttnParams p) {
   const int row_bytes = static_cast<int>(2 * row_elems);  // used only when BUF
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(gbase), static_cast<short>(0), p.S * row_bytes, 0x00020000);
-  auto gload = [&](int tile) {
+  auto gload = [&](int tile, u32x4 (&st)[4]) __attribute__((always_inline)) {
     if constexpr (BUF) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -178,7 +182,7 @@ void attn_fwd_kernel(const AttnParams p) {
       }
     }
   };
-  auto lstore = [&](int tile) {
+  auto lstore = [&](int tile, const u32x4 (&st)[4]) __attribute__((always_inline)) {
     if (k_loader) {
       u32x4* dst = Ks[tile & 1];
 #pragma unroll
@@ -238,15 +242,15 @@ void attn_fwd_kernel(const AttnParams p) {
   };
 
   // one iteration: tile t into sc; sp holds S(t-1) (unless first)
-  auto iter = [&](int t, f32x16 (&sc)[2], f32x16 (&sp)[2], auto first) {
+  // stT: set t % 2 (requests of this iteration), stO: set (t + 1) % 2 (stored this iteration)
+  auto iter = [&](int t, f32x16 (&sc)[2], f32x16 (&sp)[2], auto first, u32x4 (&stT)[4], u32x4 (&stO)[4])
+      __attribute__((always_inline)) {
     constexpr bool FIRST = decltype(first)::value;
     const int kb = t * kKT;
     const bool next = t + 1 < ntiles;
-    if (k_loader) {
-      if (next) gload(t + 1);
-    } else {
-      gload(t);
-    }
+    // K loaders request K(t+2) (written to LDS at the end of iteration t+1), V loaders V(t+1)
+    const bool req = k_loader ? t + 2 < ntiles : next;
+    if (req) gload(k_loader ? t + 2 : t + 1, stT);
     // A
     const u32x4* kp = Ks[t & 1] + kbase;
 #pragma unroll
@@ -294,33 +298,39 @@ void attn_fwd_kernel(const AttnParams p) {
         for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
       m_run = m_new;
     }
-    // stage K(t+1) / V(t)
-    __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0)
-    if (k_loader) {
-      if (next) lstore(t + 1);
+    // stage K(t+1) / V(t), requested one iteration ago; this iteration's requests may still be
+    // in flight (vmcnt counts them: KPT or 4 per thread)
+    if (!req) {
+      __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0)
+    } else if (k_loader) {
+      __builtin_amdgcn_s_waitcnt(KPT | (0x7 << 4) | (0xF << 8));
     } else {
-      lstore(t);
+      __builtin_amdgcn_s_waitcnt(4 | (0x7 << 4) | (0xF << 8));
     }
+    if (!k_loader || next) lstore(k_loader ? t + 1 : t, stO);
     barrier();
   };
 
-  // prologue: K(0)
+  // prologue: K(0) into LDS, K(1) and V(0) requested
   if (k_loader) {
-    gload(0);
-    lstore(0);
+    gload(0, st0);
+    lstore(0, st0);
+    if (ntiles > 1) gload(1, st1);
+  } else {
+    gload(0, st1);
   }
   barrier();
 
   using T_ = std::integral_constant<bool, true>;
   using F_ = std::integral_constant<bool, false>;
-  iter(0, sa, sb, T_{});
+  iter(0, sa, sb, T_{}, st0, st1);
   int t = 1;
   for (; t + 1 < ntiles; t += 2) {
-    iter(t, sb, sa, F_{});
-    iter(t + 1, sa, sb, F_{});
+    iter(t, sb, sa, F_{}, st1, st0);
+    iter(t + 1, sa, sb, F_{}, st0, st1);
   }
   if (t < ntiles) {
-    iter(t, sb, sa, F_{});
+    iter(t, sb, sa, F_{}, st1, st0);
     exp_part(sb);
   } else {
     exp_part(sa);
