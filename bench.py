@@ -548,6 +548,8 @@ def stack_summary(r, cfg, S, L, steps):
             "gpu_event_ms_per_step": round(r["gpu_ms"] / steps, 4),
             "gemm_tflops": round(gemm_tf, 1), "gemm_frac_of_peak": round(gemm_tf / MFMA_BF16_PEAK_TFLOPS, 4),
             "attn_tflops_causal": round(attn_tf, 1), "attn_frac_of_peak": round(attn_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            # the same time against the work of all S x S pairs (as if nothing were masked)
+            "attn_tflops_dense_equivalent": round(attn_tf * 2.0 * S / (S + 1), 1),
             "kernels": kernels, "finite_output": r["finite"]}
 
 
@@ -689,6 +691,7 @@ def main():
         "gemm_frac_of_peak": head["gemm_frac_of_peak"],
         "attn_tflops_causal": head["attn_tflops_causal"],
         "attn_frac_of_peak": head["attn_frac_of_peak"],
+        "attn_tflops_dense_equivalent": head["attn_tflops_dense_equivalent"],
         "kernels": head["kernels"],
         "finite_output": head["finite_output"],
         "roofline": roofline,
