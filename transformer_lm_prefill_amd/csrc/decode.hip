@@ -137,13 +137,6 @@ __global__ __launch_bounds__(256) void decode_attn_partial_kernel(DecodeAttnPara
   const int t0 = split * p.tiles_per_split;
   const int t1 = min(ntiles, t0 + p.tiles_per_split);
 
-  // the group's query rows, in the cache's format (16-bit: rounded to nearest even)
-  for (int i = tid; i < G * HD; i += 256) {
-    const float qv = p.q[static_cast<int64_t>(g) * G * HD + i];
-    if (CDT == DT_F32) reinterpret_cast<float*>(qs)[i] = qv;
-    else reinterpret_cast<uint16_t*>(qs)[i] = CDT == DT_BF16 ? f2bf(qv) : f2h(qv);
-  }
-
   const char* kbase = static_cast<const char*>(p.kc) + static_cast<int64_t>(g) * p.capacity * HD * ES;
   const char* vbase = static_cast<const char*>(p.vc) + static_cast<int64_t>(g) * p.capacity * HD * ES;
   u32x4 kr[LOADS], vr[LOADS];
@@ -169,7 +162,27 @@ __global__ __launch_bounds__(256) void decode_attn_partial_kernel(DecodeAttnPara
   }
   const int sub = lane / LPK, d0 = 2 * (lane % LPK);
 
+  // the group's query rows (at most kDecMaxGroup * HD values, QPT per thread) are requested
+  // first and the first tile's K / V rows right after, so the two latencies overlap; the rows go
+  // to LDS in the cache's format (16-bit: rounded to nearest even)
+  constexpr int QPT = kDecMaxGroup * HD / 256;
+  float qv[QPT];
+#pragma unroll
+  for (int r = 0; r < QPT; ++r) {
+    const int i = tid + 256 * r;
+    qv[r] = p.q[static_cast<int64_t>(g) * G * HD + min(i, G * HD - 1)];  // (only i < G * HD is kept)
+  }
+  asm volatile("" ::: "memory");  // the query requests go out first,
   if (t0 < t1) load_tile(t0);
+  asm volatile("" ::: "memory");  // and their stores (with the wait) come after the tile requests
+#pragma unroll
+  for (int r = 0; r < QPT; ++r) {
+    const int i = tid + 256 * r;
+    if (i < G * HD) {
+      if (CDT == DT_F32) reinterpret_cast<float*>(qs)[i] = qv[r];
+      else reinterpret_cast<uint16_t*>(qs)[i] = CDT == DT_BF16 ? f2bf(qv[r]) : f2h(qv[r]);
+    }
+  }
   for (int t = t0; t < t1; ++t) {
 #pragma unroll
     for (int r = 0; r < LOADS; ++r) {
