@@ -516,10 +516,11 @@ def run_stack(q3, spec, layers, x0, pos, rows, ds, S, L, steps, warmup):
     for _ in range(steps):
         step()
     torch.cuda.synchronize()
-    kt = q3.timing_collect()
+    med = {}
+    kt = q3.timing_collect(medians=med)
     q3.timing_enable(False)
     finite = bool(torch.isfinite(h).all().item())
-    return {"wall_s": wall, "gpu_ms": gpu_ms, "kt": kt, "finite": finite}
+    return {"wall_s": wall, "gpu_ms": gpu_ms, "kt": kt, "median": med, "finite": finite}
 
 
 def stack_summary(r, cfg, S, L, steps):
@@ -537,7 +538,7 @@ def stack_summary(r, cfg, S, L, steps):
                         "attention": cfg.attn_flops()}
     kernels = {}
     for k, (n, tot) in kt.items():
-        e = {"launches": n, "avg_ms": round(tot / n, 4)}
+        e = {"launches": n, "avg_ms": round(tot / n, 4), "median_ms": round(r["median"][k], 4)}
         if k in per_kernel_flops:
             tf = per_kernel_flops[k] / (tot / n * 1e-3) / 1e12
             e["tflops"] = round(tf, 1)

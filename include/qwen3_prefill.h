@@ -263,12 +263,14 @@ const char *qwen3_last_error(void);
 /* ---- Measurement aid -------------------------------------------------------------------
  * When enabled, every kernel launched by the calls above is bracketed by a pair of hipEvents
  * recorded on the call's stream. qwen3_timing_collect() waits for the recorded events, sums
- * the elapsed time per kernel name, writes up to `max_entries` entries and clears the record.
- * At most 65536 launches are recorded between collects; later ones are not timed. */
+ * the elapsed time per kernel name (and takes the median launch), writes up to `max_entries`
+ * entries and clears the record. At most 65536 launches are recorded between collects; later
+ * ones are not timed. */
 typedef struct {
   char name[48];
   int32_t launches;
   double total_ms;
+  double median_ms;   /* median of the launches' times (mean of the two middle ones if even) */
 } qwen3_kernel_time;
 
 int qwen3_timing_enable(int enable);

@@ -65,7 +65,7 @@ class ModelWeights(ctypes.Structure):
 
 class KernelTime(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_int32),
-                ("total_ms", ctypes.c_double)]
+                ("total_ms", ctypes.c_double), ("median_ms", ctypes.c_double)]
 
 
 class Qwen3Error(RuntimeError):

@@ -979,6 +979,7 @@ int qwen3_timing_enable(int enable) {
 int qwen3_timing_collect(qwen3_kernel_time* out, int32_t max_entries, int32_t* n_out) {
   std::lock_guard<std::mutex> lk(g_tmu);
   std::map<std::string, std::pair<int, double>> agg;
+  std::map<std::string, std::vector<float>> each;  // every launch's time, for the median
   std::vector<std::string> order;
   for (int i = 0; i < g_used; ++i) {
     hipError_t e = hipEventSynchronize(g_events[2 * i + 1]);
@@ -996,6 +997,7 @@ int qwen3_timing_collect(qwen3_kernel_time* out, int32_t max_entries, int32_t* n
     if (!agg.count(name)) order.push_back(name);
     agg[name].first += 1;
     agg[name].second += ms;
+    each[name].push_back(ms);
   }
   g_used = 0;
   int n = 0;
@@ -1006,6 +1008,10 @@ int qwen3_timing_collect(qwen3_kernel_time* out, int32_t max_entries, int32_t* n
       std::strncpy(out[n].name, name.c_str(), sizeof(out[n].name) - 1);
       out[n].launches = agg[name].first;
       out[n].total_ms = agg[name].second;
+      std::vector<float>& v = each[name];
+      std::sort(v.begin(), v.end());
+      const size_t h = v.size() / 2;
+      out[n].median_ms = v.size() % 2 ? v[h] : 0.5 * (static_cast<double>(v[h - 1]) + v[h]);
     }
     ++n;
   }

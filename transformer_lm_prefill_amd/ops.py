@@ -536,12 +536,15 @@ def timing_enable(on=True):
     _lib.check(_lib.load().qwen3_timing_enable(1 if on else 0))
 
 
-def timing_collect(max_entries=64):
-    """{kernel name: (launches, total ms)} for launches since the last collect."""
+def timing_collect(max_entries=64, medians=None):
+    """{kernel name: (launches, total ms)} for launches since the last collect; with a dict as
+    `medians`, also fills {kernel name: median ms of one launch}."""
     lib = _lib.load()
     arr = (_lib.KernelTime * max_entries)()
     n = ctypes.c_int32(0)
     _lib.check(lib.qwen3_timing_collect(arr, max_entries, ctypes.byref(n)))
+    if medians is not None:
+        medians.update({arr[i].name.decode(): arr[i].median_ms for i in range(n.value)})
     return {arr[i].name.decode(): (arr[i].launches, arr[i].total_ms) for i in range(n.value)}
 
 
