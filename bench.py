@@ -168,6 +168,9 @@ def model_prefill_extra(cfg, layers, pos, stream, vocab, spec=None):
     return {"workload": f"{cfg.name}: {len(layers)} layers, seq {cfg.seq_len}, vocab {vocab} untied head",
             "weights": spec.dtype,
             "ms": round(ms, 4), "tokens_per_s": round(cfg.seq_len / (ms * 1e-3), 1),
+            # the kernels alone (one call, event-timed): "ms" is wall time per call and also holds
+            # the token ids' host-side marshalling and their copy to the device
+            "kernels_ms": round(sum(v[1] for v in kt.values()), 4),
             "lm_head": {"avg_ms": round(head_ms, 4), "bound": "hbm",
                         "GB_per_s": round(head_bytes / (head_ms * 1e-3) / 1e9, 1),
                         "frac_of_hbm_peak": round(head_bytes / (head_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
