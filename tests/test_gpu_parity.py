@@ -46,6 +46,30 @@ def test_rms_norm_rows(wdt, ydt, rows, hidden):
     assert err16(host(y), ref, ydt) <= ALLOW16[ydt]
 
 
+def test_rms_norm_degenerate_rows():
+    """Rows of zeros give exact zeros (the mean of squares is 0, the scale 1/sqrt(eps) multiplies
+    zeros); rows far below eps in magnitude are scaled by about 1/sqrt(eps); one nonzero element
+    in a row gives +-sqrt(H)-scaled weight there (closed form of the definition)."""
+    rows, hidden = 40, 2048
+    x = _normal(3, (rows, hidden), dtype="f32")
+    x[0:5] = 0.0
+    x[5:10] *= 1e-12
+    x[10:15] = 0.0
+    x[10:15, 7] = 5.0
+    w = _normal(4, (hidden,), std=0.1, mean=1.0, dtype="bf16")
+    y = host(q3.rms_norm_rows(dev(x), dev(w, "bf16"), 1e-6, out_dtype=torch.float32))
+    assert np.all(y[0:5] == 0.0)
+    ref = oracle.rms_norm(x, w, 1e-6)
+    # elementwise: an fp32 reciprocal square root and two products (a few ulps of each element;
+    # the single-element rows hold values ~30x the RMS, beyond what the generic allowance
+    # assumes) plus the mean's summation error
+    rms = np.sqrt(np.mean(ref.astype(np.float64) ** 2))
+    assert np.all(np.abs(y - ref) <= 4 * 2.0 ** -24 * np.abs(ref) + 2e-6 * rms)
+    # one element 5 in a row of H: mean of squares 25/H, so y = 5 / sqrt(25/H + eps) * w
+    expect = 5.0 / np.sqrt(25.0 / hidden + 1e-6) * w[7]
+    assert np.allclose(y[10:15, 7], expect, rtol=2e-6) and np.all(np.delete(y[10:15], 7, axis=1) == 0.0)
+
+
 # ------------------------------------------------------------------ q/k norm + MRoPE (a3, a4)
 
 @pytest.mark.parametrize("dtype,ndt,hd,sec,theta,s,nh,nkv,image", [
