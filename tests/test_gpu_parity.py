@@ -120,6 +120,30 @@ def test_qk_norm_mrope_large_positions_bf16():
     assert rel_err(host(qf), oracle.qk_norm_mrope(q, one, 1e-6, pos, 5e6, (24, 20, 20))) <= 2e-6
 
 
+def test_qk_norm_mrope_zero_heads_and_position_zero():
+    """Head vectors of zeros stay exact zeros (normalized by 1/sqrt(eps), then rotated); at
+    position 0 on every axis the rotation is the identity, so the output is the plain per-head
+    RMSNorm of the row."""
+    s, nh, nkv, hd = 20, 4, 2, 128
+    q = _normal(9, (s, nh, hd), dtype="f32")
+    k = _normal(10, (s, nkv, hd), dtype="f32")
+    q[3, 1] = 0.0
+    k[7, 0] = 0.0
+    pos = np.tile(np.arange(s), (3, 1))
+    pos[:, 0] = 0
+    nq = _normal(11, (hd,), std=0.1, mean=1.0, dtype="f32")
+    nk = _normal(12, (hd,), std=0.1, mean=1.0, dtype="f32")
+    qd, kd = dev(q), dev(k)
+    q3.qk_norm_mrope(qd, kd, dev(nq), dev(nk), dev_i32(pos), 1e-6, 5e6, (24, 20, 20))
+    torch.cuda.synchronize()
+    hq, hk = host(qd), host(kd)
+    assert np.all(hq[3, 1] == 0.0) and np.all(hk[7, 0] == 0.0)
+    # token 0 sits at position 0: only the normalization applies
+    assert rel_err(hq[0], oracle.rms_norm(q[0], nq, 1e-6)) <= 2e-6
+    assert rel_err(hk[0], oracle.rms_norm(k[0], nk, 1e-6)) <= 2e-6
+    assert rel_err(hq, oracle.qk_norm_mrope(q, nq, 1e-6, pos, 5e6, (24, 20, 20))) <= 2e-6
+
+
 # ------------------------------------------------------------------ attention (a5)
 
 @pytest.mark.parametrize("fmt", ["f16", "bf16"])
