@@ -709,17 +709,25 @@ void gemm_d2l_kernel(const GemmParams p) {
   };
   // Workgroup barrier. With wait_lds, this thread's LDS accesses complete first (lgkmcnt(0)):
   // needed where threads write LDS before it (converted or decoded weight tiles, the LDS
-  // epilogue). The ring's direct-to-LDS loads are covered by the vmcnt waits, and the fragment
-  // reads still in flight at a step's barrier are of stages no load will overwrite before the
-  // next barrier (their MFMAs wait for them), so the step barrier of a pure direct-to-LDS ring
-  // does not wait for them.
+  // epilogue). In a ring filled only by direct-to-LDS loads (covered by the vmcnt waits), the
+  // newest MI + NI LDS reads may stay in flight across a step barrier: they are the next
+  // stage's first sub-step fragments, and the loads issued after the barrier refill the stage
+  // before that one. Every older read must be done, though: the compiler moves a step's last
+  // MFMAs, and the waits for their fragments with them, past the next barrier, and a read of the
+  // stage being refilled still in flight there would race with its direct-to-LDS write. LDS
+  // reads complete in order; scalar loads counted by the same counter only make the wait
+  // stricter.
   auto barrier = [&](auto wait_lds) {
     asm volatile("" ::: "memory");
-    if constexpr (decltype(wait_lds)::value) __builtin_amdgcn_s_waitcnt((0x7 << 4) | 0xF | (0x3 << 14));  // lgkmcnt(0)
+    if constexpr (decltype(wait_lds)::value)
+      __builtin_amdgcn_s_waitcnt((0x7 << 4) | 0xF | (0x3 << 14));  // lgkmcnt(0)
+    else
+      __builtin_amdgcn_s_waitcnt((0x7 << 4) | 0xF | (0x3 << 14) | ((MI + NI) << 8));  // lgkmcnt(MI + NI)
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
   constexpr bool LDS_W = STAGE_B || CVT_IN_LDS || BQ;  // threads write ring stages themselves
+  static_assert(MI + NI <= 15, "lgkmcnt immediate");
   using WaitLds = std::integral_constant<bool, LDS_W>;
 
 #pragma unroll
