@@ -70,16 +70,17 @@ def kernel_sources_digest():
 
 
 def stored_traffic():
-    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter
-    summary, or None if there is none or the kernel source has changed since."""
+    """(HBM bytes per launch, algorithmic bytes per launch) of the dominant kernel from the
+    committed rocprofv3 counter summary, or (None, None) if there is none or the kernel source
+    has changed since."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
-        return None
+        return None, None
     if t.get("kernel_source_sha256_16") != kernel_sources_digest():
-        return None
-    return t.get("bytes_per_launch")
+        return None, None
+    return t.get("bytes_per_launch"), t.get("algorithmic_bytes_per_launch")
 
 
 def cpu_baseline(cfg, w0, x, pos, n_tok, min_s=10.0, max_reps=8):
@@ -622,10 +623,15 @@ def main():
     dom_flops = 2.0 * S * cfg.hidden * 2 * cfg.ffn     # one launch: gate and up products
     dom_avg_ms = ms_dom / n_dom
     achieved = dom_flops / (dom_avg_ms * 1e-3) / 1e12
+    traffic, traffic_alg = stored_traffic()
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                "traffic": stored_traffic(), "kernel": DOMINANT,
+                "traffic": traffic, "kernel": DOMINANT,
                 "avg_launch_ms": round(dom_avg_ms, 4)}
+    if traffic and traffic_alg:
+        # counter bytes (L2 misses, MALL hits included) over the bytes the product must move once
+        roofline["traffic_algorithmic"] = traffic_alg
+        roofline["traffic_ratio"] = round(traffic / traffic_alg, 2)
 
     def extra(skip, fn, *a):
         """A secondary measurement; a failure is reported in its field, not by losing the line."""

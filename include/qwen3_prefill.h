@@ -92,9 +92,12 @@ typedef enum {
  *                 QWEN3_BF16 bf16 operands (bf16 weights only);
  *                 QWEN3_F32  fp32 end to end (requires wdtype QWEN3_F32).
  *               fp16 and bf16 run at the same MFMA rate; fp16 keeps 3 more mantissa bits
- *               but holds magnitudes only up to 65504 (an activation beyond that, such as a
- *               SwiGLU outlier of a real checkpoint, becomes infinite: such a model needs
- *               QWEN3_BF16). Measured agreement of the layer output with an exact (float64)
+ *               but holds magnitudes only up to 65504. With fp16 operands the SwiGLU
+ *               activation is stored as 2^-4 * a and the down product scales its sum back by
+ *               2^4 (both exact), so activations up to 65504 * 16 (about 1.05e6) stay
+ *               finite; the other fp16 operands (normalized rows, q, k, v, probabilities,
+ *               attention output) hold up to 65504 and become infinite beyond (such a model
+ *               needs QWEN3_BF16). Measured agreement of the layer output with an exact (float64)
  *               reference, max |error| / RMS over the output, on synthetic N(0, 0.02)
  *               weights:
  *                 QWEN3_F16   2e-3 .. 5e-3 at every shape measured (2048-hidden layers at
@@ -228,7 +231,8 @@ int apply_rope_tables(void *x, int32_t n, int32_t heads, int32_t head_dim, int64
  *   are those of (wdtype, act_dtype) in qwen3_layer_cfg). residual [S, hidden] f32 or NULL.
  *   out [S, hidden] of `out_dtype`: f32, or x_dtype when residual is NULL; out may equal
  *   residual. wdtype QWEN3_F16_TILED: the three matrices in the tiled layout. workspace holds
- *   the [S, ffn] activation: swiglu_ffn_workspace_bytes() bytes. */
+ *   the [S, ffn] activation (with fp16 operands scaled by 2^-4, undone exactly in the down
+ *   product, as for qwen3_layer_prefill): swiglu_ffn_workspace_bytes() bytes. */
 int swiglu_ffn(const void *x_normed, const void *w_gate, const void *w_up, const void *w_down,
                const void *residual, void *out, int32_t seq_len, int32_t hidden, int32_t ffn,
                qwen3_dtype wdtype, qwen3_dtype x_dtype, qwen3_dtype out_dtype, void *workspace,

@@ -318,6 +318,51 @@ def test_swiglu_ffn_64bit_address_path(monkeypatch, wdt, out_dtype, s, h, f):
     assert torch.equal(o_buf, o_64)
 
 
+def test_swiglu_ffn_activations_beyond_fp16_range():
+    """SwiGLU activations above fp16's largest value (65504) stay finite with fp16 operands: the
+    activation is stored as 2^-4 * a and the down product scales back by 2^4, both exact. The
+    normalized input is scaled by 200 (gate and up outputs with standard deviation ~130), so the
+    largest activation of this data is over twice 65504; the oracle confirms that."""
+    s, h, f = 300, 1024, 768
+    x = (_normal(90, (s, h), dtype="f32") * 200).astype(np.float16).astype(np.float32)
+    wg = _normal(91, (f, h), std=0.02)
+    wu = _normal(92, (f, h), std=0.02)
+    wd = _normal(93, (h, f), std=0.02)
+    r = _normal(94, (s, h), dtype="f32")
+    a = oracle.silu(oracle.linear(x, wg)) * oracle.linear(x, wu)
+    assert 65504 * 2 < np.abs(a).max() < 65504 * 16, np.abs(a).max()
+    ref = oracle.swiglu_ffn(x, wg, wu, wd) + r
+    for xdt in ("f16", "bf16"):
+        xx = x if xdt == "f16" else synth.round_to_bf16(x)
+        refx = ref if xdt == "f16" else oracle.swiglu_ffn(xx, wg, wu, wd) + r
+        out = host(q3.swiglu_ffn(dev(xx, xdt), dev(wg, "bf16"), dev(wu, "bf16"), dev(wd, "bf16"),
+                                 residual=dev(r)))
+        assert np.isfinite(out).all(), xdt
+        err = rel_err(out, refx)
+        log_err(f"swiglu_ffn_large_act[{xdt}]", err)
+        assert err <= TOL["bf16"], (xdt, err)
+
+
+def test_layer_activations_beyond_fp16_range():
+    """The layer's own gate/up and down products with SwiGLU activations above 65504: the FFN
+    norm weights are scaled by 150 (bf16 values), so the normalized rows reach a few hundred and
+    the activation several times 65504 (checked on the oracle's intermediate)."""
+    cfg = synth.get_config("qwen3vl_2b_text").with_seq(257, n_layers=1)
+    w = synth.make_layer_weights(cfg)
+    w["ffn_norm"] = synth.round_to_bf16(np.asarray(w["ffn_norm"], dtype=np.float32) * 150)
+    x = synth.make_x(cfg)
+    pos = synth.make_positions(cfg)
+    taps = {}
+    ref = oracle.layer_prefill(x, w, cfg, pos, taps=taps)
+    assert 65504 * 2 < np.abs(taps["a"]).max() < 65504 * 16, np.abs(taps["a"]).max()
+    for act in ("f16", "bf16"):
+        out = _run_layer(cfg, w, x, pos, act=act)
+        assert np.isfinite(out).all(), act
+        err = rel_err(out, ref)
+        log_err(f"layer_large_act[act={act}]", err)
+        assert err <= TOL["bf16"], (act, err)
+
+
 def test_swiglu_ffn_bf16_out():
     s, h, f = 100, 512, 384
     x = _normal(60, (s, h))

@@ -239,7 +239,15 @@ struct Proj {
   const float* R; int64_t ldr;
   int M, N, K;
   int a_t = 0, b_t = 0, c_t = 0;   // A, B, the SwiGLU output in the tiled layout (16-bit only)
+  float act_scale = 1.f, out_scale = 1.f;  // 16-bit products only (GemmParams)
 };
+
+// With fp16 operands the SwiGLU activation is stored as 2^-4 * a, and the down product that
+// reads it multiplies its sum by 2^4. Both scalings are exact (powers of two, fp16 normal
+// range), so the result is unchanged, while activations up to 65504 * 16 (about 1.05e6) stay
+// finite instead of overflowing at 65504. bf16 operands carry fp32's exponent range unscaled.
+constexpr float kActScaleF16 = 0.0625f;
+inline float act_scale_for(qwen3_dtype ad) { return ad == QWEN3_F16 ? kActScaleF16 : 1.f; }
 
 // wd: weight dtype; ad: operand dtype (A, MFMA, 16-bit outputs); q4: the B matrices are Q4_0
 // blocks decoded inside the product.
@@ -250,7 +258,8 @@ int run_gemm(const char* name, const Proj& g, int epi, qwen3_dtype wd, qwen3_dty
   if (ad != QWEN3_F32) {
     q3::GemmParams p{static_cast<const uint16_t*>(g.A), g.lda, static_cast<const uint16_t*>(g.B0),
                      static_cast<const uint16_t*>(g.B1), static_cast<const uint16_t*>(g.B2),
-                     g.nseg0, g.nseg1, g.ldb, g.C, g.ldc, g.R, g.ldr, g.M, g.N, g.K, g.a_t, g.b_t, g.c_t};
+                     g.nseg0, g.nseg1, g.ldb, g.C, g.ldc, g.R, g.ldr, g.M, g.N, g.K, g.a_t, g.b_t, g.c_t,
+                     g.act_scale, g.out_scale};
     if (q4)
       e = q3::launch_gemm_mfma_q4(p, epi, ad == QWEN3_F16 ? q3::OPH_F16 : q3::OPH_BF16, 0, s);
     else
@@ -274,10 +283,10 @@ int run_ffn(const void* x, const void* wg, const void* wu, const void* wd, const
             hipStream_t s) {
   const int wt = wdt == QWEN3_F16_TILED;
   wdt = plain_w(wdt);
-  Proj gu{x, H, wg, wu, nullptr, 0, 0, H, act, F, nullptr, 0, S, 2 * F, H, 0, wt, 0};
+  Proj gu{x, H, wg, wu, nullptr, 0, 0, H, act, F, nullptr, 0, S, 2 * F, H, 0, wt, 0, act_scale_for(adt)};
   int st = run_gemm("gemm_gate_up_swiglu", gu, q3::EPI_SWIGLU_16, wdt, adt, s);
   if (st) return st;
-  Proj dn{act, F, wd, nullptr, nullptr, H, H, F, out, H, R, H, S, H, F, 0, wt, 0};
+  Proj dn{act, F, wd, nullptr, nullptr, H, H, F, out, H, R, H, S, H, F, 0, wt, 0, 1.f, 1.f / act_scale_for(adt)};
   const int epi = out_dt == QWEN3_F32 ? q3::EPI_STORE_F32 : q3::EPI_STORE_16;
   return run_gemm(R ? "gemm_down_resid" : "gemm_down", dn, epi, wdt, adt, s);
 }
@@ -521,7 +530,7 @@ static int layer_prefill_impl(const qwen3_layer_cfg* cfg, const LayerW& w, const
     const MatW* g[2] = {&w.wg, &w.wu};
     const int rows[2] = {F, F};
     if ((st = group_weights(g, 2, rows, H, cfg->wdtype, dt, dq, B, &bdt, &q4, S16 * H, s, &bt))) return st;
-    Proj gu{xn, H, B[0], B[1], nullptr, 0, 0, H, act, F, nullptr, 0, S, 2 * F, H, at, bt, at};
+    Proj gu{xn, H, B[0], B[1], nullptr, 0, 0, H, act, F, nullptr, 0, S, 2 * F, H, at, bt, at, act_scale_for(dt)};
     if ((st = run_gemm("gemm_gate_up_swiglu", gu, q3::EPI_SWIGLU_16, bdt, dt, s, q4))) return st;
   }
   // a9: y2 = y1 + a Wd^T
@@ -529,7 +538,7 @@ static int layer_prefill_impl(const qwen3_layer_cfg* cfg, const LayerW& w, const
     const MatW* g[1] = {&w.wd};
     const int rows[1] = {H};
     if ((st = group_weights(g, 1, rows, F, cfg->wdtype, dt, dq, B, &bdt, &q4, S16 * F, s, &bt))) return st;
-    Proj dn{act, F, B[0], nullptr, nullptr, H, H, F, y, H, y, H, S, H, F, at, bt, 0};
+    Proj dn{act, F, B[0], nullptr, nullptr, H, H, F, y, H, y, H, S, H, F, at, bt, 0, 1.f, 1.f / act_scale_for(dt)};
     if ((st = run_gemm("gemm_down_resid", dn, q3::EPI_STORE_F32, bdt, dt, s, q4))) return st;
   }
   // a10: DeepStack rows (the validated host row list goes to the workspace on the stream)

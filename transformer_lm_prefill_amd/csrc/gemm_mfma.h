@@ -193,7 +193,8 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p,
             const int f = tn * (BN / 2) + wn * (16 * NI) + ni * 32 + 8 * q + c4;
             float h[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) h[r] = silu_f(acc[mi][ni][4 * q + r]) * acc[mi][ni + NI / 2][4 * q + r];
+            for (int r = 0; r < 4; ++r)
+              h[r] = silu_f(acc[mi][ni][4 * q + r]) * (acc[mi][ni + NI / 2][4 * q + r] * p.act_scale);
             *reinterpret_cast<u32x2*>(C + c_col(f)) = u32x2{F::pack2(h[0], h[1]), F::pack2(h[2], h[3])};
           }
       } else {
@@ -203,12 +204,14 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p,
           for (int q = 0; q < 4; ++q) {
             const int n = tn * BN + wn * 32 * NI + ni * 32 + 8 * q + c4;
             const f32x16& a = acc[mi][ni];
+            const float sc = p.out_scale;
             if (EPI == EPI_STORE_16) {
               uint16_t* C = static_cast<uint16_t*>(p.C) + static_cast<int64_t>(row) * p.ldc + n;
-              *reinterpret_cast<u32x2*>(C) =
-                  u32x2{F::pack2(a[4 * q], a[4 * q + 1]), F::pack2(a[4 * q + 2], a[4 * q + 3])};
+              *reinterpret_cast<u32x2*>(C) = u32x2{F::pack2(a[4 * q] * sc, a[4 * q + 1] * sc),
+                                                   F::pack2(a[4 * q + 2] * sc, a[4 * q + 3] * sc)};
             } else {
-              f32x4 v = {a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+              // with RIN the accumulators started from R / out_scale
+              f32x4 v = {a[4 * q] * sc, a[4 * q + 1] * sc, a[4 * q + 2] * sc, a[4 * q + 3] * sc};
               if (!RIN && p.R) {
                 const f32x4 r = *reinterpret_cast<const f32x4*>(p.R + static_cast<int64_t>(row) * p.ldr + n);
                 v += r;
@@ -246,7 +249,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p,
             if (!check.value || m < p.M) {
               const float g = acc[mi][ni][e];
               const float u = acc[mi][ni + NI / 2][e];
-              C[off(mi, ni, e)] = F::from_f32(silu_f(g) * u);
+              C[off(mi, ni, e)] = F::from_f32(silu_f(g) * (u * p.act_scale));
             }
           }
         }
@@ -267,7 +270,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p,
           for (int e = 0; e < 16; ++e) {
             const int m = row_base + mi * 32 + 8 * (e >> 2) + (e & 3);
             if (!check.value || m < p.M) {
-              const float v = acc[mi][ni][e];
+              const float v = acc[mi][ni][e] * p.out_scale;
               if (EPI == EPI_STORE_16) {
                 C16[static_cast<int64_t>(mi * 32 + 8 * (e >> 2) + (e & 3)) * p.ldc + ni * 32] = F::from_f32(v);
               } else {
@@ -522,6 +525,9 @@ void gemm_d2l_kernel(const GemmParams p) {
   // here, behind the ring's first tile loads, so the epilogue only stores; rows past M load a
   // clamped valid row and are never stored
   const bool rin = TRANS && p.R != nullptr;
+  // the residual enters the accumulators divided by out_scale (exact for a power of two), so
+  // the epilogue's single multiplication by out_scale leaves it unchanged
+  const float r_scale = 1.0f / p.out_scale;
   // RS: a one-tile workgroup with enough K steps takes the residual in MI * NI chunks (one
   // 32 x 32 accumulator block each) during its first groups of K steps instead of before them,
   // so a launch's residual reads (all workgroups at once) spread over the K loop instead of
@@ -540,7 +546,7 @@ void gemm_d2l_kernel(const GemmParams p) {
     for (int q = 0; q < 4; ++q) {
       const f32x4 r = *reinterpret_cast<const f32x4*>(rr + tn * BN + wn * 32 * NI + ni * 32 + 8 * q + c4);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dst[4 * q + e] = r[e];
+      for (int e = 0; e < 4; ++e) dst[4 * q + e] = r[e] * r_scale;
     }
   };
   if (rin && !rs) {
@@ -555,7 +561,7 @@ void gemm_d2l_kernel(const GemmParams p) {
         for (int q = 0; q < 4; ++q) {
           const f32x4 r = *reinterpret_cast<const f32x4*>(rr + tn * BN + wn * 32 * NI + ni * 32 + 8 * q + c4);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[mi][ni][4 * q + e] = r[e];
+          for (int e = 0; e < 4; ++e) acc[mi][ni][4 * q + e] = r[e] * r_scale;
         }
     }
   }
@@ -852,8 +858,9 @@ void gemm_d2l_kernel(const GemmParams p) {
           for (int q = 0; q < 4; ++q) {
             const int ch = ni * 8 + 2 * q + fh;
             const f32x16& a = acc[half * 2 + m2][ni];
-            buf[r * 16 + (ch ^ (r & 15))] =
-                __builtin_bit_cast(u32x4, f32x4{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]});
+            const float sc = p.out_scale;
+            buf[r * 16 + (ch ^ (r & 15))] = __builtin_bit_cast(
+                u32x4, f32x4{a[4 * q] * sc, a[4 * q + 1] * sc, a[4 * q + 2] * sc, a[4 * q + 3] * sc});
           }
       }
       __builtin_amdgcn_s_waitcnt((0x7 << 4) | 0xF | (0x3 << 14));  // lgkmcnt(0): own writes done

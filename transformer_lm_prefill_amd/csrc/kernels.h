@@ -163,6 +163,9 @@ struct GemmParams {
   // ceil(M / 16) * 16 rows, lda == K (rows past M are read and their products discarded);
   // b_tiled: every B segment, ldb == K; c_tiled: the EPI_SWIGLU_16 output, ldc == N / 2.
   int a_tiled = 0, b_tiled = 0, c_tiled = 0;
+  // Exact scales (powers of two; 1 leaves the result as is): EPI_SWIGLU_16 stores
+  // act_scale * silu(g) * u; EPI_STORE_F32 and EPI_STORE_16 store out_scale * (A B^T) [+ R].
+  float act_scale = 1.f, out_scale = 1.f;
 };
 // op: OPH_BF16 or OPH_F16, the format of A, of the MFMA and of 16-bit outputs. b_bf16: B is
 // stored as bf16 (converted to fp16 on the way to LDS when op is fp16); otherwise B is in op's
